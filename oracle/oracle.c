@@ -1,0 +1,340 @@
+/*
+ * oracle.c -- plain fp64 CPU definition of one sparse-routed MoE FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg, never by the product path.  It is written for
+ * a reader to check against the pages by eye: one token at a time, serial
+ * fp64 sums in ascending index order, no blocking, no fusion, no reordering.
+ * The only parallelism is an OpenMP loop over independent tokens or rows,
+ * which does not change any sum.
+ *
+ * Citations (page title, section): see oracle.h for the list of readings.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Widen element i of a dt-typed buffer to fp64.  bfloat16 is the upper half
+ * of a binary32 pattern, so widening it is a 16-bit left shift. */
+static double elem(const void* p, int dt, int64_t i) {
+  if (dt == ORACLE_F32) return (double)((const float*)p)[i];
+  uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 16;
+  float v;
+  memcpy(&v, &bits, sizeof v);
+  return (double)v;
+}
+
+/* Dot product of row `row` of a [rows, n] dt-typed matrix with an fp64
+ * vector, summed serially in ascending index order. */
+static double dot_row(const void* M, int dt, int64_t row, int64_t n,
+                      const double* v) {
+  double s = 0.0;
+  for (int64_t i = 0; i < n; ++i) s += elem(M, dt, row * n + i) * v[i];
+  return s;
+}
+
+static int bad_dt(int dt) { return dt != ORACLE_F32 && dt != ORACLE_BF16; }
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------- routing */
+
+/* Expert order for top-k: larger logit first; equal logits, lower index
+ * first (the tie rule).  qsort with this total order is deterministic. */
+typedef struct {
+  double logit;
+  int32_t e;
+} ranked;
+
+static int by_logit_then_index(const void* pa, const void* pb) {
+  const ranked* a = (const ranked*)pa;
+  const ranked* b = (const ranked*)pb;
+  if (a->logit > b->logit) return -1;
+  if (a->logit < b->logit) return 1;
+  return (a->e > b->e) - (a->e < b->e);
+}
+
+/* Route one token: logits (score of every expert from the router linear
+ * layer), softmax over all experts, the k experts with the largest logits,
+ * and their probabilities renormalised over the k selected ones.
+ * If forced != NULL the selection is those k experts instead.
+ * scratch holds E doubles (logits) and E ranked entries. */
+static void route_token(int64_t t, int64_t d, int64_t E, int64_t k, int dt,
+                        const void* x, const void* W_router, const float* bias,
+                        const int32_t* forced, double* xt, double* logit,
+                        ranked* order, int32_t* idx, double* w) {
+  for (int64_t i = 0; i < d; ++i) xt[i] = elem(x, dt, t * d + i);
+
+  /* 1. logits: l_e = sum_i x[t,i] W_router[e,i]  (+ b_e) */
+  for (int64_t e = 0; e < E; ++e) {
+    logit[e] = dot_row(W_router, dt, e, d, xt);
+    if (bias) logit[e] += (double)bias[e];
+  }
+
+  /* 2. softmax over all experts: p_e = exp(l_e - max) / sum_e exp(l_e - max) */
+  double m = logit[0];
+  for (int64_t e = 1; e < E; ++e)
+    if (logit[e] > m) m = logit[e];
+  double z = 0.0;
+  for (int64_t e = 0; e < E; ++e) z += exp(logit[e] - m);
+
+  /* 3. top-k by logit, ties to the lower index */
+  if (forced) {
+    for (int64_t j = 0; j < k; ++j) idx[j] = forced[j];
+  } else {
+    for (int64_t e = 0; e < E; ++e) {
+      order[e].logit = logit[e];
+      order[e].e = (int32_t)e;
+    }
+    qsort(order, (size_t)E, sizeof(ranked), by_logit_then_index);
+    for (int64_t j = 0; j < k; ++j) idx[j] = order[j].e;
+  }
+
+  /* 4. renormalise the selected probabilities so they sum to one */
+  double sel = 0.0;
+  for (int64_t j = 0; j < k; ++j) sel += exp(logit[idx[j]] - m) / z;
+  for (int64_t j = 0; j < k; ++j) w[j] = (exp(logit[idx[j]] - m) / z) / sel;
+}
+
+int oracle_route(int64_t T, int64_t d, int64_t E, int64_t k, int dt,
+                 const void* x, const void* W_router, const float* bias,
+                 double* logits, int32_t* idx, double* w) {
+  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E || bad_dt(dt)) return -1;
+  if (!x || !W_router || !idx || !w) return -1;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* xt = (double*)malloc(sizeof(double) * (size_t)d);
+    double* lg = (double*)malloc(sizeof(double) * (size_t)E);
+    ranked* order = (ranked*)malloc(sizeof(ranked) * (size_t)E);
+    if (!xt || !lg || !order) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t t = 0; t < T; ++t) {
+        route_token(t, d, E, k, dt, x, W_router, bias, NULL, xt, lg, order,
+                    idx + t * k, w + t * k);
+        if (logits) memcpy(logits + t * E, lg, sizeof(double) * (size_t)E);
+      }
+    }
+    free(xt);
+    free(lg);
+    free(order);
+  }
+  return fail ? -2 : 0;
+}
+
+/* ------------------------------------------------------------ permutation */
+
+int oracle_permute(int64_t T, int64_t k, int64_t E, int64_t S,
+                   const int32_t* idx, int32_t* counts, int32_t* offsets,
+                   int32_t* sorted_slot, int32_t* slot_pos) {
+  if (T < 0 || k < 1 || E < 1 || S < 0) return -1;
+  if (!counts || !offsets || (T > 0 && (!idx || !sorted_slot || !slot_pos)))
+    return -1;
+  int64_t n = T * k;
+  for (int64_t s = 0; s < n; ++s)
+    if (idx[s] < 0 || idx[s] >= E) return -1;
+
+  /* histogram of the routed copies; every shared expert takes all T tokens */
+  for (int64_t e = 0; e < E + S; ++e) counts[e] = 0;
+  for (int64_t s = 0; s < n; ++s) counts[idx[s]] += 1;
+  for (int64_t sg = 0; sg < S; ++sg) counts[E + sg] = (int32_t)T;
+
+  /* exclusive prefix sum */
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E + S; ++e) offsets[e + 1] = offsets[e] + counts[e];
+
+  /* stable scatter: slots visited in ascending order */
+  int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  if (!fill) return -2;
+  for (int64_t s = 0; s < n; ++s) {
+    int32_t e = idx[s];
+    int32_t pos = offsets[e] + fill[e];
+    fill[e] += 1;
+    sorted_slot[pos] = (int32_t)s;
+    slot_pos[s] = pos;
+  }
+  free(fill);
+  return 0;
+}
+
+/* ------------------------------------------------------------ expert FFN */
+
+/* SwiGLU hidden activation of token vector xt through expert e:
+ * gate = rows [0, f) of the packed gate_up matrix (w1), up = rows [f, 2f)
+ * (w3); a_n = silu(gate_n) * up_n. */
+static void expert_hidden(int64_t e, int64_t d, int64_t f, int dt,
+                          const void* W_gate_up, const double* xt,
+                          double* act) {
+  int64_t base = e * 2 * f; /* first row of expert e in [E+S, 2f, d] */
+  for (int64_t n = 0; n < f; ++n) {
+    double g = dot_row(W_gate_up, dt, base + n, d, xt);
+    double u = dot_row(W_gate_up, dt, base + f + n, d, xt);
+    double silu = g / (1.0 + exp(-g));
+    act[n] = silu * u;
+  }
+}
+
+/* Down projection of activation vector act through expert e:
+ * out_i = sum_n W_down[e, i, n] act_n. */
+static void expert_down(int64_t e, int64_t d, int64_t f, int dt,
+                        const void* W_down, const double* act, double* out) {
+  for (int64_t i = 0; i < d; ++i)
+    out[i] = dot_row(W_down, dt, e * d + i, f, act);
+}
+
+int oracle_gate_up_rows(int64_t n, const int64_t* tok, const int32_t* expert,
+                        int64_t d, int64_t f, int dt, const void* x,
+                        const void* W_gate_up, double* act) {
+  if (n < 0 || d < 1 || f < 1 || bad_dt(dt)) return -1;
+  if (n > 0 && (!tok || !expert || !x || !W_gate_up || !act)) return -1;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* xt = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!xt) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < n; ++r) {
+        for (int64_t i = 0; i < d; ++i) xt[i] = elem(x, dt, tok[r] * d + i);
+        expert_hidden(expert[r], d, f, dt, W_gate_up, xt, act + r * f);
+      }
+    }
+    free(xt);
+  }
+  return fail ? -2 : 0;
+}
+
+int oracle_down_rows(int64_t n, const int32_t* expert, int64_t d, int64_t f,
+                     int dt, const void* act, const void* W_down, double* out) {
+  if (n < 0 || d < 1 || f < 1 || bad_dt(dt)) return -1;
+  if (n > 0 && (!expert || !act || !W_down || !out)) return -1;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* a = (double*)malloc(sizeof(double) * (size_t)f);
+    if (!a) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < n; ++r) {
+        for (int64_t i = 0; i < f; ++i) a[i] = elem(act, dt, r * f + i);
+        expert_down(expert[r], d, f, dt, W_down, a, out + r * d);
+      }
+    }
+    free(a);
+  }
+  return fail ? -2 : 0;
+}
+
+/* ---------------------------------------------------------------- combine */
+
+int oracle_combine(int64_t T, int64_t k, int64_t S, int64_t d, int dt,
+                   const void* O, const int32_t* slot_pos, const double* w,
+                   double* y) {
+  if (T < 0 || k < 1 || S < 0 || d < 1 || bad_dt(dt)) return -1;
+  if (T > 0 && (!O || !slot_pos || !w || !y)) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < k; ++j) {
+        int64_t row = slot_pos[t * k + j];
+        acc += w[t * k + j] * elem(O, dt, row * d + i);
+      }
+      for (int64_t sg = 0; sg < S; ++sg) {
+        int64_t row = T * k + sg * T + t;
+        acc += elem(O, dt, row * d + i);
+      }
+      y[t * d + i] = acc;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------ whole layer */
+
+int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
+                         int64_t S, int dt, const void* x, const void* W_router,
+                         const float* bias, const void* W_gate_up,
+                         const void* W_down, int64_t n_tok,
+                         const int64_t* tok_list, const int32_t* forced_idx,
+                         int32_t* idx_out, double* w_out, double* y) {
+  if (T < 0 || d < 1 || f < 1 || E < 1 || k < 1 || k > E || S < 0 ||
+      bad_dt(dt))
+    return -1;
+  if (!tok_list) n_tok = T;
+  if (n_tok < 0) return -1;
+  if (n_tok > 0 && (!x || !W_router || !W_gate_up || !W_down || !y)) return -1;
+  if (tok_list)
+    for (int64_t q = 0; q < n_tok; ++q)
+      if (tok_list[q] < 0 || tok_list[q] >= T) return -1;
+  if (forced_idx)
+    for (int64_t q = 0; q < n_tok * k; ++q)
+      if (forced_idx[q] < 0 || forced_idx[q] >= E) return -1;
+
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* xt = (double*)malloc(sizeof(double) * (size_t)d);
+    double* lg = (double*)malloc(sizeof(double) * (size_t)E);
+    ranked* order = (ranked*)malloc(sizeof(ranked) * (size_t)E);
+    double* act = (double*)malloc(sizeof(double) * (size_t)f);
+    double* out = (double*)malloc(sizeof(double) * (size_t)d);
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    double* w = (double*)malloc(sizeof(double) * (size_t)k);
+    if (!xt || !lg || !order || !act || !out || !idx || !w) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t q = 0; q < n_tok; ++q) {
+        int64_t t = tok_list ? tok_list[q] : q;
+        route_token(t, d, E, k, dt, x, W_router, bias,
+                    forced_idx ? forced_idx + q * k : NULL, xt, lg, order, idx,
+                    w);
+        /* route_token leaves x[t] widened in xt */
+        double* yt = y + q * d;
+        for (int64_t i = 0; i < d; ++i) yt[i] = 0.0;
+        /* y_t = sum_j w_j Expert_{idx_j}(x_t): selected experts only */
+        for (int64_t j = 0; j < k; ++j) {
+          expert_hidden(idx[j], d, f, dt, W_gate_up, xt, act);
+          expert_down(idx[j], d, f, dt, W_down, act, out);
+          for (int64_t i = 0; i < d; ++i) yt[i] += w[j] * out[i];
+        }
+        /* + every shared expert with weight one */
+        for (int64_t sg = 0; sg < S; ++sg) {
+          expert_hidden(E + sg, d, f, dt, W_gate_up, xt, act);
+          expert_down(E + sg, d, f, dt, W_down, act, out);
+          for (int64_t i = 0; i < d; ++i) yt[i] += out[i];
+        }
+        if (idx_out) memcpy(idx_out + q * k, idx, sizeof(int32_t) * (size_t)k);
+        if (w_out) memcpy(w_out + q * k, w, sizeof(double) * (size_t)k);
+      }
+    }
+    free(xt);
+    free(lg);
+    free(order);
+    free(act);
+    free(out);
+    free(idx);
+    free(w);
+  }
+  return fail ? -2 : 0;
+}

@@ -1,0 +1,109 @@
+/*
+ * oracle.h -- plain fp64 CPU definition of one sparse-routed MoE FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this library: only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header, table or
+ * helper with the HIP library; the two meet only in the seeded input buffers.
+ *
+ * What is computed, and where the pages define it:
+ *   - Router score per expert from a small linear layer, then softmax and
+ *     top-k (Baidu "MoE稀疏架构是什么" page, section 三.1 and the section 四
+ *     pseudocode; yunthe "分工的艺术" page, section 1.1 gating code; qqiyuan
+ *     2026 MoE guide, the MoELayer pseudocode).
+ *   - The selected weights renormalised to sum to one (Baidu page, section 四:
+ *     softmax taken over the top-k scores, which equals softmax-over-all then
+ *     renormalise over the selected experts).
+ *   - Token copies grouped by expert id (sort, then one grouped GEMM) and the
+ *     results gathered back to token order (aitoday "MoEs in Transformers"
+ *     page, section "Expert Backend", the grouped_mm backend).
+ *   - Packed expert tensors: gate_up_proj = experts stacked on dim 0 with w1
+ *     rows then w3 rows on dim 1, giving [E, 2f, d]; down_proj stacked on dim 0,
+ *     giving [E, d, f] (aitoday page, section "Dynamic Weight Loading with
+ *     WeightConverter").
+ *   - Output = weighted sum of the selected experts' outputs only (Baidu page,
+ *     section 四).
+ *
+ * Readings where the pages are silent (each one is listed with its reason in
+ * the design notes):
+ *   - expert function: SwiGLU, a = silu(gate) * up, silu(z) = z / (1 + e^-z),
+ *     then the down projection; no biases, no clamping, no scaling;
+ *   - ranking key: the fp64 logit, ties to the lower expert index; slot j of a
+ *     token holds its rank-j expert;
+ *   - optional router bias b[E] (fp32) added to the logits before softmax;
+ *   - shared experts: S extra experts stored after the E routed ones in both
+ *     weight tensors, weight 1 for every token, outside the softmax;
+ *   - permutation order inside one expert group: ascending slot id
+ *     s = t*k + j (stable counting sort); shared groups follow the routed ones
+ *     with rows T*k + sigma*T + t.
+ *
+ * Element types: dt = ORACLE_F32 (IEEE binary32) or ORACLE_BF16 (bfloat16,
+ * passed as its raw 16-bit pattern).  Every value is widened to fp64 before
+ * use and every sum is a serial fp64 sum in ascending index order.
+ *
+ * All pointers are host pointers owned by the caller.  Functions return 0 on
+ * success and a negative value for an invalid argument; nothing is allocated
+ * that outlives a call.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Routing of every token: fp64 logits[T,E] (optional, may be NULL), the top-k
+ * expert ids idx[T,k] in rank order and their renormalised weights w[T,k]. */
+int oracle_route(int64_t T, int64_t d, int64_t E, int64_t k, int dt,
+                 const void* x, const void* W_router, const float* bias,
+                 double* logits, int32_t* idx, double* w);
+
+/* Counting-sort permutation of the T*k token copies by expert id.
+ * counts[E+S], offsets[E+S+1], sorted_slot[T*k], slot_pos[T*k]. */
+int oracle_permute(int64_t T, int64_t k, int64_t E, int64_t S,
+                   const int32_t* idx, int32_t* counts, int32_t* offsets,
+                   int32_t* sorted_slot, int32_t* slot_pos);
+
+/* SwiGLU hidden activation of n (token, expert) pairs:
+ * act[r, :] = silu(Wgu[e, 0:f, :] x[t]) * (Wgu[e, f:2f, :] x[t]),
+ * with t = tok[r], e = expert[r].  act is [n, f] fp64. */
+int oracle_gate_up_rows(int64_t n, const int64_t* tok, const int32_t* expert,
+                        int64_t d, int64_t f, int dt, const void* x,
+                        const void* W_gate_up, double* act);
+
+/* Down projection of n given activation rows (element type dt, [n, f]):
+ * out[r, :] = W_down[expert[r]] act[r].  out is [n, d] fp64. */
+int oracle_down_rows(int64_t n, const int32_t* expert, int64_t d, int64_t f,
+                     int dt, const void* act, const void* W_down, double* out);
+
+/* Weighted combine of expert-output rows stored in permuted order
+ * (element type dt, [T*k + S*T, d]):
+ * y[t] = sum_j w[t,j] * O[slot_pos[t*k+j]] + sum_sigma O[T*k + sigma*T + t]. */
+int oracle_combine(int64_t T, int64_t k, int64_t S, int64_t d, int dt,
+                   const void* O, const int32_t* slot_pos, const double* w,
+                   double* y);
+
+/* The whole layer for n_tok listed tokens (tok_list == NULL: all T tokens, in
+ * order).  y is [n_tok, d] fp64; idx_out / w_out ([n_tok, k], optional) get
+ * the routing.  forced_idx ([n_tok, k], optional) replaces the selection by
+ * the given expert ids; their weights are then the softmax over the given
+ * experts' logits. */
+int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
+                         int64_t S, int dt, const void* x, const void* W_router,
+                         const float* bias, const void* W_gate_up,
+                         const void* W_down, int64_t n_tok,
+                         const int64_t* tok_list, const int32_t* forced_idx,
+                         int32_t* idx_out, double* w_out, double* y);
+
+/* Number of OpenMP threads the oracle uses (for reporting). */
+int oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ORACLE_H */

@@ -1,0 +1,376 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Every pin takes an oracle object (oracle.Oracle) so that the same checks run
+against the real oracle (test_oracle_pins.py) and against deliberately broken
+copies of it (test_oracle_mutants.py, which requires every planted mistake to
+fail at least one pin).
+
+What each pin rests on:
+  - hand-derived worked examples (tests/golden/worked_examples.json);
+  - closed forms: zero router -> all logits tie at 0; zero gate or zero up
+    projection -> output exactly 0; identical experts -> output independent of
+    the routing; a +100 bias forces a choice;
+  - exact integer arithmetic: small-integer inputs make every logit an exact
+    integer, so the selection is fixed by integer comparisons done in Python;
+  - brute force: on tiny inputs the top-k set is the k-subset with the largest
+    logit sum (ties: lexicographically smallest), found by enumeration;
+  - independent dense formulations in numpy: k = E is dense softmax gating
+    (yunthe page, section 1.1), and any k is a masked sum over all experts;
+  - library primitives: numpy's stable argsort / bincount / cumsum for the
+    permutation, numpy matmul for the logits;
+  - invariants the pages fix: renormalised weights sum to one; every token
+    appears exactly k times; unselected experts do no work (Baidu page,
+    section 四), so changing their weights changes nothing.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+import moe_synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "worked_examples.json")
+
+
+# ----------------------------------------------------------- test helpers
+
+def wide(a):
+    """Exact fp64 view of a float32 / bf16-bits array (format helper)."""
+    if a.dtype == np.uint16:
+        return moe_synth.bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, np.float64)
+
+
+def np_silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def np_dense_layer(x, Wr, Wgu, Wd, k, S=0, bias=None):
+    """Independent numpy formulation: every expert evaluated densely on every
+    token, then masked by the selection.  Selection by np.lexsort on
+    (expert index, -logit); weights = softmax over the selected logits."""
+    x, Wr, Wgu, Wd = wide(x), wide(Wr), wide(Wgu), wide(Wd)
+    T = x.shape[0]
+    E = Wr.shape[0]
+    f = Wgu.shape[1] // 2
+    L = x @ Wr.T
+    if bias is not None:
+        L = L + np.asarray(bias, np.float64)[None, :]
+    outs = []
+    for e in range(E + S):
+        g = x @ Wgu[e, :f, :].T
+        u = x @ Wgu[e, f:, :].T
+        outs.append((np_silu(g) * u) @ Wd[e].T)
+    outs = np.stack(outs)                       # [E+S, T, d]
+    y = np.zeros((T, x.shape[1]))
+    idx = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k))
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -L[t]))
+        sel = order[:k]
+        ls = L[t, sel]
+        ws = np.exp(ls - ls.max())
+        ws /= ws.sum()
+        idx[t] = sel
+        w[t] = ws
+        for j in range(k):
+            y[t] += ws[j] * outs[sel[j], t]
+        for s in range(S):
+            y[t] += outs[E + s, t]
+    return y, idx, w, L
+
+
+def rand_layer(key, T, d, f, E, k, S=0, dtype="f32", wstd=0.3):
+    seed = key
+    x = moe_synth.normal((seed, 5, 0), (T, d), 1.0, dtype)
+    Wr = moe_synth.normal((seed, 5, 1), (E, d), wstd, dtype)
+    Wgu = moe_synth.normal((seed, 5, 2), (E + S, 2 * f, d), wstd, dtype)
+    Wd = moe_synth.normal((seed, 5, 3), (E + S, d, f), wstd, dtype)
+    return x, Wr, Wgu, Wd
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(1e-300, np.max(np.abs(b))))
+
+
+# ------------------------------------------------------------------ pins
+
+def pin_golden_route(orc):
+    g = json.load(open(GOLDEN))
+    for name in ("route_topk_renorm", "route_ties_lower_index"):
+        c = g[name]
+        x = np.array(c["x"], np.float32)
+        Wr = np.array(c["W_router"], np.float32)
+        L, idx, w = orc.route(x, Wr, c["k"])
+        assert np.array_equal(L, np.array(c["logits"])), name
+        assert np.array_equal(idx, np.array(c["idx"])), name
+        assert np.allclose(w, np.array(c["w"]), rtol=0, atol=1e-15), name
+
+
+def pin_golden_layer(orc):
+    g = json.load(open(GOLDEN))
+    c = g["swiglu_expert"]
+    x = np.array(c["x"], np.float32)
+    Wgu = np.array(c["W_gate_up"], np.float32)
+    Wd = np.array(c["W_down"], np.float32)
+    Wr = np.zeros((1, 1), np.float32)
+    y, idx, w = orc.layer_forward(x, Wr, Wgu, Wd, 1)
+    assert abs(y[0, 0] - c["y"][0][0]) <= 1e-14, (y, c["y"])
+    assert abs(y[0, 0] - c["y_if_gate_up_swapped"][0][0]) > 0.5
+
+    c = g["two_expert_layer"]
+    x = np.array(c["x"], np.float32)
+    Wr = np.array(c["W_router"], np.float32)
+    E = Wr.shape[0]
+    Wgu = np.zeros((E, 2, 2), np.float32)
+    Wd = np.zeros((E, 2, 1), np.float32)
+    for e in range(E):
+        Wgu[e, 0, 0] = e + 1
+        Wgu[e, 1, 0] = 1
+        Wd[e, 0, 0] = e + 1
+    y, idx, w = orc.layer_forward(x, Wr, Wgu, Wd, c["k"])
+    assert np.array_equal(idx, np.array(c["idx"]))
+    assert np.allclose(y, np.array(c["y"]), rtol=0, atol=1e-14), y
+
+
+def pin_zero_router_ties(orc):
+    for E, k in ((8, 2), (8, 4), (6, 1), (16, 8)):
+        T, d = 16, 32
+        x = moe_synth.normal((11, 5, 0), (T, d), 1.0, "f32")
+        Wr = np.zeros((E, d), np.float32)
+        L, idx, w = orc.route(x, Wr, k)
+        assert np.all(L == 0.0)
+        assert np.array_equal(idx, np.tile(np.arange(k, dtype=np.int32), (T, 1)))
+        assert np.all(w == 1.0 / k)          # k a power of two: exact
+        counts, offsets, ss, sp = orc.permute(idx, E)
+        assert list(counts[:k]) == [T] * k and not counts[k:].any()
+        # group of expert j lists the tokens in order
+        for j in range(k):
+            grp = ss[offsets[j]:offsets[j + 1]]
+            assert np.array_equal(grp, np.arange(T) * k + j)
+
+
+def pin_duplicate_rows_tie(orc):
+    T, d, E = 32, 24, 8
+    x = moe_synth.normal((12, 5, 0), (T, d), 1.0, "f32")
+    Wr = moe_synth.normal((12, 5, 1), (E, d), 0.1, "f32")
+    Wr[5] = Wr[2]
+    bias = np.zeros(E, np.float32)
+    bias[2] = bias[5] = 50.0
+    for k in (1, 2, 3):
+        L, idx, w = orc.route(x, Wr, k, bias=bias)
+        assert np.all(idx[:, 0] == 2)
+        if k >= 2:
+            assert np.all(idx[:, 1] == 5)
+            assert np.all(w[:, 0] == w[:, 1])
+
+
+def pin_integer_exact_routing(orc):
+    T, d, E = 96, 16, 7
+    xi = moe_synth.small_ints((13, 5, 0), (T, d), -3, 3)
+    Wi = moe_synth.small_ints((13, 5, 1), (E, d), -3, 3)
+    for k in (1, 2, 3, 7):
+        L, idx, w = orc.route(xi, Wi, k)
+        for t in range(T):
+            li = [sum(int(xi[t, i]) * int(Wi[e, i]) for i in range(d)) for e in range(E)]
+            assert list(L[t]) == [float(v) for v in li]
+            ranked = sorted(range(E), key=lambda e: (-li[e], e))[:k]
+            assert list(idx[t]) == ranked, (t, li, idx[t], ranked)
+            m = max(li[e] for e in ranked)
+            ex = [math.exp(li[e] - m) for e in ranked]
+            ref = [v / sum(ex) for v in ex]
+            assert max(abs(a - b) for a, b in zip(w[t], ref)) <= 1e-15
+
+
+def pin_bruteforce_subsets(orc):
+    for dtype, seed in (("f32", 14), ("bf16", 15)):
+        T, d, E = 8, 10, 6
+        x = moe_synth.normal((seed, 5, 0), (T, d), 1.0, dtype)
+        Wr = moe_synth.normal((seed, 5, 1), (E, d), 0.5, dtype)
+        Lnp = wide(x) @ wide(Wr).T
+        for k in range(1, E + 1):
+            L, idx, w = orc.route(x, Wr, k)
+            assert np.allclose(L, Lnp, rtol=1e-13, atol=1e-13)
+            for t in range(T):
+                best = max(itertools.combinations(range(E), k),
+                           key=lambda c: (sum(L[t, e] for e in c), [-e for e in c]))
+                assert sorted(idx[t]) == list(best)
+                # slot order is rank order
+                assert all(L[t, idx[t, j]] >= L[t, idx[t, j + 1]] for j in range(k - 1))
+
+
+def pin_weights_renormalised(orc):
+    T, d, E = 64, 40, 12
+    x = moe_synth.normal((16, 5, 0), (T, d), 1.0, "bf16")
+    Wr = moe_synth.normal((16, 5, 1), (E, d), 0.2, "bf16")
+    for k in (1, 3, 5, 12):
+        L, idx, w = orc.route(x, Wr, k)
+        assert np.all(np.abs(w.sum(1) - 1.0) <= 1e-15)
+        assert np.all(np.diff(w, axis=1) <= 0)
+        # top-k then softmax over the k picked scores (Baidu page, section 四)
+        sel = np.take_along_axis(L, idx.astype(np.int64), 1)
+        ref = np.exp(sel - sel.max(1, keepdims=True))
+        ref /= ref.sum(1, keepdims=True)
+        assert np.max(np.abs(w - ref)) <= 1e-15
+
+
+def pin_dense_gating_k_equals_E(orc):
+    T, d, f, E = 5, 6, 4, 4
+    x, Wr, Wgu, Wd = rand_layer(17, T, d, f, E, E)
+    y, idx, w = orc.layer_forward(x, Wr, Wgu, Wd, E)
+    # dense soft gating over all experts (yunthe page, section 1.1)
+    xd, Wrd, Wgud, Wdd = wide(x), wide(Wr), wide(Wgu), wide(Wd)
+    L = xd @ Wrd.T
+    p = np.exp(L - L.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    yd = np.zeros((T, d))
+    for e in range(E):
+        h = np_silu(xd @ Wgud[e, :f].T) * (xd @ Wgud[e, f:].T)
+        yd += p[:, e:e + 1] * (h @ Wdd[e].T)
+    assert rel_err(y, yd) <= 1e-12
+
+
+def pin_dense_masked_bruteforce(orc):
+    for (T, d, f, E, k, S, dt, seed) in ((7, 8, 6, 5, 2, 0, "f32", 18),
+                                         (9, 8, 8, 6, 3, 1, "bf16", 19),
+                                         (6, 5, 7, 4, 1, 2, "f32", 20)):
+        x, Wr, Wgu, Wd = rand_layer(seed, T, d, f, E, k, S, dt)
+        bias = np.linspace(0.3, -0.4, E).astype(np.float32)
+        y, idx, w = orc.layer_forward(x, Wr, Wgu, Wd, k, S=S, bias=bias)
+        yd, idxd, wd, _ = np_dense_layer(x, Wr, Wgu, Wd, k, S=S, bias=bias)
+        assert np.array_equal(idx, idxd)
+        assert np.max(np.abs(w - wd)) <= 1e-14
+        assert rel_err(y, yd) <= 1e-12, rel_err(y, yd)
+
+
+def pin_identical_experts(orc):
+    T, d, f, E, k = 12, 10, 6, 5, 3
+    x, Wr, Wgu, Wd = rand_layer(21, T, d, f, E, k)
+    Wgu[:] = Wgu[0]
+    Wd[:] = Wd[0]
+    y, idx, w = orc.layer_forward(x, Wr, Wgu, Wd, k)
+    xd = wide(x)
+    h = np_silu(xd @ wide(Wgu[0, :f]).T) * (xd @ wide(Wgu[0, f:]).T)
+    assert rel_err(y, h @ wide(Wd[0]).T) <= 1e-13
+
+
+def pin_zero_gate_or_up(orc):
+    T, d, f, E, k = 10, 12, 8, 4, 2
+    for half in (0, 1):
+        x, Wr, Wgu, Wd = rand_layer(22 + half, T, d, f, E, k, S=1)
+        Wgu[:, half * f:(half + 1) * f, :] = 0
+        y, idx, w = orc.layer_forward(x, Wr, Wgu, Wd, k, S=1)
+        assert np.all(y == 0.0)
+
+
+def pin_onehot_bias(orc):
+    T, d, E = 40, 16, 9
+    x = moe_synth.normal((24, 5, 0), (T, d), 1.0, "f32")
+    Wr = moe_synth.normal((24, 5, 1), (E, d), 0.3, "f32")
+    for e_star in (0, 4, 8):
+        bias = np.zeros(E, np.float32)
+        bias[e_star] = 100.0
+        L, idx, w = orc.route(x, Wr, 3, bias=bias)
+        assert np.all(idx[:, 0] == e_star)
+        assert np.all(w[:, 0] > 0.999)
+
+
+def pin_permutation(orc):
+    rng = np.random.default_rng([25, 5, 0])
+    for (T, k, E, S) in ((50, 3, 7, 0), (64, 8, 16, 1), (1, 1, 1, 0), (33, 2, 40, 2),
+                         (0, 2, 4, 0)):
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32) \
+            if T else np.zeros((0, k), np.int32)
+        counts, offsets, ss, sp = orc.permute(idx, E, S)
+        flat = idx.ravel()
+        assert np.array_equal(counts[:E], np.bincount(flat, minlength=E))
+        assert np.all(counts[E:] == T)
+        assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+        assert offsets[E] == T * k and offsets[E + S] == T * k + S * T
+        assert np.array_equal(ss, np.argsort(flat, kind="stable"))
+        assert np.array_equal(sp[ss], np.arange(T * k))
+        assert np.array_equal(np.sort(ss), np.arange(T * k))
+        tok_counts = np.bincount(ss // k, minlength=T) if T else np.zeros(0)
+        assert np.all(tok_counts == k)
+
+
+def pin_unselected_do_nothing(orc):
+    T, d, f, E, k = 20, 12, 8, 8, 2
+    x, Wr, Wgu, Wd = rand_layer(26, T, d, f, E, k)
+    bias = np.zeros(E, np.float32)
+    bias[5:] = -100.0
+    y0, idx, w0 = orc.layer_forward(x, Wr, Wgu, Wd, k, bias=bias)
+    assert np.all(idx < 5)
+    Wgu2, Wd2 = Wgu.copy(), Wd.copy()
+    Wgu2[5:] *= -3.0
+    Wd2[5:] += 1.0
+    y1, _, _ = orc.layer_forward(x, Wr, Wgu2, Wd2, k, bias=bias)
+    assert np.array_equal(y0, y1)
+
+
+def pin_bf16_widening(orc):
+    T, d, f, E, k = 9, 16, 8, 5, 2
+    x, Wr, Wgu, Wd = rand_layer(27, T, d, f, E, k, S=1, dtype="bf16")
+    as32 = [moe_synth.bf16_bits_to_f32(a) for a in (x, Wr, Wgu, Wd)]
+    yb, ib, wb = orc.layer_forward(x, Wr, Wgu, Wd, k, S=1)
+    yf, i_f, wf = orc.layer_forward(*as32, k, S=1)
+    assert np.array_equal(ib, i_f) and np.array_equal(wb, wf) and np.array_equal(yb, yf)
+    # and bf16 patterns really are the upper half of binary32
+    one = np.array([[0x3F80]], np.uint16)   # 1.0
+    half = np.array([[0xBF00]], np.uint16)  # -0.5
+    L, _, _ = orc.route(one, half, 1)
+    assert L[0, 0] == -0.5
+
+
+def pin_decomposed_path(orc):
+    """route -> permute -> gate_up -> down -> combine equals the whole layer;
+    combine on rows of known values equals its closed form."""
+    T, d, f, E, k, S = 11, 8, 6, 5, 2, 1
+    x, Wr, Wgu, Wd = rand_layer(28, T, d, f, E, k, S)
+    y, idx, w = orc.layer_forward(x, Wr, Wgu, Wd, k, S=S)
+    L, idx2, w2 = orc.route(x, Wr, k)
+    assert np.array_equal(idx, idx2) and np.array_equal(w, w2)
+    counts, offsets, ss, sp = orc.permute(idx2, E, S)
+    R = T * k + S * T
+    tok = np.concatenate([ss // k, np.tile(np.arange(T), S)]).astype(np.int64)
+    ex = np.concatenate([idx2.ravel()[ss],
+                         np.repeat(np.arange(E, E + S), T)]).astype(np.int32)
+    act = orc.gate_up_rows(x, Wgu, tok, ex)
+    O = orc.down_rows(act.astype(np.float32), Wd, ex)
+    y2 = orc.combine(O.astype(np.float32), sp, w2, T, k, S)
+    assert rel_err(y2, y) <= 1e-5
+    # closed form of the combine: O rows filled with their row number
+    Orow = np.repeat(np.arange(R, dtype=np.float32)[:, None], d, 1)
+    yc = orc.combine(Orow, sp, w2, T, k, S)
+    exp = (w2 * sp.reshape(T, k)).sum(1) + sum(T * k + s * T + np.arange(T) for s in range(S))
+    assert np.max(np.abs(yc - exp[:, None])) <= 1e-12
+
+
+def pin_sharding_identity(orc):
+    """Experts split into disjoint ranges: the partial outputs sum to the full
+    output (aitoday page, section 'Expert Parallelism': each device computes
+    with its own experts, partial outputs are all-reduced)."""
+    T, d, f, E, k = 16, 8, 6, 8, 3
+    x, Wr, Wgu, Wd = rand_layer(29, T, d, f, E, k)
+    y, idx, w = orc.layer_forward(x, Wr, Wgu, Wd, k)
+    counts, offsets, ss, sp = orc.permute(idx, E)
+    tok = (ss // k).astype(np.int64)
+    ex = idx.ravel()[ss]
+    O = orc.down_rows(orc.gate_up_rows(x, Wgu, tok, ex).astype(np.float32), Wd, ex)
+    total = np.zeros((T, d))
+    for lo, hi in ((0, 3), (3, 5), (5, 8)):
+        part = np.zeros_like(O, dtype=np.float32)
+        rows = slice(offsets[lo], offsets[hi])
+        part[rows] = O[rows]
+        total += orc.combine(part, sp, w, T, k)
+    full = orc.combine(O.astype(np.float32), sp, w, T, k)
+    assert rel_err(total, full) <= 1e-12
+    assert rel_err(full, y) <= 1e-5
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

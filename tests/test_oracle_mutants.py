@@ -1,0 +1,92 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and require
+every one of them to fail at least one pin.  This shows the pins constrain
+each part of the oracle rather than restating it."""
+import os
+import shutil
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(obuild.__file__), "oracle.c")
+
+MUTANTS = {
+    "gate_up_halves_swapped": (
+        "double g = dot_row(W_gate_up, dt, base + n, d, xt);\n"
+        "    double u = dot_row(W_gate_up, dt, base + f + n, d, xt);",
+        "double g = dot_row(W_gate_up, dt, base + f + n, d, xt);\n"
+        "    double u = dot_row(W_gate_up, dt, base + n, d, xt);"),
+    "no_renormalisation": (
+        "w[j] = (exp(logit[idx[j]] - m) / z) / sel;",
+        "w[j] = (exp(logit[idx[j]] - m) / z);"),
+    "ties_to_higher_index": (
+        "return (a->e > b->e) - (a->e < b->e);",
+        "return (a->e < b->e) - (a->e > b->e);"),
+    "rank_ascending": (
+        "if (a->logit > b->logit) return -1;\n  if (a->logit < b->logit) return 1;",
+        "if (a->logit > b->logit) return 1;\n  if (a->logit < b->logit) return -1;"),
+    "shared_expert_dropped": (
+        "for (int64_t sg = 0; sg < S; ++sg) {\n          expert_hidden",
+        "for (int64_t sg = 0; sg < 0; ++sg) {\n          expert_hidden"),
+    "down_proj_transposed": (
+        "out[i] = dot_row(W_down, dt, e * d + i, f, act);",
+        "{ double s_ = 0.0; for (int64_t n_ = 0; n_ < f; ++n_) "
+        "s_ += elem(W_down, dt, e * d * f + n_ * d + i) * act[n_]; out[i] = s_; }"),
+    "silu_sign": (
+        "double silu = g / (1.0 + exp(-g));",
+        "double silu = g / (1.0 + exp(g));"),
+    "bias_ignored": (
+        "if (bias) logit[e] += (double)bias[e];",
+        "(void)bias;"),
+    "unstable_scatter": (
+        "for (int64_t s = 0; s < n; ++s) {\n    int32_t e = idx[s];",
+        "for (int64_t s = n - 1; s >= 0; --s) {\n    int32_t e = idx[s];"),
+    "bf16_shift_wrong": (
+        "uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 16;",
+        "uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 15;"),
+    "combine_first_weight_only": (
+        "acc += w[t * k + j] * elem(O, dt, row * d + i);",
+        "acc += w[t * k] * elem(O, dt, row * d + i);"),
+    "router_uses_wrong_row": (
+        "logit[e] = dot_row(W_router, dt, e, d, xt);",
+        "logit[e] = dot_row(W_router, dt, E - 1 - e, d, xt);"),
+    "gate_up_expert_stride_wrong": (
+        "int64_t base = e * 2 * f;",
+        "int64_t base = e * f;"),
+    "shared_rows_misplaced": (
+        "int64_t row = T * k + sg * T + t;",
+        "int64_t row = T * k + sg * T + (T - 1 - t);"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+def test_mutations_apply_to_current_source():
+    src = open(SRC).read()
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) == 1, f"mutation {name} no longer matches oracle.c"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_dir):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1
+    d = mutant_dir / name
+    d.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(SRC), "oracle.h"), d / "oracle.h")
+    (d / "oracle.c").write_text(src.replace(old, new))
+    lib = obuild.build(src=str(d / "oracle.c"), lib=str(d / "liboracle.so"))
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"
