@@ -1,0 +1,230 @@
+"""Benchmark of one MoE FFN layer forward (router -> top-k -> permutation ->
+grouped SwiGLU GEMMs -> combine) through libmoe's C ABI on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--no-cpu]
+
+A step is one moe_layer_forward over one batch of seeded synthetic inputs
+already resident in HBM.  Default workload: the gpt-oss-20b-shaped decode
+layer (T=16, d=2880, f=2880, E=32, top-4, bf16).  Prints ONE JSON line:
+tokens/s of the whole layer, the roofline of the dominant kernel (the
+gate_up grouped GEMM, HBM-bound at decode) measured with HIP events on the
+stream the kernels run on, and the fp64 CPU oracle's rate on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_sparse_router_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=2,
+                   help="workload 1..5 (2 = gpt-oss-20b-shaped decode, the headline)")
+    p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def alg_counts(cfg, counts):
+    """Algorithmic bytes / flops of the layer and of each GEMM, from the
+    actual routing: active experts' weights read once, router weights, x in,
+    y out; GEMM flops over the routed + shared rows."""
+    b = 4 if cfg.dtype == "f32" else 2
+    G = cfg.E + cfg.S
+    active = int(sum(1 for g in range(G) if counts[g] > 0))
+    R = cfg.T * cfg.k + cfg.S * cfg.T
+    w_gu = active * 2 * cfg.f * cfg.d * b
+    w_d = active * cfg.d * cfg.f * b
+    layer_bytes = w_gu + w_d + cfg.E * cfg.d * b + 2 * cfg.T * cfg.d * b
+    gate_up_bytes = w_gu + cfg.T * cfg.d * b + R * cfg.f * b
+    down_bytes = w_d + R * cfg.f * b + R * cfg.d * b
+    layer_flops = 2 * cfg.T * cfg.d * cfg.E + 6 * cfg.d * cfg.f * R
+    return dict(active=active, R=R, layer_bytes=layer_bytes, gate_up_bytes=gate_up_bytes,
+                down_bytes=down_bytes, layer_flops=layer_flops,
+                gate_up_flops=4 * cfg.d * cfg.f * R, down_flops=2 * cfg.d * cfg.f * R)
+
+
+def time_calls(torch, fn, n):
+    """Average GPU time of fn() over n back-to-back calls, HIP events recorded
+    on the current stream (the stream every call enqueues on)."""
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(n):
+        fn()
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n * 1e-3  # seconds
+
+
+def load_traffic(key):
+    """HBM traffic of the dominant kernel from committed rocprofv3 --pmc
+    counters, valid only while the kernel source is unchanged."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(key)
+    if not ent:
+        return None
+    src_hash = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    if ent.get("gemm_src_sha256_16") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, seconds):
+    import numpy as np
+    import oracle
+    T = cfg.T
+    toks = np.arange(T)
+    per_call = min(T, 16)
+    n_done = 0
+    t0 = time.perf_counter()
+    calls = 0
+    while True:
+        sel = toks[(calls * per_call) % T:][:per_call]
+        oracle.layer_forward(inp["x"], inp["W_router"], inp["W_gate_up"], inp["W_down"],
+                             cfg.k, S=cfg.S, bias=inp["bias"], tokens=sel)
+        n_done += len(sel)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return dict(value=n_done / el, unit="tokens/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=f"{n_done} tokens of the same workload in {calls} oracle calls of "
+                       f"<= {per_call} tokens, {el:.1f} s wall")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import moe_synth
+    import mixture_experts_sparse_router_amd as moe
+
+    cfg = moe_synth.CONFIGS[args.config]
+    seed = args.seed if args.seed is not None else args.config
+    torch.cuda.set_device(0)
+    inp = moe_synth.make_layer_inputs(cfg, seed)
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    d = {k: dev(v) for k, v in inp.items()}
+    dt = moe.MOE_DT_BF16 if cfg.dtype == "bf16" else moe.MOE_DT_F32
+    s = moe.shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.S, dt)
+    ws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
+    y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16 if dt else torch.float32,
+                    device="cuda")
+    views = moe.workspace_views(s, ws)
+
+    def step():
+        moe.moe_layer_forward(s, d["x"], d["W_router"], d["bias"], d["W_gate_up"],
+                              d["W_down"], y, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_per_step = el / args.steps * 1e3
+    tok_s = cfg.T * args.steps / el
+
+    counts = views["counts"].cpu().numpy()
+    ac = alg_counts(cfg, counts)
+
+    # per-step kernel times (each entry point timed alone on the same buffers)
+    n = max(20, args.steps)
+    kt = {
+        "route": time_calls(torch, lambda: moe.moe_route(
+            s, d["x"], d["W_router"], d["bias"], views["topk_idx"], views["topk_w"]), n),
+        "permute": time_calls(torch, lambda: moe.moe_permute(
+            s, views["topk_idx"], views["counts"], views["offsets"], views["sorted_slot"],
+            views["slot_pos"]), n),
+        "gate_up": time_calls(torch, lambda: moe.moe_grouped_gemm_gate_up(
+            s, d["x"], views["sorted_slot"], views["offsets"], d["W_gate_up"],
+            views["act"]), n),
+        "down": time_calls(torch, lambda: moe.moe_grouped_gemm_down(
+            s, views["act"], views["offsets"], d["W_down"], views["expert_out"]), n),
+        "combine": time_calls(torch, lambda: moe.moe_combine(
+            s, views["expert_out"], views["slot_pos"], views["topk_w"], y), n),
+    }
+    torch.cuda.synchronize()
+
+    decode = cfg.T <= 64 and dt == moe.MOE_DT_BF16
+    if decode or dt == moe.MOE_DT_F32:
+        bound, unit = "hbm", "GB/s"
+        achieved = ac["gate_up_bytes"] / kt["gate_up"] / 1e9
+        peak = HBM_PEAK_GBS
+    else:
+        bound, unit = "mfma", "TFLOP/s"
+        achieved = ac["gate_up_flops"] / kt["gate_up"] / 1e12
+        peak = BF16_PEAK_TFLOPS
+    roof = dict(bound=bound, kernel="grouped_gemm_gate_up", achieved=round(achieved, 2),
+                peak=peak, unit=unit, frac=round(achieved / peak, 4),
+                traffic=load_traffic(cfg.name),
+                alg_bytes_per_launch=ac["gate_up_bytes"],
+                alg_flops_per_launch=ac["gate_up_flops"],
+                avg_launch_us=round(kt["gate_up"] * 1e6, 2))
+
+    layer_s = ms_per_step * 1e-3
+    out = {
+        "metric": "MoE layer tokens/s",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
+                   "k": cfg.k, "shared": cfg.S, "zipf_s": cfg.zipf_s, "seed": seed,
+                   "active_experts": ac["active"], "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"alg_bytes": ac["layer_bytes"], "alg_flops": ac["layer_flops"],
+                  "hbm_frac": round(ac["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(ac["layer_flops"] / layer_s / 1e12 /
+                                     (BF16_PEAK_TFLOPS if dt else FP32_PEAK_TFLOPS), 4),
+                  "kernel_us": {k: round(v * 1e6, 2) for k, v in kt.items()}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE feed-forward layer library.
+ *
+ * One sparse-routed Mixture-of-Experts FFN layer, forward pass, in five steps:
+ *
+ *   1. router logits      L[t,e] = sum_i x[t,i] W_router[e,i] (+ bias[e])
+ *   2. routing            softmax over the E experts, the k largest taken
+ *                         (ties to the lower expert index), their
+ *                         probabilities renormalised to sum to one
+ *   3. permutation        token copies grouped by expert: per-expert
+ *                         histogram, exclusive prefix sum, stable scatter
+ *   4. expert FFN         grouped GEMMs over the variable-size groups:
+ *                         act = silu(x W_gate^T) * (x W_up^T), out = act W_down^T
+ *   5. combine            y[t] = sum_j w[t,j] out[copy (t,j)] (+ shared experts)
+ *
+ * Where the pages define each step:
+ *   - router = small linear layer scoring every expert, then softmax and
+ *     top-k: Baidu "MoE稀疏架构是什么" page, section 三.1 and the section 四
+ *     pseudocode; qqiyuan 2026 MoE guide, MoELayer pseudocode; yunthe
+ *     "分工的艺术" page, section 1.1;
+ *   - renormalised top-k weights and the weighted sum over the selected
+ *     experts only: Baidu page, section 四;
+ *   - sort tokens by expert id, group them, one grouped GEMM, then apply the
+ *     routing weights and gather/reorder back: aitoday "MoEs in
+ *     Transformers" page, section "Expert Backend" (grouped_mm);
+ *   - packed expert weights, gate_up_proj [E, 2f, d] (w1 rows then w3 rows)
+ *     and down_proj [E, d, f]: aitoday page, section "Dynamic Weight Loading
+ *     with WeightConverter".
+ * The expert function (SwiGLU), the tie rule, shared experts and the router
+ * bias are readings where the pages are silent; they are stated at each call.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library allocates and frees nothing and keeps no state between calls.
+ *   - Tensors are dense row-major, last dimension contiguous, 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work; results are valid once the stream is
+ *     synchronised.  No call synchronises the host.
+ *   - Arguments are checked on the host before any HIP call; a rejected call
+ *     enqueues nothing.  Launch failures are reported as MOE_ERR_HIP.
+ *   - Element type: dt = MOE_DT_BF16 (bfloat16) or MOE_DT_F32 (binary32) for
+ *     x, W_router, W_gate_up, W_down, act, expert_out and y alike.  Routing
+ *     weights are always float32, indices int32.
+ *   - Numerics: router logits are accumulated in fp64; GEMMs multiply in dt
+ *     and accumulate in fp32; act and expert_out are rounded to dt (round to
+ *     nearest even); the combine accumulates in fp32 in a fixed order, so
+ *     repeated calls are bitwise identical.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* bad size, null or misaligned pointer       */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the library handles */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than moe_workspace_size  */
+  MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed         */
+} moe_status;
+
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+
+/* Layer shape.
+ *   T        tokens (rows of x), T >= 0
+ *   d        model dimension, multiple of 8
+ *   f        expert FFN dimension, multiple of 8
+ *   E        routed experts, 1 <= E
+ *   k        experts per token, 1 <= k <= E
+ *   n_shared always-on shared experts S >= 0 with E + S <= 1024; they are
+ *            stored after the routed experts in W_gate_up / W_down, get
+ *            weight 1 for every token and take no part in the softmax
+ *   dt       moe_dtype of the float tensors
+ * Derived: R = T*k + S*T rows of the permuted buffers; R < 2^31. */
+typedef struct {
+  int64_t T, d, f, E, k, n_shared;
+  int32_t dt;
+} moe_shape;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int status);
+
+/* Library version string, e.g. "moe-gfx950 1.0". */
+const char* moe_version(void);
+
+/* Text of the last HIP error an entry point of this library met on the
+ * calling thread ("no error" if none); use it after MOE_ERR_HIP. */
+const char* moe_last_hip_error(void);
+
+/* ---------------------------------------------------------------- step 1+2
+ * moe_route: router logits and top-k routing of every token.
+ *   x         [T, d]  dt
+ *   W_router  [E, d]  dt
+ *   bias      [E] float32 added to the logits, or NULL (reading: used only
+ *             to give a router prior, e.g. a Zipf-skewed load)
+ *   topk_idx  [T, k]  int32 out: slot j of token t holds its rank-j expert
+ *             (larger logit first; equal logits, lower index first)
+ *   topk_w    [T, k]  float32 out: softmax probabilities of the selected
+ *             experts renormalised over the k of them (each row sums to 1)
+ * Logits are accumulated in fp64 and ranked in fp64. */
+int moe_route(const moe_shape* s, const void* x, const void* W_router,
+              const float* bias, int32_t* topk_idx, float* topk_w,
+              void* stream);
+
+/* ------------------------------------------------------------------ step 3
+ * moe_permute: group the T*k token copies by expert.
+ * Copy s = t*k + j goes to expert topk_idx[s].
+ *   counts      [E+S]   int32 out: copies per expert; every shared expert
+ *               counts T
+ *   offsets     [E+S+1] int32 out: exclusive prefix sum of counts
+ *               (offsets[E] = T*k, offsets[E+S] = R)
+ *   sorted_slot [T*k]   int32 out: row r < T*k of the permuted buffers holds
+ *               copy sorted_slot[r]; inside one expert the copies are in
+ *               ascending s (stable).  Rows T*k + sigma*T + t (shared expert
+ *               sigma, token t) are implicit and not stored.
+ *   slot_pos    [T*k]   int32 out: inverse map, row of copy s
+ * topk_idx entries must lie in [0, E). */
+int moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
+                void* stream);
+
+/* ------------------------------------------------------------------ step 4
+ * moe_grouped_gemm_gate_up: first expert GEMM with the SwiGLU epilogue.
+ * For every row r of expert group e (offsets[e] <= r < offsets[e+1]):
+ *   token t = sorted_slot[r] / k          (r <  T*k)
+ *           = (r - T*k) % T               (shared rows)
+ *   act[r, n] = silu(g) * u,  g = W_gate_up[e, n, :] . x[t, :],
+ *                             u = W_gate_up[e, f + n, :] . x[t, :],
+ *   silu(z) = z / (1 + exp(-z)), 0 <= n < f.
+ *   W_gate_up [E+S, 2f, d] dt   act [R, f] dt out.
+ * Experts with no rows read none of their weights. */
+int moe_grouped_gemm_gate_up(const moe_shape* s, const void* x,
+                             const int32_t* sorted_slot, const int32_t* offsets,
+                             const void* W_gate_up, void* act, void* stream);
+
+/* moe_grouped_gemm_down: second expert GEMM.
+ *   expert_out[r, i] = W_down[e, i, :] . act[r, :] for the rows of group e.
+ *   act [R, f] dt,  W_down [E+S, d, f] dt,  expert_out [R, d] dt out. */
+int moe_grouped_gemm_down(const moe_shape* s, const void* act,
+                          const int32_t* offsets, const void* W_down,
+                          void* expert_out, void* stream);
+
+/* moe_grouped_gemm: both expert GEMMs (gate_up + SwiGLU, then down). */
+int moe_grouped_gemm(const moe_shape* s, const void* x,
+                     const int32_t* sorted_slot, const int32_t* offsets,
+                     const void* W_gate_up, const void* W_down, void* act,
+                     void* expert_out, void* stream);
+
+/* ------------------------------------------------------------------ step 5
+ * moe_combine: weighted un-permute back to token order.
+ *   y[t] = sum_{j<k} topk_w[t,j] * expert_out[slot_pos[t*k+j]]
+ *        + sum_{sigma<S} expert_out[T*k + sigma*T + t]
+ * accumulated in fp32 in that fixed order (no atomics), rounded to dt.
+ *   expert_out [R, d] dt,  slot_pos [T*k],  topk_w [T, k],  y [T, d] dt out. */
+int moe_combine(const moe_shape* s, const void* expert_out,
+                const int32_t* slot_pos, const float* topk_w, void* y,
+                void* stream);
+
+/* ------------------------------------------------------------- whole layer
+ * moe_layer_forward: steps 1-5 enqueued back to back on one stream.
+ * Intermediates live in the caller's workspace (device memory of at least
+ * moe_workspace_size(s) bytes, 256-byte aligned); its layout is given by
+ * moe_workspace_offsets.  y [T, d] dt out. */
+size_t moe_workspace_size(const moe_shape* s);
+
+enum {
+  MOE_WS_TOPK_IDX = 0, /* int32 [T, k]     */
+  MOE_WS_TOPK_W,       /* float [T, k]     */
+  MOE_WS_COUNTS,       /* int32 [E+S]      */
+  MOE_WS_OFFSETS,      /* int32 [E+S+1]    */
+  MOE_WS_SORTED_SLOT,  /* int32 [T*k]      */
+  MOE_WS_SLOT_POS,     /* int32 [T*k]      */
+  MOE_WS_ACT,          /* dt    [R, f]     */
+  MOE_WS_EXPERT_OUT,   /* dt    [R, d]     */
+  MOE_WS_COUNT
+};
+
+/* Byte offsets of the intermediates inside the workspace; out has
+ * MOE_WS_COUNT entries.  Returns MOE_OK or MOE_ERR_INVALID_ARG. */
+int moe_workspace_offsets(const moe_shape* s, size_t* out);
+
+int moe_layer_forward(const moe_shape* s, const void* x, const void* W_router,
+                      const float* bias, const void* W_gate_up,
+                      const void* W_down, void* y, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,211 @@
+// abi.hip -- the C entry points of libmoe: argument checks, workspace layout
+// and the stream-ordered launch sequence of the layer.  The steps and where
+// the pages define them are documented in include/moe.h.
+#include <string.h>
+
+#include "moe_common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int64_t kMaxGroups = 1024;
+constexpr int64_t kMaxK = 64;
+constexpr int64_t kMaxRows = (int64_t)1 << 31;
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Non-null and 16-byte aligned, unless the tensor is empty.
+inline bool ok_ptr(const void* p, int64_t elems) {
+  if (elems == 0) return true;
+  return p != nullptr && aligned16(p);
+}
+
+inline int64_t esize(const Shape& s) { return s.dt == MOE_DT_BF16 ? 2 : 4; }
+
+int check_shape(const moe_shape* m) {
+  if (!m) return MOE_ERR_INVALID_ARG;
+  if (m->T < 0 || m->d < 1 || m->f < 1 || m->E < 1 || m->k < 1 || m->k > m->E ||
+      m->n_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (m->dt != MOE_DT_F32 && m->dt != MOE_DT_BF16) return MOE_ERR_INVALID_ARG;
+  if (m->d % 8 != 0 || m->f % 8 != 0) return MOE_ERR_INVALID_ARG;
+  if (m->E + m->n_shared > kMaxGroups) return MOE_ERR_UNSUPPORTED;
+  if (m->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (m->d > ((int64_t)1 << 30) || m->f > ((int64_t)1 << 30)) return MOE_ERR_UNSUPPORTED;
+  if (m->T >= kMaxRows / (m->k + m->n_shared)) return MOE_ERR_UNSUPPORTED;  // R < 2^31
+  return MOE_OK;
+}
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+inline int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = e;
+  return MOE_ERR_HIP;
+}
+
+inline size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+void layout(const Shape& s, size_t* off, size_t* total) {
+  const size_t Tk = (size_t)s.Tk();
+  const size_t R = (size_t)s.R();
+  const size_t G = (size_t)s.G();
+  const size_t sizes[MOE_WS_COUNT] = {
+      Tk * 4, Tk * 4, G * 4, (G + 1) * 4, Tk * 4, Tk * 4,
+      R * (size_t)s.f * (size_t)esize(s), R * (size_t)s.d * (size_t)esize(s)};
+  size_t at = 0;
+  for (int i = 0; i < MOE_WS_COUNT; ++i) {
+    off[i] = at;
+    at += round_up(sizes[i]);
+  }
+  *total = at;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_version(void) { return "moe-gfx950 1.0"; }
+
+const char* moe_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
+
+size_t moe_workspace_size(const moe_shape* m) {
+  if (check_shape(m) != MOE_OK) return 0;
+  size_t off[MOE_WS_COUNT], total;
+  layout(to_shape(m), off, &total);
+  return total;
+}
+
+int moe_workspace_offsets(const moe_shape* m, size_t* out) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  if (!out) return MOE_ERR_INVALID_ARG;
+  size_t total;
+  layout(to_shape(m), out, &total);
+  return MOE_OK;
+}
+
+int moe_route(const moe_shape* m, const void* x, const void* W_router, const float* bias,
+              int32_t* topk_idx, float* topk_w, void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(x, s.T * s.d) || !ok_ptr(W_router, s.E * s.d) ||
+      !ok_ptr(topk_idx, s.Tk()) || !ok_ptr(topk_w, s.Tk()))
+    return MOE_ERR_INVALID_ARG;
+  if (bias && ((uintptr_t)bias & 3u)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_route(s, x, W_router, bias, topk_idx, topk_w, (hipStream_t)stream));
+}
+
+int moe_permute(const moe_shape* m, const int32_t* topk_idx, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(topk_idx, s.Tk()) || !ok_ptr(counts, s.G()) || !ok_ptr(offsets, s.G() + 1) ||
+      !ok_ptr(sorted_slot, s.Tk()) || !ok_ptr(slot_pos, s.Tk()))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_permute(s, topk_idx, counts, offsets, sorted_slot, slot_pos,
+                                   (hipStream_t)stream));
+}
+
+int moe_grouped_gemm_gate_up(const moe_shape* m, const void* x, const int32_t* sorted_slot,
+                             const int32_t* offsets, const void* W_gate_up, void* act,
+                             void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(x, s.T * s.d) || !ok_ptr(sorted_slot, s.Tk()) || !ok_ptr(offsets, s.G() + 1) ||
+      !ok_ptr(W_gate_up, s.G() * 2 * s.f * s.d) || !ok_ptr(act, s.R() * s.f))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(
+      launch_gate_up(s, x, sorted_slot, offsets, W_gate_up, act, (hipStream_t)stream));
+}
+
+int moe_grouped_gemm_down(const moe_shape* m, const void* act, const int32_t* offsets,
+                          const void* W_down, void* expert_out, void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(act, s.R() * s.f) || !ok_ptr(offsets, s.G() + 1) ||
+      !ok_ptr(W_down, s.G() * s.d * s.f) || !ok_ptr(expert_out, s.R() * s.d))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_down(s, act, offsets, W_down, expert_out, (hipStream_t)stream));
+}
+
+int moe_grouped_gemm(const moe_shape* m, const void* x, const int32_t* sorted_slot,
+                     const int32_t* offsets, const void* W_gate_up, const void* W_down,
+                     void* act, void* expert_out, void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(x, s.T * s.d) || !ok_ptr(sorted_slot, s.Tk()) || !ok_ptr(offsets, s.G() + 1) ||
+      !ok_ptr(W_gate_up, s.G() * 2 * s.f * s.d) || !ok_ptr(W_down, s.G() * s.d * s.f) ||
+      !ok_ptr(act, s.R() * s.f) || !ok_ptr(expert_out, s.R() * s.d))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_gate_up(s, x, sorted_slot, offsets, W_gate_up, act, st);
+  if (e == hipSuccess) e = launch_down(s, act, offsets, W_down, expert_out, st);
+  return hip_status(e);
+}
+
+int moe_combine(const moe_shape* m, const void* expert_out, const int32_t* slot_pos,
+                const float* topk_w, void* y, void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(expert_out, s.R() * s.d) || !ok_ptr(slot_pos, s.Tk()) ||
+      !ok_ptr(topk_w, s.Tk()) || !ok_ptr(y, s.T * s.d))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(s, expert_out, slot_pos, topk_w, y, (hipStream_t)stream));
+}
+
+int moe_layer_forward(const moe_shape* m, const void* x, const void* W_router,
+                      const float* bias, const void* W_gate_up, const void* W_down, void* y,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(x, s.T * s.d) || !ok_ptr(W_router, s.E * s.d) ||
+      !ok_ptr(W_gate_up, s.G() * 2 * s.f * s.d) || !ok_ptr(W_down, s.G() * s.d * s.f) ||
+      !ok_ptr(y, s.T * s.d))
+    return MOE_ERR_INVALID_ARG;
+  if (bias && ((uintptr_t)bias & 3u)) return MOE_ERR_INVALID_ARG;
+  size_t off[MOE_WS_COUNT], total;
+  layout(s, off, &total);
+  if (workspace_bytes < total) return MOE_ERR_WORKSPACE;
+  if (total > 0 && (!workspace || ((uintptr_t)workspace & 255u))) return MOE_ERR_INVALID_ARG;
+  if (s.T == 0) return MOE_OK;
+
+  char* ws = (char*)workspace;
+  int32_t* idx = (int32_t*)(ws + off[MOE_WS_TOPK_IDX]);
+  float* w = (float*)(ws + off[MOE_WS_TOPK_W]);
+  int32_t* counts = (int32_t*)(ws + off[MOE_WS_COUNTS]);
+  int32_t* offsets = (int32_t*)(ws + off[MOE_WS_OFFSETS]);
+  int32_t* sorted_slot = (int32_t*)(ws + off[MOE_WS_SORTED_SLOT]);
+  int32_t* slot_pos = (int32_t*)(ws + off[MOE_WS_SLOT_POS]);
+  void* act = ws + off[MOE_WS_ACT];
+  void* out = ws + off[MOE_WS_EXPERT_OUT];
+
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_route(s, x, W_router, bias, idx, w, st);
+  if (e == hipSuccess) e = launch_permute(s, idx, counts, offsets, sorted_slot, slot_pos, st);
+  if (e == hipSuccess) e = launch_gate_up(s, x, sorted_slot, offsets, W_gate_up, act, st);
+  if (e == hipSuccess) e = launch_down(s, act, offsets, W_down, out, st);
+  if (e == hipSuccess) e = launch_combine(s, out, slot_pos, w, y, st);
+  return hip_status(e);
+}
+
+}  // extern "C"

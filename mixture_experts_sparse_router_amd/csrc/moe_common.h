@@ -1,0 +1,94 @@
+// moe_common.h -- internal helpers shared by the HIP sources of libmoe.
+// (Not part of the public ABI; the public header is include/moe.h.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ types
+
+typedef uint16_t bf16_t;  // raw bfloat16 bit pattern in memory
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+struct alignas(16) u32x4 {
+  uint32_t x, y, z, w;
+};
+
+// ------------------------------------------------------------ conversions
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+// Low / high bfloat16 of a packed pair, widened exactly.
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// float -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// silu(z) * u in fp32.  silu(z) = z / (1 + e^-z).
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+// --------------------------------------------------------- token of a row
+// Row r of the permuted buffers belongs to token sorted_slot[r] / k for the
+// routed rows r < T*k, and to token (r - T*k) % T for the shared rows.
+__device__ __forceinline__ int64_t row_token(int64_t r, const int32_t* sorted_slot,
+                                             int64_t Tk, int64_t k, int64_t T) {
+  return r < Tk ? (int64_t)sorted_slot[r] / k : (r - Tk) % T;
+}
+
+// ----------------------------------------------------------- host helpers
+
+struct Shape {
+  int64_t T, d, f, E, k, S;
+  int dt;
+  int64_t Tk() const { return T * k; }
+  int64_t R() const { return T * k + S * T; }
+  int64_t G() const { return E + S; }  // expert groups
+};
+
+inline Shape to_shape(const moe_shape* s) {
+  return Shape{s->T, s->d, s->f, s->E, s->k, s->n_shared, (int)s->dt};
+}
+
+// Launchers (return hipSuccess or the launch error).  Argument checking is
+// done by the ABI layer before any of these is called.
+hipError_t launch_route(const Shape& s, const void* x, const void* W_router,
+                        const float* bias, int32_t* topk_idx, float* topk_w,
+                        hipStream_t st);
+hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
+                          hipStream_t st);
+hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* sorted_slot,
+                          const int32_t* offsets, const void* W_gate_up, void* act,
+                          hipStream_t st);
+hipError_t launch_down(const Shape& s, const void* act, const int32_t* offsets,
+                       const void* W_down, void* expert_out, hipStream_t st);
+hipError_t launch_combine(const Shape& s, const void* expert_out,
+                          const int32_t* slot_pos, const float* topk_w, void* y,
+                          hipStream_t st);
+
+}  // namespace moe

@@ -156,3 +156,26 @@ def small_ints(key, shape, lo: int, hi: int) -> np.ndarray:
     """Seeded integers in [lo, hi] as float32 (exact in every format used)."""
     rng = np.random.default_rng(list(key))
     return rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+def random_routing(key, T: int, E: int, k: int, zipf_s: float | None = None) -> np.ndarray:
+    """Seeded expert ids [T, k] (int32), distinct within a row; with zipf_s
+    the ids are drawn without replacement with probability ~ (e+1)^-zipf_s,
+    which leaves some experts with many copies and some with none."""
+    rng = np.random.default_rng(list(key))
+    idx = np.empty((T, k), np.int32)
+    if zipf_s is None:
+        for t in range(T):
+            idx[t] = rng.permutation(E)[:k]
+    else:
+        p = np.arange(1, E + 1, dtype=np.float64) ** -zipf_s
+        p /= p.sum()
+        for t in range(T):
+            idx[t] = rng.choice(E, size=k, replace=False, p=p)
+    return idx
+
+
+def random_unit(key, shape) -> np.ndarray:
+    """Seeded float32 values in (0, 1]."""
+    rng = np.random.default_rng(list(key))
+    return (1.0 - rng.random(size=shape)).astype(np.float32)

@@ -1,0 +1,224 @@
+"""Parity of each step of the layer (HIP path through the C ABI) with the
+fp64 oracle, on seeded inputs that span several tiles, ragged tails, empty
+experts and the size limits."""
+import numpy as np
+import pytest
+
+import moe_synth
+import oracle
+import mixture_experts_sparse_router_amd as moe
+from gpu_util import (abs_scores, assert_rows_close, check_routing, dev, dt_code, empty,
+                      host)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ route
+
+def _route_case(name):
+    n = moe_synth.normal
+    if name == "tiny_fp32":
+        inp = moe_synth.make_layer_inputs(moe_synth.CONFIGS[1], 1, experts=False)
+        return inp["x"], inp["W_router"], None, 2
+    if name == "gpt_oss_20b_decode":
+        inp = moe_synth.make_layer_inputs(moe_synth.CONFIGS[2], 2, experts=False)
+        return inp["x"], inp["W_router"], None, 4
+    if name == "fine_grained_zipf_full":
+        inp = moe_synth.make_layer_inputs(moe_synth.CONFIGS[4], 4, experts=False)
+        return inp["x"], inp["W_router"], inp["bias"], 8
+    if name == "deepseek_v3_full":
+        inp = moe_synth.make_layer_inputs(moe_synth.CONFIGS[5], 5, experts=False)
+        return inp["x"], inp["W_router"], None, 8
+    if name == "zero_router_ties":
+        return n((40, 5, 0), (40, 64), 1.0, "bf16"), np.zeros((16, 64), np.uint16), None, 4
+    if name == "duplicate_rows":
+        x = n((41, 5, 0), (33, 96), 1.0, "bf16")
+        W = n((41, 5, 1), (12, 96), 0.05, "bf16")
+        W[7] = W[3]
+        b = np.zeros(12, np.float32)
+        b[3] = b[7] = 30.0
+        return x, W, b, 3
+    if name == "integer_exact_f32":
+        return (moe_synth.small_ints((42, 5, 0), (70, 24), -3, 3),
+                moe_synth.small_ints((42, 5, 1), (7, 24), -3, 3), None, 3)
+    if name == "integer_exact_bf16":
+        return (moe_synth.to_bf16_bits(moe_synth.small_ints((43, 5, 0), (70, 24), -3, 3)),
+                moe_synth.to_bf16_bits(moe_synth.small_ints((43, 5, 1), (9, 24), -2, 2)),
+                None, 4)
+    if name == "ragged_E100_d136":
+        return n((44, 5, 0), (37, 136), 1.0, "bf16"), n((44, 5, 1), (100, 136), 0.1, "bf16"), \
+            np.linspace(0.5, -0.5, 100).astype(np.float32), 5
+    if name == "max_E1024":
+        return n((45, 5, 0), (50, 64), 1.0, "bf16"), n((45, 5, 1), (1024, 64), 0.1, "bf16"), \
+            None, 8
+    if name == "k_equals_E":
+        return n((46, 5, 0), (19, 40), 1.0, "f32"), n((46, 5, 1), (6, 40), 0.2, "f32"), None, 6
+    raise KeyError(name)
+
+
+ROUTE_CASES = ["tiny_fp32", "gpt_oss_20b_decode", "zero_router_ties", "duplicate_rows",
+               "integer_exact_f32", "integer_exact_bf16", "ragged_E100_d136", "max_E1024",
+               "k_equals_E", "fine_grained_zipf_full", "deepseek_v3_full"]
+
+
+@pytest.mark.parametrize("name", ROUTE_CASES)
+def test_route(name):
+    x, W, bias, k = _route_case(name)
+    dtype = "bf16" if x.dtype == np.uint16 else "f32"
+    T, d = x.shape
+    E = W.shape[0]
+    print(f"route {name}: T={T} d={d} E={E} k={k} {dtype}", flush=True)
+    s = moe.shape(T, d, 8, E, k, 0, dt_code(dtype))
+    idx_d, w_d = empty((T, k), "i32"), empty((T, k), "f32")
+    moe.moe_route(s, dev(x), dev(W), dev(bias), idx_d, w_d)
+    _sync()
+    L, idx_ref, w_ref = oracle.route(x, W, k, bias=bias)
+    amb = check_routing(host(idx_d), host(w_d), L, abs_scores(x, W), idx_ref, w_ref)
+    assert len(amb) <= max(1, T // 1000), f"{len(amb)} near-tie tokens"
+    if name in ("zero_router_ties", "duplicate_rows") or name.startswith("integer"):
+        assert not amb and np.array_equal(host(idx_d), idx_ref)
+
+
+# ---------------------------------------------------------------- permute
+
+PERMUTE_CASES = [
+    # (T, E, k, S, zipf)
+    (16, 32, 4, 0, None), (37, 8, 2, 0, None), (1, 1, 1, 0, None), (0, 4, 2, 1, None),
+    (4096, 128, 8, 0, 1.2), (4096, 256, 8, 1, None), (8192, 8, 2, 0, None),
+    (300, 1000, 7, 24, None), (513, 1023, 64, 1, None), (2000, 64, 3, 2, 2.0),
+]
+
+
+@pytest.mark.parametrize("case", PERMUTE_CASES, ids=str)
+def test_permute(case):
+    T, E, k, S, zipf = case
+    print(f"permute T={T} E={E} k={k} S={S} zipf={zipf}", flush=True)
+    idx = moe_synth.random_routing((50, T, E), T, E, k, zipf) if T else \
+        np.zeros((0, k), np.int32)
+    s = moe.shape(T, 8, 8, E, k, S, moe.MOE_DT_BF16)
+    G = E + S
+    counts, offsets = empty((G,), "i32"), empty((G + 1,), "i32")
+    ss, sp = empty((T * k,), "i32"), empty((T * k,), "i32")
+    moe.moe_permute(s, dev(idx) if T else empty((0,), "i32"), counts, offsets, ss, sp)
+    _sync()
+    c_ref, o_ref, ss_ref, sp_ref = oracle.permute(idx, E, S)
+    assert np.array_equal(host(counts), c_ref)
+    assert np.array_equal(host(offsets), o_ref)
+    assert np.array_equal(host(ss), ss_ref)
+    assert np.array_equal(host(sp), sp_ref)
+
+
+# ----------------------------------------------------------- expert GEMMs
+
+def _rows_of(idx, ss, T, k, E, S):
+    """(token, expert) of every permuted row, from an oracle permutation."""
+    tok = np.concatenate([ss // k, np.tile(np.arange(T), S)]).astype(np.int64)
+    ex = np.concatenate([idx.ravel()[ss], np.repeat(np.arange(E, E + S), T)]).astype(np.int32)
+    return tok, ex
+
+
+GEMM_CASES = [
+    # (name, T, d, f, E, k, S, dtype, zipf)
+    ("decode_gpt_oss_shape", 16, 2880, 2880, 32, 4, 0, "bf16", None),
+    ("decode_T1_k1", 1, 512, 264, 4, 1, 0, "bf16", None),
+    ("decode_T50_shared", 50, 320, 200, 12, 3, 1, "bf16", None),
+    ("tiled_ragged_shared", 300, 256, 200, 6, 2, 1, "bf16", None),
+    ("tiled_zipf_empty_experts", 700, 520, 136, 24, 4, 0, "bf16", 1.5),
+    ("tiled_one_big_group", 400, 192, 384, 3, 1, 0, "bf16", 3.0),
+    ("tiled_T65", 65, 128, 64, 2, 2, 0, "bf16", None),
+    ("f32_tiny_shape", 128, 256, 512, 8, 2, 0, "f32", None),
+    ("f32_ragged_shared", 90, 72, 40, 5, 2, 2, "f32", 1.0),
+]
+
+
+def _gemm_inputs(case):
+    name, T, d, f, E, k, S, dtype, zipf = case
+    seed = 60 + GEMM_CASES.index(case)
+    x = moe_synth.normal((seed, 5, 0), (T, d), 1.0, dtype)
+    Wgu = moe_synth.normal((seed, 5, 2), (E + S, 2 * f, d), 0.05, dtype)
+    Wd = moe_synth.normal((seed, 5, 3), (E + S, d, f), 0.05, dtype)
+    idx = moe_synth.random_routing((seed, 5, 4), T, E, k, zipf)
+    counts, offsets, ss, sp = oracle.permute(idx, E, S)
+    return x, Wgu, Wd, idx, counts, offsets, ss, sp
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: c[0])
+def test_gate_up(case):
+    name, T, d, f, E, k, S, dtype, zipf = case
+    print(f"gate_up {case}", flush=True)
+    x, Wgu, Wd, idx, counts, offsets, ss, sp = _gemm_inputs(case)
+    R = T * k + S * T
+    s = moe.shape(T, d, f, E, k, S, dt_code(dtype))
+    act = empty((R, f), dtype)
+    act.fill_(float("nan"))
+    moe.moe_grouped_gemm_gate_up(s, dev(x), dev(ss), dev(offsets), dev(Wgu), act)
+    _sync()
+    tok, ex = _rows_of(idx, ss, T, k, E, S)
+    ref = oracle.gate_up_rows(x, Wgu, tok, ex)
+    assert_rows_close(host(act), ref, dtype, f"gate_up {name}")
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: c[0])
+def test_down(case):
+    name, T, d, f, E, k, S, dtype, zipf = case
+    print(f"down {case}", flush=True)
+    x, Wgu, Wd, idx, counts, offsets, ss, sp = _gemm_inputs(case)
+    R = T * k + S * T
+    act = moe_synth.normal((70, 5, 0), (R, f), 0.5, dtype)
+    s = moe.shape(T, d, f, E, k, S, dt_code(dtype))
+    out = empty((R, d), dtype)
+    out.fill_(float("nan"))
+    moe.moe_grouped_gemm_down(s, dev(act), dev(offsets), dev(Wd), out)
+    _sync()
+    tok, ex = _rows_of(idx, ss, T, k, E, S)
+    ref = oracle.down_rows(act, Wd, ex)
+    assert_rows_close(host(out), ref, dtype, f"down {name}")
+
+
+@pytest.mark.parametrize("case", GEMM_CASES[:4], ids=lambda c: c[0])
+def test_grouped_gemm_both(case):
+    """moe_grouped_gemm = gate_up then down on the same buffers."""
+    name, T, d, f, E, k, S, dtype, zipf = case
+    x, Wgu, Wd, idx, counts, offsets, ss, sp = _gemm_inputs(case)
+    R = T * k + S * T
+    s = moe.shape(T, d, f, E, k, S, dt_code(dtype))
+    act, out = empty((R, f), dtype), empty((R, d), dtype)
+    moe.moe_grouped_gemm(s, dev(x), dev(ss), dev(offsets), dev(Wgu), dev(Wd), act, out)
+    _sync()
+    tok, ex = _rows_of(idx, ss, T, k, E, S)
+    ref_act = oracle.gate_up_rows(x, Wgu, tok, ex)
+    assert_rows_close(host(act), ref_act, dtype, f"act {name}")
+    # the down projection of the oracle's activation
+    ref_out = oracle.down_rows(ref_act.astype(np.float32), moe_synth.bf16_bits_to_f32(Wd)
+                               if dtype == "bf16" else Wd, ex)
+    assert_rows_close(host(out), ref_out, dtype, f"out {name}")
+
+
+# ---------------------------------------------------------------- combine
+
+COMBINE_CASES = [(16, 2880, 32, 4, 0, "bf16"), (128, 256, 8, 2, 0, "f32"),
+                 (77, 264, 10, 3, 2, "bf16"), (1, 8, 1, 1, 1, "f32"),
+                 (4096, 7168, 256, 8, 1, "bf16")]
+
+
+@pytest.mark.parametrize("case", COMBINE_CASES, ids=str)
+def test_combine(case):
+    T, d, E, k, S, dtype = case
+    print(f"combine {case}", flush=True)
+    idx = moe_synth.random_routing((80, T, E), T, E, k)
+    counts, offsets, ss, sp = oracle.permute(idx, E, S)
+    R = T * k + S * T
+    O = moe_synth.normal((80, 5, 1), (R, d), 1.0, dtype)
+    w = moe_synth.random_unit((80, 5, 2), (T, k))
+    s = moe.shape(T, d, 8, E, k, S, dt_code(dtype))
+    y = empty((T, d), dtype)
+    moe.moe_combine(s, dev(O), dev(sp), dev(w), y)
+    _sync()
+    ref = oracle.combine(O, sp, w.astype(np.float64), T, k, S)
+    assert_rows_close(host(y), ref, dtype, "combine")
