@@ -17,10 +17,11 @@
 // so SwiGLU is applied to the fp32 accumulators before rounding to bf16.
 //
 // Kernels
-//   stream_gemm  bf16, groups of at most 64 rows (decode-shaped).  No LDS:
-//                each wave owns 16 output columns of one expert and streams
+//   stream_gemm  bf16, groups of at most 64 rows (decode-shaped).  Each
+//                workgroup owns 16 output columns of one expert and streams
 //                those weight rows from HBM exactly once, straight into MFMA
-//                operand registers; the few token rows ride along.  HBM-bound.
+//                operand registers (4 waves split K); the few token rows ride
+//                along.  HBM-bound.
 //   tiled_gemm   bf16, large groups.  128x128 block tile, 4 waves of 64x64,
 //                K staged through LDS in double-buffered 64-wide slices,
 //                v_mfma_f32_16x16x32_bf16.  Tiles of empty groups are never
@@ -36,6 +37,10 @@ namespace {
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ u32x4 zero_unless(bool ok, u32x4 v) {
+  return u32x4{ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u};
 }
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, f32x4 c) {
@@ -86,25 +91,54 @@ __device__ bool find_mtile(const int32_t* offsets, int G, int BM, int tile, int*
 }
 
 // ============================================================ stream_gemm
-// One wave = 16 output columns of one expert group, all of the group's rows
-// (16*MB rows per pass).  Lane (j = l%16, kb = l/16) loads, for K chunk c of
-// a 128-wide step, elements [k0 + 32c + 8kb, +8) of weight row n0+j and of
-// token row j: 4 lanes cover 64 contiguous bytes of a row per load.
+// One workgroup = 16 output columns of one expert group for all of the
+// group's rows (16*MB rows per pass).  Its 4 waves split K: wave w takes the
+// 128-wide K steps w, w+4, w+8, ..., so together they sweep each weight row
+// front to back, and the 4 partial accumulators are added in LDS in wave
+// order (fixed, so results are reproducible).  Lane (j = l%16, kb = l/16)
+// loads, for chunk c of a K step, elements [k0 + 32c + 8kb, +8) of weight
+// row n0+j and of token row j: 4 lanes cover 64 contiguous bytes of a row
+// per load.
+template <bool GATED, int MB>
+struct StreamRegs {
+  u32x4 bg[4], bu[4], a[MB][4];
+  bool ok[4];  // chunk c lies inside K (else its registers are zeroed at use)
+};
+
+// Loads of one K step.  Chunks past K read a valid address (offset 0) and
+// are zeroed by a select when they are used, so the loads stay branch-free.
+template <bool GATED, int MB>
+__device__ __forceinline__ void stream_load(StreamRegs<GATED, MB>& r, const bf16_t* Bg,
+                                            const bf16_t* Bu, const bf16_t* const* Ap,
+                                            int64_t k0, int kb, int64_t K) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int64_t kk = k0 + 32 * c + 8 * kb;
+    const bool ok = kk < K;
+    const int64_t ka = ok ? kk : 0;
+    r.ok[c] = ok;
+    r.bg[c] = ldg16(Bg + ka);
+    if constexpr (GATED) r.bu[c] = ldg16(Bu + ka);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) r.a[mb][c] = ldg16(Ap[mb] + ka);
+  }
+}
+
 template <bool GATED, int MB>
 __global__ __launch_bounds__(256) void stream_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
     bf16_t* __restrict__ out, int64_t K, int64_t N, int64_t T, int64_t Tk, int64_t k,
     int G, int ntiles) {
-  const int lane = threadIdx.x & 63;
-  const int wv = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int g = wv / ntiles;
+  __shared__ f32x4 red[3][MB][2][64];  // partials of waves 1..3
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = (int)blockIdx.x / ntiles;
   if (g >= G) return;
   const int64_t row_begin = offsets[g];
   const int64_t rows = offsets[g + 1] - row_begin;
   if (rows <= 0) return;  // empty expert: its weights are never read
   const int j = lane & 15, kb = lane >> 4;
-  const int64_t n0 = (int64_t)(wv % ntiles) * 16;
+  const int64_t n0 = (int64_t)((int)blockIdx.x % ntiles) * 16;
   const int64_t col = n0 + j;
   const bool col_ok = col < N;
   const int64_t colc = col_ok ? col : N - 1;
@@ -130,41 +164,58 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
       accg[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
       accu[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int64_t k0 = 0; k0 < K; k0 += 128) {
-      u32x4 bg[4], bu[4], a[MB][4];
+    // one K step at a time: latency is hidden by the other resident waves
+    // (explicit two-step register pipelining measured slower: it lowers
+    // occupancy more than it adds bytes in flight)
+    for (int64_t k0 = (int64_t)wave * 128; k0 < K; k0 += 512) {
+      StreamRegs<GATED, MB> r;
+      stream_load<GATED, MB>(r, Bg, Bu, Ap, k0, kb, K);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int64_t kk = k0 + 32 * c + 8 * kb;
-        const bool ok = kk < K;
-        const u32x4 z{0u, 0u, 0u, 0u};
-        bg[c] = ok ? ldg16(Bg + kk) : z;
-        if constexpr (GATED) bu[c] = ok ? ldg16(Bu + kk) : z;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) a[mb][c] = ok ? ldg16(Ap[mb] + kk) : z;
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
+        const u32x4 bg = zero_unless(r.ok[c], r.bg[c]);
+        const u32x4 bu = GATED ? zero_unless(r.ok[c], r.bu[c]) : bg;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          accg[mb] = mfma16(a[mb][c], bg[c], accg[mb]);
-          if constexpr (GATED) accu[mb] = mfma16(a[mb][c], bu[c], accu[mb]);
+          const u32x4 a = zero_unless(r.ok[c], r.a[mb][c]);
+          accg[mb] = mfma16(a, bg, accg[mb]);
+          if constexpr (GATED) accu[mb] = mfma16(a, bu, accu[mb]);
         }
       }
     }
-    // lane holds D[4*kb + q][j], q = 0..3
-    if (col_ok) {
+    // add the four K-split partials in wave order
+    if (wave > 0) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
+        red[wave - 1][mb][0][lane] = accg[mb];
+        if constexpr (GATED) red[wave - 1][mb][1][lane] = accu[mb];
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t r = m0 + mb * 16 + kb * 4 + q;
-          if (r < rows) {
-            const float v = GATED ? swiglu(accg[mb][q], accu[mb][q]) : accg[mb][q];
-            out[(row_begin + r) * N + col] = f32_to_bf16(v);
+      for (int w = 0; w < 3; ++w) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          accg[mb] += red[w][mb][0][lane];
+          if constexpr (GATED) accu[mb] += red[w][mb][1][lane];
+        }
+      }
+      // lane holds D[4*kb + q][j], q = 0..3
+      if (col_ok) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t r = m0 + mb * 16 + kb * 4 + q;
+            if (r < rows) {
+              const float v = GATED ? swiglu(accg[mb][q], accu[mb][q]) : accg[mb][q];
+              out[(row_begin + r) * N + col] = f32_to_bf16(v);
+            }
           }
         }
       }
     }
+    __syncthreads();  // red is reused by the next row pass
   }
 }
 
@@ -413,8 +464,7 @@ hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot
   const int G = (int)s.G();
   if (s.T <= 64) {
     const int ntiles = (int)((N + 15) / 16);
-    const int64_t waves = (int64_t)G * ntiles;
-    const unsigned grid = (unsigned)((waves + 3) / 4);
+    const unsigned grid = (unsigned)((int64_t)G * ntiles);
     const int MB = (int)((s.T + 15) / 16);
 #define MOE_STREAM(mb)                                                                 \
   hipLaunchKernelGGL((stream_gemm_kernel<GATED, mb>), dim3(grid), dim3(256), 0, st,    \
