@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy (torch copy_) 10 times: the "
+                        "reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
 
 
@@ -120,6 +123,16 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 10}), flush=True)
+        return
 
     import moe_synth
     import mixture_experts_sparse_router_amd as moe
