@@ -28,6 +28,8 @@
 //                launched work; m-tiles are found on the device from offsets.
 //   f32_gemm     fp32 inputs: LDS-tiled FMA (fp32 vector and matrix peaks are
 //                equal on MI355X), 64x64 tiles.
+#include <type_traits>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -220,141 +222,322 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
 }
 
 // ============================================================= tiled_gemm
-constexpr int TBM = 128;        // rows per block tile
-constexpr int TBN = 128;        // weight rows per block tile (GATED: 64 gate + 64 up)
-constexpr int TBK = 64;         // K per LDS stage
-constexpr int TLD = TBK + 8;    // padded LDS row (144 bytes): conflict-free 16B reads
+// Block tile BM x 256 (weight rows), 4 waves in a 2 x 2 grid, each
+// wave BM/2 x 128 with v_mfma_f32_32x32x16_bf16 (the 16x16x32 form runs at
+// half the rate on gfx950).  GATED: the 256 weight rows of a tile are 128
+// gate rows and the 128 matching up rows, so wave column wn owns 64 output
+// columns as 2 gate + 2 up 32-column blocks and SwiGLU pairs block ni with
+// ni + 2 in registers.
+//
+// LDS: a ring of NST stages of A [BM][32] and B [256][32] bf16 (K tiles of
+// 32), 64-byte rows whose 16-byte chunks are XOR-swizzled (swz below) so the
+// 16-byte MFMA operand reads are bank-conflict free.  K tiles are copied
+// global -> LDS directly (no registers) NST-1 tiles ahead; while the MFMAs
+// of tile j run, tile j+1's operand fragments are read into a second
+// register set.  One barrier per K tile.  Chunks past the end of K are
+// copied from a 16-byte zero block.
+//
+// Tiles: m-tiles of every expert group (ceil(n_g / BM) each) times the
+// n-tiles.  The host launches an upper bound; each workgroup computes the
+// actual tile count from offsets and maps its id to a tile.  Workgroups are
+// dealt to the 8 XCDs round robin, so ids with the same residue mod 8 get a
+// contiguous run of the tile order, in which one expert group's tiles come
+// as rectangles of its m-tiles by kBandN n-tiles.
+constexpr int TBN = 256;        // weight rows per block tile
 
-template <bool GATED>
-__global__ __launch_bounds__(256) void tiled_gemm_kernel(
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// K per LDS stage and number of stages in the ring.
+constexpr int SBK = 32;
+constexpr int NST = 4;
+
+// Element offset of logical 16-byte chunk c (0..3) of LDS row r (SBK bf16,
+// 64 bytes per row).  The chunk is XOR-ed with (r >> 2) & 3, so the 16-byte
+// operand reads of 16 consecutive rows at one logical chunk touch 16
+// distinct 16-byte bank groups (the LDS serves 256 bytes per cycle).
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * SBK + ((c ^ ((r >> 2) & 3)) << 3);
+}
+
+// n-tiles per band of the tile order: consecutive tiles of one expert group
+// form (m-tiles x kBandN) rectangles, so workgroups running side by side on
+// one XCD share both their activation rows and their weight panels in L2.
+constexpr int kBandN = 4;
+
+// Tile lookup: returns false for workgroups past the last tile.
+__device__ bool find_tile(const int32_t* offsets, int G, int BM, int ntN, int bid, int* g_out,
+                          int* mt_out, int* nt_out) {
+  __shared__ int s_res[3];
+  __shared__ int s_wave[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int c[4];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = tid * 4 + i;
+    c[i] = g < G ? (offsets[g + 1] - offsets[g] + BM - 1) / BM : 0;  // m-tiles of g
+    mine += c[i];
+  }
+  int inc = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) s_wave[wave] = inc;
+  if (tid == 0) s_res[0] = -1;
+  __syncthreads();
+  const int total = (s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3]) * ntN;
+  const int per = (total + 7) / 8;
+  const int slot = bid >> 3;
+  const int L = (bid & 7) * per + slot;  // XCD (bid mod 8) takes a contiguous run
+  const bool valid = slot < per && L < total;
+  int start = inc - mine;
+  for (int w = 0; w < wave; ++w) start += s_wave[w];
+  start *= ntN;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = c[i] * ntN;  // tiles of group tid*4+i
+    if (valid && L >= start && L < start + n) {
+      const int q = L - start;
+      const int band = q / (c[i] * kBandN);
+      const int bw = min(kBandN, ntN - band * kBandN);
+      const int rem = q - band * c[i] * kBandN;
+      s_res[0] = tid * 4 + i;
+      s_res[1] = rem / bw;
+      s_res[2] = band * kBandN + rem % bw;
+    }
+    start += n;
+  }
+  __syncthreads();
+  *g_out = s_res[0];
+  *mt_out = s_res[1];
+  *nt_out = s_res[2];
+  return s_res[0] >= 0;
+}
+
+// 16 zero bytes: the source of LDS chunks that lie past the end of K.
+__device__ __attribute__((aligned(16))) bf16_t g_zero_chunk[8];
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l of the wave writes
+// lds_base + 16*l.  No registers are involved, so the loads of the next K
+// tile stay in flight for the whole of the current tile's MFMAs.
+__device__ __forceinline__ void dma16(const void* src, bf16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                   0, 0);
+}
+
+template <bool GATED, int BM>
+__global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
     bf16_t* __restrict__ out, int64_t K, int64_t N, int64_t T, int64_t Tk, int64_t k,
-    int G) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][TBM * TLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][TBN * TLD];
-  int g, mt;
-  if (!find_mtile(offsets, G, TBM, (int)blockIdx.x, &g, &mt)) return;
+    int G, int ntN) {
+  constexpr int MI = BM / 64;         // 32-row blocks per wave
+  constexpr int NI = 4;               // 32-column blocks per wave
+  constexpr int AI = BM / 64;         // A copies (16 rows, 1 KB) per wave per stage
+  constexpr int BI = TBN / 64;        // B copies per wave per stage
+  constexpr int NF = MI + NI;         // operand fragments per K sub-step of 16
+  // one LDS object per ring slot: the compiler can then see that copies into
+  // one slot never alias reads of another and need not wait for them
+  __shared__ __attribute__((aligned(1024))) bf16_t sA0[BM * SBK], sA1[BM * SBK],
+      sA2[BM * SBK], sA3[BM * SBK];
+  __shared__ __attribute__((aligned(1024))) bf16_t sB0[TBN * SBK], sB1[TBN * SBK],
+      sB2[TBN * SBK], sB3[TBN * SBK];
+  static_assert(NST == 4, "four ring slots");
+  auto slotA = [&](auto st) -> bf16_t* {
+    if constexpr (decltype(st)::value == 0) return sA0;
+    else if constexpr (decltype(st)::value == 1) return sA1;
+    else if constexpr (decltype(st)::value == 2) return sA2;
+    else return sA3;
+  };
+  auto slotB = [&](auto st) -> bf16_t* {
+    if constexpr (decltype(st)::value == 0) return sB0;
+    else if constexpr (decltype(st)::value == 1) return sB1;
+    else if constexpr (decltype(st)::value == 2) return sB2;
+    else return sB3;
+  };
+  int g, mt, nt;
+  if (!find_tile(offsets, G, BM, ntN, (int)blockIdx.x, &g, &mt, &nt)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int64_t row_begin = offsets[g] + (int64_t)mt * TBM;
+  const int64_t row_begin = offsets[g] + (int64_t)mt * BM;
   const int64_t rows_left = offsets[g + 1] - row_begin;
-  const int64_t rows = rows_left < TBM ? rows_left : TBM;
-  // output columns covered by this block
+  const int rows = (int)(rows_left < BM ? rows_left : BM);
   const int64_t ncols = GATED ? TBN / 2 : TBN;
-  const int64_t n0 = (int64_t)blockIdx.y * ncols;
+  const int64_t n0 = (int64_t)nt * ncols;
 
-  // ---- per-thread global source rows (4 A pieces + 4 B pieces of 16B)
-  const int prow = tid >> 3;        // 0..31
-  const int pcol = (tid & 7) * 8;   // element offset inside the 64-wide slice
-  const bf16_t* asrc[4];
-  const bf16_t* bsrc[4];
+  // ---- copy plan: wave w fills A rows [w*BM/4, (w+1)*BM/4) and B rows
+  // [64w, 64w+64), 16 rows (1 KB) per copy.  Lane l lands on row l/4,
+  // physical chunk l%4, which holds logical chunk (l%4) ^ ((row >> 2) & 3).
+  const int lrow = lane >> 2;
+  const int lphys = lane & 3;
+  const bf16_t* asrc[AI];
+  int achunk[AI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int64_t r = prow + 32 * i;
-    if (r >= rows) r = rows - 1;
-    const int64_t grow = row_begin + r;
+  for (int i = 0; i < AI; ++i) {
+    const int r = wave * (BM / 4) + 16 * i + lrow;
+    const int rc = r < rows ? r : rows - 1;  // padding rows repeat a valid row
+    const int64_t grow = row_begin + rc;
     if constexpr (GATED) {
-      asrc[i] = A + row_token(grow, sorted_slot, Tk, k, T) * K + pcol;
+      asrc[i] = A + row_token(grow, sorted_slot, Tk, k, T) * K;
     } else {
-      asrc[i] = A + grow * K + pcol;
+      asrc[i] = A + grow * K;
     }
-    const int br = prow + 32 * i;  // 0..127
+    achunk[i] = (lphys ^ ((r >> 2) & 3)) * 8;
+  }
+  const bf16_t* bsrc[BI];
+  int bchunk[BI];
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int br = wave * (TBN / 4) + 16 * i + lrow;  // 0..255
     int64_t wrow;
     if constexpr (GATED) {
-      int64_t c = n0 + (br & 63);
+      int64_t c = n0 + (br & 127);
       if (c >= N) c = N - 1;
-      wrow = (int64_t)g * 2 * N + (br < 64 ? c : N + c);
+      wrow = (int64_t)g * 2 * N + (br < 128 ? c : N + c);
     } else {
       int64_t c = n0 + br;
       if (c >= N) c = N - 1;
       wrow = (int64_t)g * N + c;
     }
-    bsrc[i] = W + wrow * K + pcol;
+    bsrc[i] = W + wrow * K;
+    bchunk[i] = (lphys ^ ((br >> 2) & 3)) * 8;
   }
-
-  const u32x4 z{0u, 0u, 0u, 0u};
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int64_t k0) {
-    const bool ok = k0 + pcol < K;
+  const int nk = (int)((K + SBK - 1) / SBK);
+  // copy K tile j (clamped to the last tile) into ring slot st = j % NST
+  auto issue = [&](auto st, int j) {
+    j = j < nk ? j : nk - 1;
+    const int64_t k0 = (int64_t)j * SBK;
+    bf16_t* a = slotA(st);
+    bf16_t* b = slotB(st);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ok ? ldg16(asrc[i] + k0) : z;
-      rb[i] = ok ? ldg16(bsrc[i] + k0) : z;
+    for (int i = 0; i < AI; ++i) {
+      const int64_t kk = k0 + achunk[i];
+      dma16(kk < K ? (const void*)(asrc[i] + kk) : (const void*)g_zero_chunk,
+            a + (wave * (BM / 4) + 16 * i) * SBK);
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int64_t kk = k0 + bchunk[i];
+      dma16(kk < K ? (const void*)(bsrc[i] + kk) : (const void*)g_zero_chunk,
+            b + (wave * (TBN / 4) + 16 * i) * SBK);
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&sA[buf][(prow + 32 * i) * TLD + pcol]) = ra[i];
-      *reinterpret_cast<u32x4*>(&sB[buf][(prow + 32 * i) * TLD + pcol]) = rb[i];
-    }
-  };
 
-  // ---- wave sub-tile: rows wm*64 .. +64; weight rows per the GATED layout
+  // ---- wave sub-tile
   const int wm = wave >> 1, wn = wave & 1;
-  const int j = lane & 15, kb = lane >> 4;
-  int brow[4];  // LDS B rows of the 4 column blocks this wave multiplies
+  const int lr = lane & 31, lh = lane >> 5;
+  int arow[MI], brow[NI];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+  for (int mi = 0; mi < MI; ++mi) arow[mi] = wm * (BM / 2) + mi * 32 + lr;
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
     if constexpr (GATED) {
-      // ni 0,1: gate columns 32wn + 16ni; ni 2,3: the matching up columns
-      brow[ni] = (ni < 2 ? 0 : 64) + 32 * wn + 16 * (ni & 1) + j;
+      // ni 0,1: gate columns 64wn + 32ni; ni 2,3: the matching up columns
+      brow[ni] = (ni < 2 ? 0 : 128) + 64 * wn + 32 * (ni & 1) + lr;
     } else {
-      brow[ni] = 64 * wn + 16 * ni + j;
+      brow[ni] = 128 * wn + 32 * ni + lr;
     }
   }
-  f32x4 acc[4][4];
+  f32x16 acc[MI][NI];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
 
-  const int nk = (int)((K + TBK - 1) / TBK);
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((int64_t)(kt + 1) * TBK);
+  // operand fragments of the K tile in ring slot st (2 sub-steps of 16)
+  auto frags = [&](auto st, u32x4 (&f)[2][NF]) {
+    const bf16_t* a = slotA(st);
+    const bf16_t* b = slotB(st);
 #pragma unroll
-    for (int ks = 0; ks < TBK / 32; ++ks) {
-      u32x4 af[4], bfr[4];
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[mi] = *reinterpret_cast<const u32x4*>(
-            &sA[cur][(wm * 64 + mi * 16 + j) * TLD + ks * 32 + kb * 8]);
+      for (int mi = 0; mi < MI; ++mi)
+        f[s][mi] = *reinterpret_cast<const u32x4*>(a + swz(arow[mi], 2 * s + lh));
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        bfr[ni] = *reinterpret_cast<const u32x4*>(
-            &sB[cur][brow[ni] * TLD + ks * 32 + kb * 8]);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma16(af[mi], bfr[ni], acc[mi][ni]);
+      for (int ni = 0; ni < NI; ++ni)
+        f[s][MI + ni] = *reinterpret_cast<const u32x4*>(b + swz(brow[ni], 2 * s + lh));
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
-  }
+  };
+  // One K tile j (ring slot st): wait until tile j+1 has landed (this wave's
+  // copies, then the barrier for everyone's), copy tile j+NST-1 into the
+  // slot freed by tile j-1, read tile j+1's fragments into `nxt` while the
+  // MFMAs of tile j run on `cur`.  Branch-free, so the interleaving holds.
+  auto step = [&](auto st, int j, u32x4 (&cur)[2][NF], u32x4 (&nxt)[2][NF]) {
+    constexpr int S = decltype(st)::value;
+    // a plain s_barrier, not __syncthreads(): its release fence would wait
+    // for every copy in flight, including those of the later tiles
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 3) * (AI + BI)) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(std::integral_constant<int, (S + NST - 1) % NST>{}, j + NST - 1);
+    frags(std::integral_constant<int, (S + 1) % NST>{}, nxt);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = mfma32(cur[s][mi], cur[s][MI + ni], acc[mi][ni]);
+    // order: copies, then the 2*NF LDS reads spread between the 2*MI*NI MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x020, AI + BI, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MI * NI / NF, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI * NI - 2 * NF * (MI * NI / NF), 0);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
 
-  // ---- epilogue: lane holds D[4*kb + q][j] of each 16x16 block
+  u32x4 f0[2][NF], f1[2][NF];
+  issue(S0{}, 0);
+  issue(S1{}, 1);
+  issue(S2{}, 2);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * (AI + BI)) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  frags(S0{}, f0);
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
+    step(S0{}, kt, f0, f1);
+    step(S1{}, kt + 1, f1, f0);
+    step(S2{}, kt + 2, f0, f1);
+    step(S3{}, kt + 3, f1, f0);
+  }
+  if (kt < nk) step(S0{}, kt, f0, f1);
+  if (kt + 1 < nk) step(S1{}, kt + 1, f1, f0);
+  if (kt + 2 < nk) step(S2{}, kt + 2, f0, f1);
+  // drain the copies still in flight before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue: lane holds D[8*(q/4) + 4*lh + (q%4)][lr] of each 32x32 block
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+  for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t r = wm * 64 + mi * 16 + kb * 4 + q;
+    for (int q = 0; q < 16; ++q) {
+      const int r = wm * (BM / 2) + mi * 32 + 8 * (q >> 2) + 4 * lh + (q & 3);
       if (r >= rows) continue;
       bf16_t* orow = out + (row_begin + r) * N;
       if constexpr (GATED) {
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
-          const int64_t c = n0 + 32 * wn + 16 * ni + j;
+          const int64_t c = n0 + 64 * wn + 32 * ni + lr;
           if (c < N) orow[c] = f32_to_bf16(swiglu(acc[mi][ni][q], acc[mi][ni + 2][q]));
         }
       } else {
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int64_t c = n0 + 64 * wn + 16 * ni + j;
+        for (int ni = 0; ni < NI; ++ni) {
+          const int64_t c = n0 + 128 * wn + 32 * ni + lr;
           if (c < N) orow[c] = f32_to_bf16(acc[mi][ni][q]);
         }
       }
@@ -479,11 +662,21 @@ hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot
 #undef MOE_STREAM
     return hipGetLastError();
   }
+  // rows per m-tile: 256 when groups are large on average, else 128
+  const int64_t avg_rows = s.R() / (s.G() > 0 ? s.G() : 1);
   const int64_t ncols = GATED ? TBN / 2 : TBN;
-  dim3 grid(mtile_bound(s, TBM), (unsigned)((N + ncols - 1) / ncols));
-  hipLaunchKernelGGL((tiled_gemm_kernel<GATED>), grid, dim3(256), 0, st, (const bf16_t*)A,
-                     sorted_slot, offsets, (const bf16_t*)W, (bf16_t*)out, K, N, s.T,
-                     s.Tk(), s.k, G);
+  const int ntN = (int)((N + ncols - 1) / ncols);
+  if (avg_rows >= 192) {
+    const unsigned grid = ((mtile_bound(s, 256) * (unsigned)ntN) + 7u) & ~7u;
+    hipLaunchKernelGGL((tiled_gemm_kernel<GATED, 256>), dim3(grid), dim3(256), 0, st,
+                       (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W, (bf16_t*)out,
+                       K, N, s.T, s.Tk(), s.k, G, ntN);
+  } else {
+    const unsigned grid = ((mtile_bound(s, 128) * (unsigned)ntN) + 7u) & ~7u;
+    hipLaunchKernelGGL((tiled_gemm_kernel<GATED, 128>), dim3(grid), dim3(256), 0, st,
+                       (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W, (bf16_t*)out,
+                       K, N, s.T, s.Tk(), s.k, G, ntN);
+  }
   return hipGetLastError();
 }
 
