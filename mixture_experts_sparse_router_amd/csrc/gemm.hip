@@ -330,6 +330,64 @@ __device__ __forceinline__ void dma16(const void* src, bf16_t* lds_base) {
                                    0, 0);
 }
 
+// One K tile of the tiled GEMM (see tiled_gemm_kernel).  The LDS slot being
+// filled and the slot being read are separate __restrict__ parameters: once
+// inlined, the compiler knows that the copies in flight never alias the
+// operand reads and does not make the reads wait for them.
+template <int MI, int NI, int AI, int BI, int ROWS_A>
+__device__ __forceinline__ void gemm_tile_step(
+    bf16_t* __restrict__ fillA, bf16_t* __restrict__ fillB, const bf16_t* __restrict__ readA,
+    const bf16_t* __restrict__ readB, const bf16_t* const (&asrc)[AI], const int (&achunk)[AI],
+    const bf16_t* const (&bsrc)[BI], const int (&bchunk)[BI], int64_t k0, int64_t K,
+    const int (&arow)[MI], const int (&brow)[NI], int lh, int wave,
+    const u32x4 (&cur)[2][MI + NI], u32x4 (&nxt)[2][MI + NI], f32x16 (&acc)[MI][NI]) {
+  constexpr int NF = MI + NI;
+  // tile j+1 has landed: this wave's copies, then everyone's (a plain
+  // s_barrier: __syncthreads()'s release fence would wait for all copies)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(1 * (AI + BI)) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  // copy tile j+3 into the slot tile j-1 used
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int64_t kk = k0 + achunk[i];
+    dma16(kk < K ? (const void*)(asrc[i] + kk) : (const void*)g_zero_chunk,
+          fillA + (wave * (ROWS_A / 4) + 16 * i) * SBK);
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int64_t kk = k0 + bchunk[i];
+    dma16(kk < K ? (const void*)(bsrc[i] + kk) : (const void*)g_zero_chunk,
+          fillB + (wave * (TBN / 4) + 16 * i) * SBK);
+  }
+  // tile j+1's operand fragments
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+      nxt[s][mi] = *reinterpret_cast<const u32x4*>(readA + swz(arow[mi], 2 * s + lh));
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+      nxt[s][MI + ni] = *reinterpret_cast<const u32x4*>(readB + swz(brow[ni], 2 * s + lh));
+  }
+  // tile j's MFMAs
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = mfma32(cur[s][mi], cur[s][MI + ni], acc[mi][ni]);
+  // order: copies, then the 2*NF LDS reads spread between the 2*MI*NI MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x020, AI + BI, 0);
+#pragma unroll
+  for (int i = 0; i < 2 * NF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MI * NI / NF, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI * NI - 2 * NF * (MI * NI / NF), 0);
+}
+
 template <bool GATED, int BM>
 __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
@@ -348,6 +406,7 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) bf16_t sB0[TBN * SBK], sB1[TBN * SBK],
       sB2[TBN * SBK], sB3[TBN * SBK];
   static_assert(NST == 4, "four ring slots");
+  static_assert(NST - 3 == 1, "gemm_tile_step waits for NST-3 = 1 later tile");
   auto slotA = [&](auto st) -> bf16_t* {
     if constexpr (decltype(st)::value == 0) return sA0;
     else if constexpr (decltype(st)::value == 1) return sA1;
@@ -465,34 +524,16 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(
         f[s][MI + ni] = *reinterpret_cast<const u32x4*>(b + swz(brow[ni], 2 * s + lh));
     }
   };
-  // One K tile j (ring slot st): wait until tile j+1 has landed (this wave's
-  // copies, then the barrier for everyone's), copy tile j+NST-1 into the
-  // slot freed by tile j-1, read tile j+1's fragments into `nxt` while the
-  // MFMAs of tile j run on `cur`.  Branch-free, so the interleaving holds.
+  // One K tile j in ring slot st: see gemm_tile_step.
   auto step = [&](auto st, int j, u32x4 (&cur)[2][NF], u32x4 (&nxt)[2][NF]) {
     constexpr int S = decltype(st)::value;
-    // a plain s_barrier, not __syncthreads(): its release fence would wait
-    // for every copy in flight, including those of the later tiles
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 3) * (AI + BI)) : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue(std::integral_constant<int, (S + NST - 1) % NST>{}, j + NST - 1);
-    frags(std::integral_constant<int, (S + 1) % NST>{}, nxt);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = mfma32(cur[s][mi], cur[s][MI + ni], acc[mi][ni]);
-    // order: copies, then the 2*NF LDS reads spread between the 2*MI*NI MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x020, AI + BI, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * NF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, MI * NI / NF, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI * NI - 2 * NF * (MI * NI / NF), 0);
+    using Fill = std::integral_constant<int, (S + NST - 1) % NST>;
+    using Read = std::integral_constant<int, (S + 1) % NST>;
+    const int jf = j + NST - 1 < nk ? j + NST - 1 : nk - 1;  // clamped copy
+    gemm_tile_step<MI, NI, AI, BI, BM>(slotA(Fill{}), slotB(Fill{}), slotA(Read{}),
+                                       slotB(Read{}), asrc, achunk, bsrc, bchunk,
+                                       (int64_t)jf * SBK, K, arow, brow, lh, wave, cur, nxt,
+                                       acc);
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
