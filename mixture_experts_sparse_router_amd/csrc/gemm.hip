@@ -37,17 +37,6 @@ namespace {
 
 // --------------------------------------------------------------- helpers
 
-__device__ __forceinline__ u32x4 ldg16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
-__device__ __forceinline__ u32x4 zero_unless(bool ok, u32x4 v) {
-  return u32x4{ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u};
-}
-
-__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
-}
 
 // Block-cooperative lookup of m-tile `tile` in the device-side tile list:
 // group g owns ceil(count_g / BM) consecutive m-tiles.  Returns false when the

@@ -47,6 +47,21 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ u32x4 zero_unless(bool ok, u32x4 v) {
+  return u32x4{ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u};
+}
+
+// D = A * B + C on a 16x16x32 bf16 tile (fp32 accumulate).  Lane l supplies
+// A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16]; it receives
+// D[4*(l/16) + q][l%16] in element q.
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 // silu(z) * u in fp32.  silu(z) = z / (1 + e^-z).
 __device__ __forceinline__ float swiglu(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;

@@ -27,6 +27,7 @@ namespace {
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxGroups = 1024;
+constexpr int kBatch = 16;  // steps of 64 copies whose loads are issued together
 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63;
@@ -71,27 +72,37 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
 
   for (int e = lane; e < E; e += 64) hist[wave][e] = 0;
 
-  // ---- A: rank inside the wave's range
-  for (int64_t base = s_begin; base < s_end; base += 64) {
-    const int64_t s = base + lane;
-    const int v = s < s_end ? idx[s] : -1;
-    const bool active = v >= 0 && v < E;  // ids outside [0, E) are skipped
-    const int key = active ? v : E;       // E: distinct dummy key
-    uint64_t peers = ~0ull;
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (key >> b) & 1;
-      const uint64_t bal = __ballot(bit);
-      peers &= bit ? bal : ~bal;
+  // ---- A: rank inside the wave's range; the expert ids of kBatch steps of
+  // 64 copies are loaded up front so their latency overlaps
+  for (int64_t b0 = s_begin; b0 < s_end; b0 += 64 * kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t s = b0 + 64 * u + lane;
+      v[u] = s < s_end ? idx[s] : -1;
     }
-    const int rank = __popcll(peers & lanes_below);
-    const int leader = 63 - __clzll(peers);
-    int before = 0;
-    if (active && lane == leader) {
-      before = hist[wave][key];
-      hist[wave][key] = before + __popcll(peers);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (b0 + 64 * u >= s_end) break;
+      const int64_t s = b0 + 64 * u + lane;
+      const bool active = v[u] >= 0 && v[u] < E;  // ids outside [0, E) are skipped
+      const int key = active ? v[u] : E;          // E: distinct dummy key
+      uint64_t peers = ~0ull;
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
+      }
+      const int rank = __popcll(peers & lanes_below);
+      const int leader = 63 - __clzll(peers);
+      int before = 0;
+      if (active && lane == leader) {
+        before = hist[wave][key];
+        hist[wave][key] = before + __popcll(peers);
+      }
+      before = __shfl(before, leader, 64);
+      if (active) slot_pos[s] = before + rank;
     }
-    before = __shfl(before, leader, 64);
-    if (active) slot_pos[s] = before + rank;
   }
   __syncthreads();
 
@@ -120,16 +131,28 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
   }
   __syncthreads();
 
-  // ---- C: scatter
-  for (int64_t s = s_begin + lane; s < s_end; s += 64) {
-    const int e = idx[s];
-    if (e < 0 || e >= E) {
-      slot_pos[s] = -1;
-      continue;
+  // ---- C: scatter (loads batched as in A)
+  for (int64_t b0 = s_begin; b0 < s_end; b0 += 64 * kBatch) {
+    int v[kBatch], r[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t s = b0 + 64 * u + lane;
+      v[u] = s < s_end ? idx[s] : -1;
+      r[u] = s < s_end ? slot_pos[s] : 0;
     }
-    const int pos = hist[wave][e] + slot_pos[s];
-    sorted_slot[pos] = (int32_t)s;
-    slot_pos[s] = pos;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t s = b0 + 64 * u + lane;
+      if (s >= s_end) continue;
+      const int e = v[u];
+      if (e < 0 || e >= E) {
+        slot_pos[s] = -1;
+        continue;
+      }
+      const int pos = hist[wave][e] + r[u];
+      sorted_slot[pos] = (int32_t)s;
+      slot_pos[s] = pos;
+    }
   }
 }
 

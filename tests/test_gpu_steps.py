@@ -57,6 +57,24 @@ def _route_case(name):
     if name == "max_E1024":
         return n((45, 5, 0), (50, 64), 1.0, "bf16"), n((45, 5, 1), (1024, 64), 0.1, "bf16"), \
             None, 8
+    if name == "screen_E1024":
+        return n((47, 5, 0), (100, 64), 1.0, "bf16"), n((47, 5, 1), (1024, 64), 0.1, "bf16"), \
+            None, 8
+    if name == "screen_E300_ragged":
+        return n((48, 5, 0), (77, 136), 1.0, "bf16"), n((48, 5, 1), (300, 136), 0.1, "bf16"), \
+            np.linspace(0.2, -0.3, 300).astype(np.float32), 6
+    if name == "screen_E8_long_d":
+        return n((49, 5, 0), (130, 4104), 1.0, "bf16"), n((49, 5, 1), (8, 4104), 0.02, "bf16"), \
+            None, 2
+    if name == "screen_zero_router":
+        return n((50, 5, 0), (90, 96), 1.0, "bf16"), np.zeros((40, 96), np.uint16), None, 5
+    if name == "screen_duplicate_rows":
+        x = n((51, 5, 0), (97, 256), 1.0, "bf16")
+        W = n((51, 5, 1), (64, 256), 0.05, "bf16")
+        W[40] = W[9]
+        b = np.zeros(64, np.float32)
+        b[9] = b[40] = 30.0
+        return x, W, b, 4
     if name == "k_equals_E":
         return n((46, 5, 0), (19, 40), 1.0, "f32"), n((46, 5, 1), (6, 40), 0.2, "f32"), None, 6
     raise KeyError(name)
@@ -64,7 +82,9 @@ def _route_case(name):
 
 ROUTE_CASES = ["tiny_fp32", "gpt_oss_20b_decode", "zero_router_ties", "duplicate_rows",
                "integer_exact_f32", "integer_exact_bf16", "ragged_E100_d136", "max_E1024",
-               "k_equals_E", "fine_grained_zipf_full", "deepseek_v3_full"]
+               "k_equals_E", "screen_E1024", "screen_E300_ragged", "screen_E8_long_d",
+               "screen_zero_router", "screen_duplicate_rows", "fine_grained_zipf_full",
+               "deepseek_v3_full"]
 
 
 @pytest.mark.parametrize("name", ROUTE_CASES)
@@ -81,7 +101,8 @@ def test_route(name):
     L, idx_ref, w_ref = oracle.route(x, W, k, bias=bias)
     amb = check_routing(host(idx_d), host(w_d), L, abs_scores(x, W), idx_ref, w_ref)
     assert len(amb) <= max(1, T // 1000), f"{len(amb)} near-tie tokens"
-    if name in ("zero_router_ties", "duplicate_rows") or name.startswith("integer"):
+    if name in ("zero_router_ties", "duplicate_rows", "screen_zero_router",
+                "screen_duplicate_rows") or name.startswith("integer"):
         assert not amb and np.array_equal(host(idx_d), idx_ref)
 
 
