@@ -24,7 +24,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_sparse_router_amd", "csrc", "gemm.hip")
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_sparse_router_amd", "csrc", "gemm_stream.hip")
 
 
 def parse():

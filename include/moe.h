@@ -76,7 +76,9 @@ typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
  *            stored after the routed experts in W_gate_up / W_down, get
  *            weight 1 for every token and take no part in the softmax
  *   dt       moe_dtype of the float tensors
- * Derived: R = T*k + S*T rows of the permuted buffers; R < 2^31. */
+ * Derived: R = T*k + S*T rows of the permuted buffers; R < 2^31.
+ * bf16 with T > 64 also needs T*d < 2^30 and f*d < 2^29 (x and one expert's
+ * gate_up weights each under 2 GiB); other shapes get MOE_ERR_UNSUPPORTED. */
 typedef struct {
   int64_t T, d, f, E, k, n_shared;
   int32_t dt;

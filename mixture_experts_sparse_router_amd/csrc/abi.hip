@@ -34,6 +34,11 @@ int check_shape(const moe_shape* m) {
   if (m->k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (m->d > ((int64_t)1 << 30) || m->f > ((int64_t)1 << 30)) return MOE_ERR_UNSUPPORTED;
   if (m->T >= kMaxRows / (m->k + m->n_shared)) return MOE_ERR_UNSUPPORTED;  // R < 2^31
+  // bf16 batches past decode size: the tiled GEMM addresses x and one
+  // expert's weights with 32-bit byte offsets below 2^31
+  if (m->dt == MOE_DT_BF16 && m->T > 64 &&
+      (m->T * m->d >= ((int64_t)1 << 30) || m->f * m->d >= ((int64_t)1 << 29)))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -100,6 +100,10 @@ hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int32_t* coun
 hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* sorted_slot,
                           const int32_t* offsets, const void* W_gate_up, void* act,
                           hipStream_t st);
+// Decode-sized groups (T <= 64), bf16 only; gated selects the gate_up form.
+hipError_t launch_stream_gemm(bool gated, const Shape& s, const void* A,
+                              const int32_t* sorted_slot, const int32_t* offsets, const void* W,
+                              void* out, int64_t K, int64_t N, hipStream_t st);
 hipError_t launch_down(const Shape& s, const void* act, const int32_t* offsets,
                        const void* W_down, void* expert_out, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const void* expert_out,

@@ -92,8 +92,16 @@ def test_unsupported_shapes():
     L = moe.lib()
     p = ctypes.c_void_p(4096)
     for s in (_shape(E=1024, n_shared=1), _shape(E=128, k=65),
-              _shape(T=1 << 30, k=4)):
+              _shape(T=1 << 30, k=4),
+              # bf16 past decode size: x or one expert's weights of 2 GiB or more
+              _shape(T=1 << 17, d=1 << 13, k=2, dt=moe.MOE_DT_BF16),
+              _shape(T=128, d=1 << 15, f=1 << 14, dt=moe.MOE_DT_BF16)):
         assert L.moe_route(ctypes.byref(s), p, p, None, p, p, None) == moe.MOE_ERR_UNSUPPORTED
+    # just inside those limits, and any size at decode batch or in fp32
+    for s in (_shape(T=(1 << 17) - 8, d=1 << 13, k=2, dt=moe.MOE_DT_BF16),
+              _shape(T=64, d=1 << 15, f=1 << 14, dt=moe.MOE_DT_BF16),
+              _shape(T=128, d=1 << 15, f=1 << 14, dt=moe.MOE_DT_F32)):
+        assert L.moe_workspace_size(ctypes.byref(s)) > 0
 
 
 def test_null_and_misaligned_pointers():
