@@ -20,7 +20,7 @@
 //   stream_gemm  bf16, T <= 64 (decode): in gemm_stream.hip.
 //   tiled_gemm   bf16, larger batches.  BM x 256 block tile (BM = 128 or
 //                256), 4 waves in a 2 x 2 grid, v_mfma_f32_32x32x16_bf16; K
-//                staged through a 4-slot LDS ring by direct global -> LDS
+//                staged through a 5- or 3-stage LDS ring by direct global -> LDS
 //                copies.  Tiles of empty groups are never launched work;
 //                m-tiles are found on the device from offsets.
 //   f32_gemm     fp32 inputs: LDS-tiled FMA (fp32 vector and matrix peaks are
@@ -87,7 +87,8 @@ __device__ bool find_mtile(const int32_t* offsets, int G, int BM, int tile, int*
 // as 2 gate + 2 up 32-column blocks and SwiGLU pairs block ni with ni + 2 in
 // registers.
 //
-// LDS: a ring of NST stages, each A [BM][32] then B [256][32] bf16 (K tiles
+// LDS: a ring of NST stages (5 for BM = 256 at one workgroup per CU; 3 for
+// BM = 128 at two per CU), each A [BM][32] and B [256][32] bf16 (K tiles
 // of 32), 64-byte rows whose 16-byte chunks are XOR-swizzled so that the
 // 16-byte MFMA operand reads are bank-conflict free.  K tiles are copied
 // global -> LDS directly (buffer loads with the LDS bit, no registers)
@@ -108,7 +109,6 @@ __device__ bool find_mtile(const int32_t* offsets, int G, int BM, int tile, int*
 // as rectangles of its m-tiles by kBandN n-tiles.
 constexpr int TBN = 256;  // weight rows per block tile
 constexpr int SBK = 32;   // K per LDS stage
-constexpr int NST = 4;    // stages in the ring
 
 // Buffer resource word 3 for raw (untyped, stride 0) buffers on gfx9-family
 // parts: 32-bit data format; the range check is then "offset >= num_records".
@@ -159,10 +159,11 @@ constexpr int kSchedVmem = 0x020, kSchedDsRead = 0x100;
 constexpr int kBandN = 4;
 
 // Tile lookup: returns false for workgroups past the last tile.
+// lds: 7 ints of workgroup-shared scratch.
 __device__ bool find_tile(const int32_t* offsets, int G, int BM, int ntN, int bid, int* g_out,
-                          int* mt_out, int* nt_out) {
-  __shared__ int s_res[3];
-  __shared__ int s_wave[4];
+                          int* mt_out, int* nt_out, int* lds) {
+  int* s_res = lds;       // [3]
+  int* s_wave = lds + 3;  // [4]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   int c[4];
@@ -211,8 +212,8 @@ __device__ bool find_tile(const int32_t* offsets, int G, int BM, int ntN, int bi
   return s_res[0] >= 0;
 }
 
-template <bool GATED, int BM>
-__global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(
+template <bool GATED, int BM, int NST, int OCC>
+__global__ __launch_bounds__(256, OCC) void tiled_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
     bf16_t* __restrict__ out, int64_t K, int64_t N, int64_t T, int64_t Tk, int64_t k,
@@ -222,13 +223,24 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(
   constexpr int AI = BM / 64;   // A copies (16 rows, 1 KB) per wave per stage
   constexpr int BI = TBN / 64;  // B copies per wave per stage
   constexpr int NF = MI + NI;   // operand fragments per sub-step
-  constexpr uint32_t ROWB = SBK * 2;                  // bytes per LDS row
-  constexpr uint32_t STAGE = (BM + TBN) * ROWB;       // bytes per ring stage
-  constexpr uint32_t BOFF = BM * ROWB;                // B block inside a stage
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[NST * STAGE];
+  constexpr uint32_t ROWB = SBK * 2;         // bytes per LDS row
+  constexpr uint32_t STA = BM * ROWB;         // bytes per stage of A
+  constexpr uint32_t STB = TBN * ROWB;        // bytes per stage of B
+  // two LDS objects (A and B stages): with more than one, the compiler tags
+  // each LDS access with the object it touches
+  __shared__ __attribute__((aligned(1024))) unsigned char ringA[NST * STA];
+  __shared__ __attribute__((aligned(1024))) unsigned char ringB[NST * STB];
+
+  static_assert(NST * (STA + STB) * OCC <= 160 * 1024, "ring fits the LDS");
+  static_assert((NST - 2) * (AI + BI) < 64, "vmcnt range");
 
   int g, mt, nt;
-  if (!find_tile(offsets, G, BM, ntN, (int)blockIdx.x, &g, &mt, &nt)) return;
+  // the tile lookup's scratch lives at the start of the ring; the barrier
+  // after it keeps the first copies from overwriting it while it is read
+  if (!find_tile(offsets, G, BM, ntN, (int)blockIdx.x, &g, &mt, &nt,
+                 reinterpret_cast<int*>(ringA)))
+    return;
+  __syncthreads();
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t row_begin = offsets[g] + (int64_t)mt * BM;
@@ -282,21 +294,21 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(
   }
   // the ring's LDS address as an integer for the copies, kept apart from the
   // pointer arithmetic of the fragment reads
-  uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
-  asm("" : "+s"(ring_lds));
-  // copies of K tile j into ring stage j % NST (all out of range past the end)
-  auto issue = [&](int j) {
+  uint32_t ring_a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ringA;
+  uint32_t ring_b = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ringB;
+  asm("" : "+s"(ring_a), "+s"(ring_b));
+  // copies of K tile j into ring stage sg (all out of range past the end)
+  auto issue = [&](int sg, int j) {
     const int64_t k0 = (int64_t)j * SBK;
     const bool kin = k0 + kchunk < K;
     const uint32_t kb = (uint32_t)k0 * 2;
-    const uint32_t st = ring_lds + (uint32_t)(j % NST) * STAGE;
+    const uint32_t sa = ring_a + (uint32_t)sg * STA, sb = ring_b + (uint32_t)sg * STB;
 #pragma unroll
     for (int i = 0; i < AI; ++i)
-      copy16(ra, kin ? aoff[i] + kb : kOOB, st + (uint32_t)(wave * (BM / 4) + 16 * i) * ROWB);
+      copy16(ra, kin ? aoff[i] + kb : kOOB, sa + (uint32_t)(wave * (BM / 4) + 16 * i) * ROWB);
 #pragma unroll
     for (int i = 0; i < BI; ++i)
-      copy16(rb, kin ? boff[i] + kb : kOOB,
-             st + BOFF + (uint32_t)(wave * (TBN / 4) + 16 * i) * ROWB);
+      copy16(rb, kin ? boff[i] + kb : kOOB, sb + (uint32_t)(wave * (TBN / 4) + 16 * i) * ROWB);
   };
 
   // ---- wave sub-tile and its fragment addresses.  Fragment rows are
@@ -305,25 +317,28 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lh = lane >> 5;
   const int q = (lr >> 2) & 3;
-  uint32_t fa[2], fb[2];  // per sub-step s: byte offset of block 0 inside a stage
+  uint32_t fa[2], fb[2];  // per sub-step s: byte offset of block 0 inside a stage of A / B
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const uint32_t ch = (uint32_t)(((2 * s + lh) ^ q) << 4);
     fa[s] = (uint32_t)(wm * (BM / 2) + lr) * ROWB + ch;
-    fb[s] = BOFF + (uint32_t)((GATED ? 64 : 128) * wn + lr) * ROWB + ch;
+    fb[s] = (uint32_t)((GATED ? 64 : 128) * wn + lr) * ROWB + ch;
   }
   // B block ni starts at row bro(ni) + (64 or 128) * wn
   constexpr auto bro = [](int ni) constexpr -> int {
     return GATED ? (ni < 2 ? 0 : 128) + 32 * (ni & 1) : 32 * ni;
   };
-  auto frags = [&](int j, int s, u32x4 (&f)[NF]) {
-    const unsigned char* st = ring + (uint32_t)(j % NST) * STAGE;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-      f[mi] = *reinterpret_cast<const u32x4*>(st + fa[s] + (uint32_t)(32 * mi) * ROWB);
+  auto frags = [&](int sg, int s, u32x4 (&f)[NF]) {
+    const unsigned char* sa = ringA + (uint32_t)sg * STA;
+    const unsigned char* sb = ringB + (uint32_t)sg * STB;
+    // in the order the MFMAs (mi-major) consume them: A0, B0..B3, A1, A2, ...
+    f[0] = *reinterpret_cast<const u32x4*>(sa + fa[s]);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
-      f[MI + ni] = *reinterpret_cast<const u32x4*>(st + fb[s] + (uint32_t)bro(ni) * ROWB);
+      f[MI + ni] = *reinterpret_cast<const u32x4*>(sb + fb[s] + (uint32_t)bro(ni) * ROWB);
+#pragma unroll
+    for (int mi = 1; mi < MI; ++mi)
+      f[mi] = *reinterpret_cast<const u32x4*>(sa + fa[s] + (uint32_t)(32 * mi) * ROWB);
   };
 
   f32x16 acc[MI][NI];
@@ -341,17 +356,20 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(
   };
 
   const int nk = (int)((K + SBK - 1) / SBK);
+  auto next = [](int sg) { return sg + 1 == NST ? 0 : sg + 1; };
   u32x4 f0[NF], f1[NF];
-  issue(0);
-  issue(1);
-  issue(2);
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t) issue(t, t);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * (AI + BI)) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   frags(0, 0, f0);
+  int s_rd = 0;        // stage of tile j
+  int s_cp = NST - 1;  // stage of tile j-1, which takes tile j+NST-1
   for (int j = 0; j < nk; ++j) {
+    const int s_nx = next(s_rd);  // stage of tile j+1
     // sub-step 0 of tile j; read sub-step 1's fragments meanwhile
-    frags(j, 1, f1);
+    frags(s_rd, 1, f1);
     mma(f0);
     sched_spread<MI * NI, NF, kSchedDsRead, 0, kSchedVmem>(
         std::make_integer_sequence<int, MI * NI>{});
@@ -362,12 +380,14 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     // sub-step 1 of tile j; read the fragments of tile j+1's sub-step 0 and
-    // copy tile j+3 into tile j-1's stage
-    frags(j + 1, 0, f0);
-    issue(j + NST - 1);
+    // copy tile j+NST-1 into tile j-1's stage
+    frags(s_nx, 0, f0);
+    issue(s_cp, j + NST - 1);
     mma(f1);
     sched_spread<MI * NI, NF, kSchedDsRead, AI + BI, kSchedVmem>(
         std::make_integer_sequence<int, MI * NI>{});
+    s_cp = s_rd;
+    s_rd = s_nx;
   }
   // drain the copies still in flight before the workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -498,18 +518,22 @@ hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot
                        int64_t N, hipStream_t st) {
   const int G = (int)s.G();
   if (s.T <= 64) return launch_stream_gemm(GATED, s, A, sorted_slot, offsets, W, out, K, N, st);
-  // rows per m-tile: 256 when groups are large on average, else 128
+  // Large groups (>= 512 rows on average): 256 x 256 tiles, one workgroup
+  // per CU with a 5-stage ring (least L2 -> LDS traffic per flop).  Smaller
+  // groups: 128 x 256 tiles, two workgroups per CU with 3 stages each, so
+  // that one computes while the other waits on its copies (measured faster
+  // on groups of ~128-256 rows, which also waste less of a tile).
   const int64_t avg_rows = s.R() / (s.G() > 0 ? s.G() : 1);
   const int64_t ncols = GATED ? TBN / 2 : TBN;
   const int ntN = (int)((N + ncols - 1) / ncols);
-  if (avg_rows >= 192) {
+  if (avg_rows >= 512) {
     const unsigned grid = ((mtile_bound(s, 256) * (unsigned)ntN) + 7u) & ~7u;
-    hipLaunchKernelGGL((tiled_gemm_kernel<GATED, 256>), dim3(grid), dim3(256), 0, st,
+    hipLaunchKernelGGL((tiled_gemm_kernel<GATED, 256, 5, 1>), dim3(grid), dim3(256), 0, st,
                        (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W, (bf16_t*)out,
                        K, N, s.T, s.Tk(), s.k, G, ntN);
   } else {
     const unsigned grid = ((mtile_bound(s, 128) * (unsigned)ntN) + 7u) & ~7u;
-    hipLaunchKernelGGL((tiled_gemm_kernel<GATED, 128>), dim3(grid), dim3(256), 0, st,
+    hipLaunchKernelGGL((tiled_gemm_kernel<GATED, 128, 3, 2>), dim3(grid), dim3(256), 0, st,
                        (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W, (bf16_t*)out,
                        K, N, s.T, s.Tk(), s.k, G, ntN);
   }

@@ -153,6 +153,8 @@ GEMM_CASES = [
     ("tiled_zipf_empty_experts", 700, 520, 136, 24, 4, 0, "bf16", 1.5),
     ("tiled_one_big_group", 400, 192, 384, 3, 1, 0, "bf16", 3.0),
     ("tiled_T65", 65, 128, 64, 2, 2, 0, "bf16", None),
+    # >= 512 rows per group on average: the 256-row tiles; K % 32 = 8 in both GEMMs
+    ("tiled_bm256_ragged_k", 1100, 264, 136, 2, 1, 0, "bf16", None),
     ("f32_tiny_shape", 128, 256, 512, 8, 2, 0, "f32", None),
     ("f32_ragged_shared", 90, 72, 40, 5, 2, 2, "f32", 1.0),
 ]
