@@ -19,10 +19,11 @@
 // Kernels
 //   stream_gemm  bf16, T <= 64 (decode): in gemm_stream.hip.
 //   tiled_gemm   bf16, larger batches.  BM x 256 block tile (BM = 128 or
-//                256), 4 waves in a 2 x 2 grid, v_mfma_f32_32x32x16_bf16; K
-//                staged through a 5- or 3-stage LDS ring by direct global -> LDS
-//                copies.  Tiles of empty groups are never launched work;
-//                m-tiles are found on the device from offsets.
+//                256), 4 or 8 waves in a 2 x (2 or 4) grid,
+//                v_mfma_f32_32x32x16_bf16; K tiles of 32 or 64 staged
+//                through a ring of LDS stages by direct global -> LDS copies.
+//                Tiles of empty groups are never launched work; m-tiles are
+//                found on the device from offsets.
 //   f32_gemm     fp32 inputs: LDS-tiled FMA (fp32 vector and matrix peaks are
 //                equal on MI355X), 64x64 tiles.
 #include <type_traits>
@@ -80,21 +81,21 @@ __device__ bool find_mtile(const int32_t* offsets, int G, int BM, int tile, int*
 }
 
 // ============================================================= tiled_gemm
-// Block tile BM x 256 (weight rows), 4 waves in a 2 x 2 grid, each wave
-// BM/2 x 128 with v_mfma_f32_32x32x16_bf16 (the 16x16x32 form runs at half
-// the rate on gfx950).  GATED: the 256 weight rows of a tile are 128 gate
-// rows and the 128 matching up rows, so wave column wn owns 64 output columns
-// as 2 gate + 2 up 32-column blocks and SwiGLU pairs block ni with ni + 2 in
-// registers.
+// Block tile BM x 256 (weight rows), NW = 4 or 8 waves in a 2 x NW/2 grid,
+// each wave BM/2 x 512/NW with v_mfma_f32_32x32x16_bf16 (the 16x16x32 form
+// runs at half the rate on gfx950).  GATED: the 256 weight rows of a tile
+// are 128 gate rows and the 128 matching up rows, so wave column wn owns
+// 256/NW output columns as gate blocks plus the matching up blocks, and
+// SwiGLU pairs block ni with ni + NI/2 in registers.
 //
-// LDS: a ring of NST stages (5 for BM = 256 at one workgroup per CU; 3 for
-// BM = 128 at two per CU), each A [BM][32] and B [256][32] bf16 (K tiles
-// of 32), 64-byte rows whose 16-byte chunks are XOR-swizzled so that the
-// 16-byte MFMA operand reads are bank-conflict free.  K tiles are copied
-// global -> LDS directly (buffer loads with the LDS bit, no registers)
-// NST-1 tiles ahead.  A K tile is two MFMA sub-steps of K = 16; the operand
-// fragments of the next sub-step are read from LDS into a second register
-// set while the current sub-step's MFMAs run.  One barrier per K tile.
+// LDS: a ring of NST stages, each A [BM][SBK] and B [256][SBK] bf16 (K
+// tiles of SBK = 32 or 64), rows of 64 or 128 bytes whose 16-byte chunks are
+// XOR-swizzled so that the 16-byte MFMA operand reads are bank-conflict
+// free.  K tiles are copied global -> LDS directly (buffer loads with the
+// LDS bit, no registers) NST tiles ahead.  A K tile is SBK/16 MFMA
+// sub-steps of K = 16; the operand fragments of the next sub-step are read
+// from LDS into a second register set while the current sub-step's MFMAs
+// run.  One barrier per K tile.
 //
 // Out-of-range elements come back as zeros from the buffer loads' range
 // check: rows past the group (or past N), chunks past the end of K, and the
@@ -108,7 +109,6 @@ __device__ bool find_mtile(const int32_t* offsets, int G, int BM, int tile, int*
 // contiguous run of the tile order, in which one expert group's tiles come
 // as rectangles of its m-tiles by kBandN n-tiles.
 constexpr int TBN = 256;  // weight rows per block tile
-constexpr int SBK = 32;   // K per LDS stage
 
 // Buffer resource word 3 for raw (untyped, stride 0) buffers on gfx9-family
 // parts: 32-bit data format; the range check is then "offset >= num_records".
@@ -159,11 +159,13 @@ constexpr int kSchedVmem = 0x020, kSchedDsRead = 0x100;
 constexpr int kBandN = 4;
 
 // Tile lookup: returns false for workgroups past the last tile.
-// lds: 7 ints of workgroup-shared scratch.
+// NW waves per workgroup (4*64*NW >= 1024 groups covered); lds: 3 + NW
+// ints of workgroup-shared scratch.
+template <int NW>
 __device__ bool find_tile(const int32_t* offsets, int G, int BM, int ntN, int bid, int* g_out,
                           int* mt_out, int* nt_out, int* lds) {
   int* s_res = lds;       // [3]
-  int* s_wave = lds + 3;  // [4]
+  int* s_wave = lds + 3;  // [NW]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   int c[4];
@@ -183,7 +185,10 @@ __device__ bool find_tile(const int32_t* offsets, int G, int BM, int ntN, int bi
   if (lane == 63) s_wave[wave] = inc;
   if (tid == 0) s_res[0] = -1;
   __syncthreads();
-  const int total = (s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3]) * ntN;
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) total += s_wave[w];
+  total *= ntN;
   const int per = (total + 7) / 8;
   const int slot = bid >> 3;
   const int L = (bid & 7) * per + slot;  // XCD (bid mod 8) takes a contiguous run
@@ -212,16 +217,22 @@ __device__ bool find_tile(const int32_t* offsets, int G, int BM, int ntN, int bi
   return s_res[0] >= 0;
 }
 
-template <bool GATED, int BM, int NST, int OCC>
-__global__ __launch_bounds__(256, OCC) void tiled_gemm_kernel(
+template <bool GATED, int BM, int NST, int OCC, int NW, int SBK>
+__global__ __launch_bounds__(64 * NW, OCC) void tiled_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
     bf16_t* __restrict__ out, int64_t K, int64_t N, int64_t T, int64_t Tk, int64_t k,
     int G, int ntN) {
-  constexpr int MI = BM / 64;   // 32-row blocks per wave
-  constexpr int NI = 4;         // 32-column blocks per wave
-  constexpr int AI = BM / 64;   // A copies (16 rows, 1 KB) per wave per stage
-  constexpr int BI = TBN / 64;  // B copies per wave per stage
+  constexpr int WN = NW / 2;            // wave grid 2 x WN
+  constexpr int MI = BM / 64;           // 32-row blocks per wave (BM/2 rows)
+  constexpr int NI = 8 / WN;            // 32-column blocks per wave (256/WN columns)
+  constexpr int CPR = SBK / 8;          // 16-byte chunks per LDS row (4 or 8)
+  constexpr int RPC = 64 / CPR;         // rows per copy instruction (16 or 8)
+  constexpr int NSUB = SBK / 16;        // MFMA sub-steps per K tile
+  constexpr int AI = BM / (RPC * NW);   // A copies (1 KB each) per wave per stage
+  constexpr int BI = TBN / (RPC * NW);  // B copies per wave per stage
+  static_assert(SBK == 32 || SBK == 64, "K tile");
+  static_assert(AI >= 1 && BI >= 1 && NI >= 2, "tile split");
   constexpr int NF = MI + NI;   // operand fragments per sub-step
   constexpr uint32_t ROWB = SBK * 2;         // bytes per LDS row
   constexpr uint32_t STA = BM * ROWB;         // bytes per stage of A
@@ -232,13 +243,13 @@ __global__ __launch_bounds__(256, OCC) void tiled_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char ringB[NST * STB];
 
   static_assert(NST * (STA + STB) * OCC <= 160 * 1024, "ring fits the LDS");
-  static_assert((NST - 2) * (AI + BI) < 64, "vmcnt range");
+  static_assert((NST - 1) * (AI + BI) < 64 && NST >= 2, "vmcnt range");
 
   int g, mt, nt;
   // the tile lookup's scratch lives at the start of the ring; the barrier
   // after it keeps the first copies from overwriting it while it is read
-  if (!find_tile(offsets, G, BM, ntN, (int)blockIdx.x, &g, &mt, &nt,
-                 reinterpret_cast<int*>(ringA)))
+  if (!find_tile<NW>(offsets, G, BM, ntN, (int)blockIdx.x, &g, &mt, &nt,
+                     reinterpret_cast<int*>(ringA)))
     return;
   __syncthreads();
   const int tid = threadIdx.x;
@@ -262,33 +273,42 @@ __global__ __launch_bounds__(256, OCC) void tiled_gemm_kernel(
       __builtin_amdgcn_make_buffer_rsrc((void*)bbase, 0, (int)(uint32_t)(wrows * K * 2),
                                         kRsrcWord3);
 
-  // ---- copy plan: wave w fills A rows [w*BM/4, (w+1)*BM/4) and B rows
-  // [64w, 64w+64), 16 rows (1 KB) per copy.  Lane l lands on row l/4 of the
-  // 16, physical chunk l%4, which holds logical chunk (l%4) ^ ((row>>2)&3);
-  // the XOR term only depends on l, since the copies start at multiples of
-  // 16 rows.
-  const int lrow = lane >> 2;
-  const int kchunk = ((lane & 3) ^ ((lrow >> 2) & 3)) * 8;  // K element of the lane's chunk
+  // ---- copy plan: wave w fills A rows [w*BM/NW, (w+1)*BM/NW) and B rows
+  // [w*256/NW, (w+1)*256/NW), RPC rows (1 KB) per copy.  Lane l lands on row
+  // l/CPR of the copy, physical chunk l%CPR, which holds logical chunk
+  // (l%CPR) ^ sw(row); sw(row) = (row / (16/CPR)) & (CPR-1) makes the 16-byte
+  // reads of 16 consecutive rows hit 16 distinct bank groups.  For CPR = 4
+  // the XOR term only depends on l; for CPR = 8 also on the copy's parity.
+  const int lrow = lane / CPR;
+  auto kchunk_of = [&](int first_row) {  // K element of the lane's chunk
+    const int row = first_row + lrow;
+    return ((lane % CPR) ^ ((row / (16 / CPR)) & (CPR - 1))) * 8;
+  };
   uint32_t aoff[AI], boff[BI];  // byte offset of the lane's row + chunk, or kOOB
+  int akc[AI], bkc[BI];         // the lane's K element within a tile
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int r = wave * (BM / 4) + 16 * i + lrow;
+    const int r0 = wave * (BM / NW) + RPC * i;
+    const int r = r0 + lrow;
+    akc[i] = kchunk_of(r0);
     uint32_t o = kOOB;
     if (r < rows) {
       const int64_t src_row =
           GATED ? row_token(row_begin + r, sorted_slot, Tk, k, T) : (int64_t)r;
-      o = (uint32_t)src_row * Kb + (uint32_t)kchunk * 2;
+      o = (uint32_t)src_row * Kb + (uint32_t)akc[i] * 2;
     }
     aoff[i] = o;
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    const int br = wave * (TBN / 4) + 16 * i + lrow;  // 0..255
+    const int b0 = wave * (TBN / NW) + RPC * i;
+    const int br = b0 + lrow;  // 0..255
+    bkc[i] = kchunk_of(b0);
     const int64_t c = n0 + (GATED ? (br & 127) : br);
     uint32_t o = kOOB;
     if (c < N) {
       const int64_t wrow = GATED ? (br < 128 ? c : N + c) : c;
-      o = (uint32_t)wrow * Kb + (uint32_t)kchunk * 2;
+      o = (uint32_t)wrow * Kb + (uint32_t)bkc[i] * 2;
     }
     boff[i] = o;
   }
@@ -300,38 +320,40 @@ __global__ __launch_bounds__(256, OCC) void tiled_gemm_kernel(
   // copies of K tile j into ring stage sg (all out of range past the end)
   auto issue = [&](int sg, int j) {
     const int64_t k0 = (int64_t)j * SBK;
-    const bool kin = k0 + kchunk < K;
     const uint32_t kb = (uint32_t)k0 * 2;
     const uint32_t sa = ring_a + (uint32_t)sg * STA, sb = ring_b + (uint32_t)sg * STB;
 #pragma unroll
     for (int i = 0; i < AI; ++i)
-      copy16(ra, kin ? aoff[i] + kb : kOOB, sa + (uint32_t)(wave * (BM / 4) + 16 * i) * ROWB);
+      copy16(ra, k0 + akc[i] < K ? aoff[i] + kb : kOOB,
+             sa + (uint32_t)(wave * (BM / NW) + RPC * i) * ROWB);
 #pragma unroll
     for (int i = 0; i < BI; ++i)
-      copy16(rb, kin ? boff[i] + kb : kOOB, sb + (uint32_t)(wave * (TBN / 4) + 16 * i) * ROWB);
+      copy16(rb, k0 + bkc[i] < K ? boff[i] + kb : kOOB,
+             sb + (uint32_t)(wave * (TBN / NW) + RPC * i) * ROWB);
   };
 
   // ---- wave sub-tile and its fragment addresses.  Fragment rows are
   // wm*BM/2 + 32*mi + (l%32) (A) and the brow below (B); their swizzle term
-  // ((row>>2)&3) is ((l%32)>>2)&3 for all of them.
-  const int wm = wave >> 1, wn = wave & 1;
+  // ((row>>2)&3) is ((l%32)>>2)&3 for all of them.  GATED: wave column wn
+  // owns 128/WN gate rows of B and the matching up rows (128 further on).
+  const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, lh = lane >> 5;
-  const int q = (lr >> 2) & 3;
-  uint32_t fa[2], fb[2];  // per sub-step s: byte offset of block 0 inside a stage of A / B
+  const int q = (lr / (16 / CPR)) & (CPR - 1);  // swizzle term of every fragment row
+  uint32_t fa[NSUB], fb[NSUB];  // per sub-step s: byte offset of block 0 in a stage of A / B
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < NSUB; ++s) {
     const uint32_t ch = (uint32_t)(((2 * s + lh) ^ q) << 4);
     fa[s] = (uint32_t)(wm * (BM / 2) + lr) * ROWB + ch;
-    fb[s] = (uint32_t)((GATED ? 64 : 128) * wn + lr) * ROWB + ch;
+    fb[s] = (uint32_t)((GATED ? 128 / WN : 256 / WN) * wn + lr) * ROWB + ch;
   }
-  // B block ni starts at row bro(ni) + (64 or 128) * wn
+  // B block ni starts at row bro(ni) + (128/WN or 256/WN) * wn
   constexpr auto bro = [](int ni) constexpr -> int {
-    return GATED ? (ni < 2 ? 0 : 128) + 32 * (ni & 1) : 32 * ni;
+    return GATED ? (ni < NI / 2 ? 0 : 128) + 32 * (ni % (NI / 2)) : 32 * ni;
   };
   auto frags = [&](int sg, int s, u32x4 (&f)[NF]) {
     const unsigned char* sa = ringA + (uint32_t)sg * STA;
     const unsigned char* sb = ringB + (uint32_t)sg * STB;
-    // in the order the MFMAs (mi-major) consume them: A0, B0..B3, A1, A2, ...
+    // in the order the MFMAs (mi-major) consume them: A0, B0.., A1, A2, ...
     f[0] = *reinterpret_cast<const u32x4*>(sa + fa[s]);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
@@ -358,35 +380,56 @@ __global__ __launch_bounds__(256, OCC) void tiled_gemm_kernel(
   const int nk = (int)((K + SBK - 1) / SBK);
   auto next = [](int sg) { return sg + 1 == NST ? 0 : sg + 1; };
   u32x4 f0[NF], f1[NF];
+  // tiles 0 .. NST-1 into stages 0 .. NST-1; wait for tile 0
 #pragma unroll
-  for (int t = 0; t < NST - 1; ++t) issue(t, t);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * (AI + BI)) : "memory");
+  for (int t = 0; t < NST; ++t) issue(t, t);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 1) * (AI + BI)) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   frags(0, 0, f0);
-  int s_rd = 0;        // stage of tile j
-  int s_cp = NST - 1;  // stage of tile j-1, which takes tile j+NST-1
+  int s_rd = 0;  // stage of tile j
   for (int j = 0; j < nk; ++j) {
     const int s_nx = next(s_rd);  // stage of tile j+1
-    // sub-step 0 of tile j; read sub-step 1's fragments meanwhile
-    frags(s_rd, 1, f1);
-    mma(f0);
-    sched_spread<MI * NI, NF, kSchedDsRead, 0, kSchedVmem>(
-        std::make_integer_sequence<int, MI * NI>{});
-    // tile j+1 has landed: this wave's copies, then everyone's (a plain
-    // s_barrier: __syncthreads()'s release fence would wait for all copies);
-    // after it, every wave is also done reading the stage of tile j-1
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 3) * (AI + BI)) : "memory");
+    // sub-steps 0 .. NSUB-2 of tile j, reading the next sub-step's
+    // fragments meanwhile (f0 / f1 alternate)
+#pragma unroll
+    for (int s = 0; s + 1 < NSUB; ++s) {
+      if (s % 2 == 0) {
+        frags(s_rd, s + 1, f1);
+        mma(f0);
+      } else {
+        frags(s_rd, s + 1, f0);
+        mma(f1);
+      }
+      sched_spread<MI * NI, NF, kSchedDsRead, 0, kSchedVmem>(
+          std::make_integer_sequence<int, MI * NI>{});
+    }
+    // tile j+1 has landed (this wave's copies, then everyone's: a plain
+    // s_barrier, since __syncthreads()'s release fence would wait for all
+    // copies), and every wave's reads of tile j are complete (lgkmcnt(0)
+    // before the barrier), so tile j's stage can be refilled
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NST - 2) * (AI + BI)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // sub-step 1 of tile j; read the fragments of tile j+1's sub-step 0 and
-    // copy tile j+NST-1 into tile j-1's stage
-    frags(s_nx, 0, f0);
-    issue(s_cp, j + NST - 1);
-    mma(f1);
+    // last sub-step of tile j; read the fragments of tile j+1's sub-step 0
+    // and copy tile j+NST into tile j's stage
+    constexpr bool odd = (NSUB - 1) % 2 == 1;
+    if constexpr (odd) {
+      frags(s_nx, 0, f0);
+      issue(s_rd, j + NST);
+      mma(f1);
+    } else {
+      frags(s_nx, 0, f1);
+      issue(s_rd, j + NST);
+      mma(f0);
+    }
     sched_spread<MI * NI, NF, kSchedDsRead, AI + BI, kSchedVmem>(
         std::make_integer_sequence<int, MI * NI>{});
-    s_cp = s_rd;
+    if constexpr (!odd) {
+      // f0 must hold the next tile's sub-step 0
+#pragma unroll
+      for (int i = 0; i < NF; ++i) f0[i] = f1[i];
+    }
     s_rd = s_nx;
   }
   // drain the copies still in flight before the workgroup's LDS is released
@@ -402,14 +445,15 @@ __global__ __launch_bounds__(256, OCC) void tiled_gemm_kernel(
       bf16_t* orow = out + (row_begin + r) * N;
       if constexpr (GATED) {
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int64_t c = n0 + 64 * wn + 32 * ni + lr;
-          if (c < N) orow[c] = f32_to_bf16(swiglu(acc[mi][ni][e], acc[mi][ni + 2][e]));
+        for (int ni = 0; ni < NI / 2; ++ni) {
+          const int64_t c = n0 + (128 / WN) * wn + 32 * ni + lr;
+          if (c < N)
+            orow[c] = f32_to_bf16(swiglu(acc[mi][ni][e], acc[mi][ni + NI / 2][e]));
         }
       } else {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          const int64_t c = n0 + 128 * wn + 32 * ni + lr;
+          const int64_t c = n0 + (256 / WN) * wn + 32 * ni + lr;
           if (c < N) orow[c] = f32_to_bf16(acc[mi][ni][e]);
         }
       }
@@ -518,25 +562,29 @@ hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot
                        int64_t N, hipStream_t st) {
   const int G = (int)s.G();
   if (s.T <= 64) return launch_stream_gemm(GATED, s, A, sorted_slot, offsets, W, out, K, N, st);
-  // Large groups (>= 512 rows on average): 256 x 256 tiles, one workgroup
-  // per CU with a 5-stage ring (least L2 -> LDS traffic per flop).  Smaller
-  // groups: 128 x 256 tiles, two workgroups per CU with 3 stages each, so
-  // that one computes while the other waits on its copies (measured faster
-  // on groups of ~128-256 rows, which also waste less of a tile).
+  // Tile shapes, as measured fastest on the MI355X:
+  //  - large groups (>= 512 rows on average): 256 x 256 tiles, 8 waves (two
+  //    per SIMD, so one computes while the other waits), K tiles of 64
+  //    (whole 128-byte lines per copied row) in 2 stages of 64 KB;
+  //  - smaller groups, gate_up: 128 x 256 tiles, 8 waves, K tiles of 64, 3
+  //    stages; down: 128 x 256 tiles, 4 waves, K tiles of 32, two workgroups
+  //    per CU with 3 stages each.
   const int64_t avg_rows = s.R() / (s.G() > 0 ? s.G() : 1);
   const int64_t ncols = GATED ? TBN / 2 : TBN;
   const int ntN = (int)((N + ncols - 1) / ncols);
+#define MOE_TILED(bm, nst, occ, nw, sbk)                                                 \
+  hipLaunchKernelGGL((tiled_gemm_kernel<GATED, bm, nst, occ, nw, sbk>),                 \
+                     dim3(((mtile_bound(s, bm) * (unsigned)ntN) + 7u) & ~7u), dim3(64 * nw), \
+                     0, st, (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W,      \
+                     (bf16_t*)out, K, N, s.T, s.Tk(), s.k, G, ntN)
   if (avg_rows >= 512) {
-    const unsigned grid = ((mtile_bound(s, 256) * (unsigned)ntN) + 7u) & ~7u;
-    hipLaunchKernelGGL((tiled_gemm_kernel<GATED, 256, 5, 1>), dim3(grid), dim3(256), 0, st,
-                       (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W, (bf16_t*)out,
-                       K, N, s.T, s.Tk(), s.k, G, ntN);
+    MOE_TILED(256, 2, 1, 8, 64);
+  } else if (GATED) {
+    MOE_TILED(128, 3, 1, 8, 64);
   } else {
-    const unsigned grid = ((mtile_bound(s, 128) * (unsigned)ntN) + 7u) & ~7u;
-    hipLaunchKernelGGL((tiled_gemm_kernel<GATED, 128, 3, 2>), dim3(grid), dim3(256), 0, st,
-                       (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W, (bf16_t*)out,
-                       K, N, s.T, s.Tk(), s.k, G, ntN);
+    MOE_TILED(128, 3, 2, 4, 32);
   }
+#undef MOE_TILED
   return hipGetLastError();
 }
 

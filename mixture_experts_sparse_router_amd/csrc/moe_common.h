@@ -69,10 +69,16 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 
 // --------------------------------------------------------- token of a row
 // Row r of the permuted buffers belongs to token sorted_slot[r] / k for the
-// routed rows r < T*k, and to token (r - T*k) % T for the shared rows.
+// routed rows r < T*k, and to token (r - T*k) % T for the shared rows.  Every
+// quantity is below 2^31 (R < 2^31), so the divisions are 32-bit.
+__device__ __forceinline__ int64_t token_of(int64_t r, int32_t slot, int64_t Tk, int64_t k,
+                                            int64_t T) {
+  return r < Tk ? (int64_t)((uint32_t)slot / (uint32_t)k)
+                : (int64_t)((uint32_t)(r - Tk) % (uint32_t)T);
+}
 __device__ __forceinline__ int64_t row_token(int64_t r, const int32_t* sorted_slot,
                                              int64_t Tk, int64_t k, int64_t T) {
-  return r < Tk ? (int64_t)sorted_slot[r] / k : (r - Tk) % T;
+  return token_of(r, r < Tk ? sorted_slot[r] : 0, Tk, k, T);
 }
 
 // ----------------------------------------------------------- host helpers
