@@ -27,6 +27,8 @@
 //   topk_wave: one wave per token; each lane holds ceil(E/64) logits and k
 //     rounds of a wave-wide argmax (butterfly over (value, index)) pick the
 //     experts.
+#include <atomic>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -36,6 +38,7 @@ constexpr int kThreads = 256;
 constexpr int kKC = 32;          // K elements per staged chunk (tiled)
 constexpr int kMaxP = 256;       // experts per pass (tiled)
 constexpr int kMaxE = 1024;
+constexpr int kMaxDevices = 64;
 
 template <typename In>
 __device__ __forceinline__ void load8(const In* p, float* out);
@@ -624,13 +627,19 @@ hipError_t launch_dt(const Shape& s, const void* x, const void* Wr, const float*
   if constexpr (sizeof(In) == 2) {
     const unsigned grid = (unsigned)((s.T + kScreenTT - 1) / kScreenTT);
     const size_t lds = (size_t)screen_lds((int)s.E).total;
-    static bool lds_opt_in = false;  // allow more than 64 KB of dynamic LDS
-    if (!lds_opt_in) {
-      hipError_t e = hipFuncSetAttribute((const void*)route_screen_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)screen_lds(1024).total);
+    // allow more than 64 KB of dynamic LDS, once per device (the attribute
+    // belongs to the device's copy of the kernel)
+    static std::atomic<bool> lds_opt_in[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!lds_opt_in[dev].load(std::memory_order_acquire)) {
+      e = hipFuncSetAttribute((const void*)route_screen_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)screen_lds(1024).total);
       if (e != hipSuccess) return e;
-      lds_opt_in = true;
+      lds_opt_in[dev].store(true, std::memory_order_release);
     }
     hipLaunchKernelGGL(route_screen_kernel, dim3(grid), dim3(kThreads), lds, st,
                        (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, s.T, s.d, (int)s.E,
