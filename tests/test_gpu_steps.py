@@ -155,6 +155,10 @@ GEMM_CASES = [
     ("tiled_T65", 65, 128, 64, 2, 2, 0, "bf16", None),
     # >= 512 rows per group on average: the 256-row tiles; K % 32 = 8 in both GEMMs
     ("tiled_bm256_ragged_k", 1100, 264, 136, 2, 1, 0, "bf16", None),
+    # K shorter than one K tile (40 and 24): one partly zero-filled tile
+    ("tiled_k_below_tile", 100, 40, 24, 4, 2, 0, "bf16", None),
+    # the most expert groups the library takes (E + S = 1024)
+    ("tiled_1024_groups", 128, 64, 32, 1000, 2, 24, "bf16", None),
     ("f32_tiny_shape", 128, 256, 512, 8, 2, 0, "f32", None),
     ("f32_ragged_shared", 90, 72, 40, 5, 2, 2, "f32", 1.0),
 ]
