@@ -411,19 +411,20 @@ __global__ __launch_bounds__(64 * NW, OCC) void tiled_gemm_kernel(
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NST - 2) * (AI + BI)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // last sub-step of tile j; read the fragments of tile j+1's sub-step 0
-    // and copy tile j+NST into tile j's stage
+    // last sub-step of tile j; copy tile j+NST into tile j's stage (first:
+    // the copies are the long pole) and read the fragments of tile j+1's
+    // sub-step 0
     constexpr bool odd = (NSUB - 1) % 2 == 1;
     if constexpr (odd) {
-      frags(s_nx, 0, f0);
       issue(s_rd, j + NST);
+      frags(s_nx, 0, f0);
       mma(f1);
     } else {
-      frags(s_nx, 0, f1);
       issue(s_rd, j + NST);
+      frags(s_nx, 0, f1);
       mma(f0);
     }
-    sched_spread<MI * NI, NF, kSchedDsRead, AI + BI, kSchedVmem>(
+    sched_spread<MI * NI, AI + BI, kSchedVmem, NF, kSchedDsRead>(
         std::make_integer_sequence<int, MI * NI>{});
     if constexpr (!odd) {
       // f0 must hold the next tile's sub-step 0
