@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--rotate", type=int, default=1,
+                   help="use N device copies of the expert weights in turn, so that no step "
+                        "finds the previous step's weights in a cache (default 1)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (torch copy_) 10 times: the "
                         "reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -150,6 +153,9 @@ def main():
         return torch.from_numpy(a).cuda()
 
     d = {k: dev(v) for k, v in inp.items()}
+    rot = max(1, args.rotate)
+    w_gu = [d["W_gate_up"]] + [d["W_gate_up"].clone() for _ in range(rot - 1)]
+    w_dn = [d["W_down"]] + [d["W_down"].clone() for _ in range(rot - 1)]
     dt = moe.MOE_DT_BF16 if cfg.dtype == "bf16" else moe.MOE_DT_F32
     s = moe.shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.S, dt)
     ws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
@@ -157,16 +163,16 @@ def main():
                     device="cuda")
     views = moe.workspace_views(s, ws)
 
-    def step():
-        moe.moe_layer_forward(s, d["x"], d["W_router"], d["bias"], d["W_gate_up"],
-                              d["W_down"], y, ws)
+    def step(i=0):
+        moe.moe_layer_forward(s, d["x"], d["W_router"], d["bias"], w_gu[i % rot],
+                              w_dn[i % rot], y, ws)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_per_step = el / args.steps * 1e3
@@ -225,7 +231,8 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
                    "k": cfg.k, "shared": cfg.S, "zipf_s": cfg.zipf_s, "seed": seed,
-                   "active_experts": ac["active"], "parallelism": "single GPU"},
+                   "active_experts": ac["active"], "weight_copies": rot,
+                  "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"alg_bytes": ac["layer_bytes"], "alg_flops": ac["layer_flops"],
                   "hbm_frac": round(ac["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
