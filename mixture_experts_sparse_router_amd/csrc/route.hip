@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void route_tiled_kernel(
 //      expert, so identical rows still tie exactly); the top-k and weights
 //      are taken over these exact logits by topk_wave.
 // The result is the same selection and weights as the fp64-everywhere path.
-constexpr int kScreenTT = 16;                  // tokens per workgroup
+constexpr int kScreenTT = 16;                  // token rows of the screen (LDS rows)
 constexpr double kScreenRel = 7.62939453125e-06;  // 2^-17
 constexpr int kCandBatch = 4;                  // candidates per fp64 pass
 
@@ -323,7 +323,8 @@ __host__ __device__ inline ScreenLds screen_lds(int E) {
 __global__ __launch_bounds__(kThreads, 2) void route_screen_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int64_t T, int64_t d, int E,
-    int k) {
+    int k, int tok) {
+  // tok (8 or 16): tokens per workgroup; screen rows past them repeat the last
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const ScreenLds L = screen_lds(E);
   double* lg = reinterpret_cast<double*>(smem + L.lg);  // [16][E]
@@ -334,8 +335,9 @@ __global__ __launch_bounds__(kThreads, 2) void route_screen_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, kb = lane >> 4;
-  const int64_t t0 = (int64_t)blockIdx.x * kScreenTT;
-  const int64_t tj = t0 + j < T ? t0 + j : T - 1;  // padding tokens repeat the last
+  const int64_t t0 = (int64_t)blockIdx.x * tok;
+  const int jt = j < tok ? j : tok - 1;
+  const int64_t tj = t0 + jt < T ? t0 + jt : T - 1;  // padding tokens repeat the last
   const bf16_t* xa = x + tj * d;
   const int64_t nch = (d + 31) / 32;               // K chunks of 32
 
@@ -489,7 +491,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_screen_kernel(
 
   // ---- 2./3. one wave per token
   int* mycand = cand + wave * E;
-  for (int tl = wave; tl < kScreenTT; tl += kThreads / 64) {
+  for (int tl = wave; tl < tok; tl += kThreads / 64) {
     const int64_t t = t0 + tl;
     if (t >= T) break;
     double* row = lg + (int64_t)tl * E;
@@ -625,15 +627,29 @@ hipError_t launch_dt(const Shape& s, const void* x, const void* Wr, const float*
                      int32_t* idx, float* w, hipStream_t st) {
   if (s.T <= 64) return launch_small<In>(s, x, Wr, bias, idx, w, st);
   if constexpr (sizeof(In) == 2) {
-    const unsigned grid = (unsigned)((s.T + kScreenTT - 1) / kScreenTT);
     const size_t lds = (size_t)screen_lds((int)s.E).total;
     // allow more than 64 KB of dynamic LDS, once per device (the attribute
     // belongs to the device's copy of the kernel)
     static std::atomic<bool> lds_opt_in[kMaxDevices];
+    static std::atomic<int> cu_count[kMaxDevices];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int cus = cu_count[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+      e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      cu_count[dev].store(cus, std::memory_order_relaxed);
+    }
+    // 16 tokens per workgroup; 8 when that still leaves workgroup slots (two
+    // per CU) empty and the router matrix is small enough (<= 1 MB) for the
+    // extra workgroups to re-read it cheaply (measured: E=128, d=2048 faster;
+    // E=256, d=7168 and T=8192 slower)
+    int tok = kScreenTT;
+    if ((s.T + kScreenTT - 1) / kScreenTT < 2 * (int64_t)cus && s.E * s.d * 2 <= (1 << 20))
+      tok = 8;
+    const unsigned grid = (unsigned)((s.T + tok - 1) / tok);
     if (!lds_opt_in[dev].load(std::memory_order_acquire)) {
       e = hipFuncSetAttribute((const void*)route_screen_kernel,
                               hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -643,7 +659,7 @@ hipError_t launch_dt(const Shape& s, const void* x, const void* Wr, const float*
     }
     hipLaunchKernelGGL(route_screen_kernel, dim3(grid), dim3(kThreads), lds, st,
                        (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, s.T, s.d, (int)s.E,
-                       (int)s.k);
+                       (int)s.k, tok);
     return hipGetLastError();
   } else {
     if (s.E > 512) return launch_tiled<In, 8>(s, x, Wr, bias, idx, w, st);
