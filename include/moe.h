@@ -31,7 +31,9 @@
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
- *     library allocates and frees nothing and keeps no state between calls.
+ *     library allocates and frees nothing and carries no data between calls
+ *     (it only caches per-device configuration: the CU count and one kernel
+ *     attribute, set on first use).
  *   - Tensors are dense row-major, last dimension contiguous, 16-byte aligned.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work; results are valid once the stream is
@@ -41,7 +43,10 @@
  *   - Element type: dt = MOE_DT_BF16 (bfloat16) or MOE_DT_F32 (binary32) for
  *     x, W_router, W_gate_up, W_down, act, expert_out and y alike.  Routing
  *     weights are always float32, indices int32.
- *   - Numerics: router logits are accumulated in fp64; GEMMs multiply in dt
+ *   - Numerics: router logits are accumulated in fp64 (for bf16 batches of
+ *     more than 64 tokens, only for the experts that a bf16 screen with a
+ *     proven error bound cannot rule out; selection and weights are the
+ *     same as with fp64 everywhere); GEMMs multiply in dt
  *     and accumulate in fp32; act and expert_out are rounded to dt (round to
  *     nearest even); the combine accumulates in fp32 in a fixed order, so
  *     repeated calls are bitwise identical.
