@@ -1,0 +1,62 @@
+"""bench.py's contract on the host: the refusal of more than one GPU, the
+algorithmic byte / flop counts it divides by, and the rule that committed
+HBM traffic counters only count while the kernel they measured is unchanged."""
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_algorithmic_counts_by_hand():
+    b = _bench()
+
+    class Cfg:
+        T, d, f, E, k, S, dtype = 16, 2880, 2880, 32, 4, 0, "bf16"
+
+    counts = [2] * 29 + [0] * 3  # 29 active experts
+    ac = b.alg_counts(Cfg, counts)
+    R = 16 * 4
+    assert ac["active"] == 29 and ac["R"] == R
+    w_gu = 29 * 2 * 2880 * 2880 * 2
+    assert ac["gate_up_bytes"] == w_gu + 16 * 2880 * 2 + R * 2880 * 2
+    assert ac["gate_up_bytes"] == 962611200  # the decode workload's figure
+    assert ac["down_bytes"] == 29 * 2880 * 2880 * 2 + 2 * R * 2880 * 2
+    assert ac["gate_up_flops"] == 4 * 2880 * 2880 * R
+    assert ac["layer_flops"] == 2 * 16 * 2880 * 32 + 6 * 2880 * 2880 * R
+
+    class Cfg5(Cfg):
+        T, d, f, E, k, S = 4096, 7168, 2048, 256, 8, 1
+
+    ac5 = b.alg_counts(Cfg5, [128] * 256 + [4096])
+    assert ac5["active"] == 257 and ac5["R"] == 4096 * 8 + 4096
+
+
+def test_traffic_only_while_the_kernel_is_unchanged(tmp_path, monkeypatch):
+    b = _bench()
+    data = json.load(open(b.TRAFFIC_FILE))
+    ent = data["gpt_oss_20b_decode"]
+    assert b.load_traffic("gpt_oss_20b_decode") == ent["bytes_per_launch"]
+    assert b.load_traffic("no_such_workload") is None
+    # a changed kernel source invalidates the committed counters
+    src = tmp_path / "gemm_stream.hip"
+    src.write_bytes(open(b.GEMM_SRC, "rb").read() + b"\n// changed\n")
+    monkeypatch.setattr(b, "GEMM_SRC", str(src))
+    assert b.load_traffic("gpt_oss_20b_decode") is None
