@@ -2,13 +2,17 @@
 grouped SwiGLU GEMMs -> combine) through libmoe's C ABI on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--no-cpu]
+                    [--no-prefill]
 
 A step is one moe_layer_forward over one batch of seeded synthetic inputs
 already resident in HBM.  Default workload: the gpt-oss-20b-shaped decode
 layer (T=16, d=2880, f=2880, E=32, top-4, bf16).  Prints ONE JSON line:
-tokens/s of the whole layer, the roofline of the dominant kernel (the
-gate_up grouped GEMM, HBM-bound at decode) measured with HIP events on the
-stream the kernels run on, and the fp64 CPU oracle's rate on the host cores.
+tokens/s of the whole layer (wall clock around exactly K steps, with the
+same interval also measured by HIP events on the stream the kernels run
+on), the roofline of the dominant kernel (the gate_up grouped GEMM), the
+fp64 CPU oracle's rate on the host cores, and, under "prefill", the same
+layer measurement for the Mixtral-8x7B-shaped prefill workload against the
+bf16 MFMA peak.
 """
 import argparse
 import hashlib
@@ -25,9 +29,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_sparse_router_amd", "csrc", "gemm_stream.hip")
+PREFILL_CONFIG = 3             # Mixtral-8x7B-shaped prefill
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
@@ -37,13 +42,16 @@ def parse():
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the Mixtral-shaped prefill measurement")
+    p.add_argument("--prefill-steps", type=int, default=20)
     p.add_argument("--rotate", type=int, default=1,
                    help="use N device copies of the expert weights in turn, so that no step "
                         "finds the previous step's weights in a cache (default 1)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (torch copy_) 10 times: the "
                         "reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
-    return p.parse_args()
+    return p.parse_args(argv)
 
 
 def alg_counts(cfg, counts):
@@ -63,6 +71,15 @@ def alg_counts(cfg, counts):
     return dict(active=active, R=R, layer_bytes=layer_bytes, gate_up_bytes=gate_up_bytes,
                 down_bytes=down_bytes, layer_flops=layer_flops,
                 gate_up_flops=4 * cfg.d * cfg.f * R, down_flops=2 * cfg.d * cfg.f * R)
+
+
+def binding_roof(flops, nbytes, fp32=False):
+    """The roof that bounds a kernel of these algorithmic flops and bytes: the
+    one whose time at peak is longer (flop/byte below the ridge -> HBM)."""
+    peak_tf = FP32_PEAK_TFLOPS if fp32 else BF16_PEAK_TFLOPS
+    t_mfma = flops / (peak_tf * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    return ("mfma", peak_tf) if t_mfma > t_hbm else ("hbm", HBM_PEAK_GBS)
 
 
 def time_calls(torch, fn, n):
@@ -94,7 +111,20 @@ def load_traffic(key):
     return ent.get("bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, inp, seconds):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload's
+    tokens (calls of at most 16 tokens, cycling through the batch, until
+    `seconds` of wall time have passed)."""
     import numpy as np
     import oracle
     T = cfg.T
@@ -113,18 +143,148 @@ def cpu_baseline(cfg, inp, seconds):
         if el >= seconds:
             break
     return dict(value=n_done / el, unit="tokens/s", cores=oracle.num_threads(),
-                kind="oracle",
+                kind="oracle", cpu_model=cpu_model(),
                 sample=f"{n_done} tokens of the same workload in {calls} oracle calls of "
                        f"<= {per_call} tokens, {el:.1f} s wall")
 
 
-def main():
-    args = parse()
+class Layer:
+    """Device buffers and the step function of one workload."""
+
+    def __init__(self, torch, moe, cfg, seed, rotate=1):
+        import numpy as np
+        import moe_synth
+        self.cfg, self.seed = cfg, seed
+        self.inp = moe_synth.make_layer_inputs(cfg, seed)
+
+        def dev(a):
+            if a is None:
+                return None
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+            return torch.from_numpy(a).cuda()
+
+        self.d = {k: dev(v) for k, v in self.inp.items()}
+        self.rot = max(1, rotate)
+        self.w_gu = [self.d["W_gate_up"]] + [self.d["W_gate_up"].clone()
+                                             for _ in range(self.rot - 1)]
+        self.w_dn = [self.d["W_down"]] + [self.d["W_down"].clone()
+                                          for _ in range(self.rot - 1)]
+        self.dt = moe.MOE_DT_BF16 if cfg.dtype == "bf16" else moe.MOE_DT_F32
+        self.s = moe.shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.S, self.dt)
+        self.ws = torch.empty(moe.workspace_size(self.s), dtype=torch.uint8, device="cuda")
+        self.y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16 if self.dt else torch.float32,
+                             device="cuda")
+        self.views = moe.workspace_views(self.s, self.ws)
+        self.moe = moe
+
+    def step(self, i=0):
+        d = self.d
+        self.moe.moe_layer_forward(self.s, d["x"], d["W_router"], d["bias"],
+                                   self.w_gu[i % self.rot], self.w_dn[i % self.rot], self.y,
+                                   self.ws)
+
+    def kernel_times(self, torch, n):
+        """Average time of each step's entry point called alone, back to back,
+        on the buffers of the last layer call."""
+        moe, s, d, v = self.moe, self.s, self.d, self.views
+        return {
+            "route": time_calls(torch, lambda: moe.moe_route(
+                s, d["x"], d["W_router"], d["bias"], v["topk_idx"], v["topk_w"]), n),
+            "permute": time_calls(torch, lambda: moe.moe_permute(
+                s, v["topk_idx"], v["counts"], v["offsets"], v["sorted_slot"],
+                v["slot_pos"]), n),
+            "gate_up": time_calls(torch, lambda: moe.moe_grouped_gemm_gate_up(
+                s, d["x"], v["sorted_slot"], v["offsets"], d["W_gate_up"], v["act"]), n),
+            "down": time_calls(torch, lambda: moe.moe_grouped_gemm_down(
+                s, v["act"], v["offsets"], d["W_down"], v["expert_out"]), n),
+            "combine": time_calls(torch, lambda: moe.moe_combine(
+                s, v["expert_out"], v["slot_pos"], v["topk_w"], self.y), n),
+        }
+
+    def timed_steps(self, torch, steps):
+        """Exactly `steps` layer calls between two synchronisations: wall
+        clock, and HIP events recorded on the stream the calls enqueue on."""
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(st)
+        for i in range(steps):
+            self.step(i)
+        e1.record(st)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, e0.elapsed_time(e1) * 1e-3
+
+    def summary(self, torch, kt, layer_s):
+        cfg = self.cfg
+        counts = self.views["counts"].cpu().numpy()
+        ac = alg_counts(cfg, counts)
+        fp32 = self.dt == self.moe.MOE_DT_F32
+        bound, peak = binding_roof(ac["gate_up_flops"], ac["gate_up_bytes"], fp32)
+        if bound == "hbm":
+            achieved, unit = ac["gate_up_bytes"] / kt["gate_up"] / 1e9, "GB/s"
+        else:
+            achieved, unit = ac["gate_up_flops"] / kt["gate_up"] / 1e12, "TFLOP/s"
+        roof = dict(bound=bound, kernel="grouped_gemm_gate_up", achieved=round(achieved, 2),
+                    peak=peak, unit=unit, frac=round(achieved / peak, 4),
+                    traffic=load_traffic(cfg.name),
+                    alg_bytes_per_launch=ac["gate_up_bytes"],
+                    alg_flops_per_launch=ac["gate_up_flops"],
+                    avg_launch_us=round(kt["gate_up"] * 1e6, 2))
+        mfma_peak = FP32_PEAK_TFLOPS if fp32 else BF16_PEAK_TFLOPS
+        layer = {"alg_bytes": ac["layer_bytes"], "alg_flops": ac["layer_flops"],
+                 "hbm_frac": round(ac["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
+                 "mfma_frac": round(ac["layer_flops"] / layer_s / 1e12 / mfma_peak, 4),
+                 "kernel_us": {k: round(v * 1e6, 2) for k, v in kt.items()},
+                 "gemm_frac": {
+                     "gate_up_hbm": round(ac["gate_up_bytes"] / kt["gate_up"] / 1e9
+                                          / HBM_PEAK_GBS, 4),
+                     "gate_up_mfma": round(ac["gate_up_flops"] / kt["gate_up"] / 1e12
+                                           / mfma_peak, 4),
+                     "down_hbm": round(ac["down_bytes"] / kt["down"] / 1e9 / HBM_PEAK_GBS, 4),
+                     "down_mfma": round(ac["down_flops"] / kt["down"] / 1e12 / mfma_peak, 4)}}
+        return ac, roof, layer
+
+
+def config_dict(cfg, seed, ac, rot):
+    return {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
+            "k": cfg.k, "shared": cfg.S, "zipf_s": cfg.zipf_s, "seed": seed,
+            "active_experts": ac["active"], "weight_copies": rot,
+            "parallelism": "single GPU"}
+
+
+def prefill_extra(torch, moe, steps, no_cpu):
+    """The Mixtral-8x7B-shaped prefill layer (T=8192, d=4096, f=14336, E=8,
+    top-2): layer tokens/s and its fraction of the bf16 MFMA peak."""
+    import moe_synth
+    cfg = moe_synth.CONFIGS[PREFILL_CONFIG]
+    L = Layer(torch, moe, cfg, PREFILL_CONFIG)
+    for i in range(3):
+        L.step(i)
+    kt = L.kernel_times(torch, 5)
+    wall, ev = L.timed_steps(torch, steps)
+    ac, roof, layer = L.summary(torch, kt, ev / steps)
+    out = {"workload": cfg.name, "steps": steps,
+           "ms_per_step": round(wall / steps * 1e3, 4),
+           "ms_per_step_hip_events": round(ev / steps * 1e3, 4),
+           "tokens_per_s": round(cfg.T * steps / wall, 1),
+           "config": config_dict(cfg, PREFILL_CONFIG, ac, 1),
+           "roofline": roof, "layer": layer}
+    if not no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cfg, L.inp, 5.0)
+    del L
+    torch.cuda.empty_cache()
+    return out
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     if args.calibrate_copy:
@@ -143,79 +303,21 @@ def main():
     cfg = moe_synth.CONFIGS[args.config]
     seed = args.seed if args.seed is not None else args.config
     torch.cuda.set_device(0)
-    inp = moe_synth.make_layer_inputs(cfg, seed)
-
-    def dev(a):
-        if a is None:
-            return None
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(a).cuda()
-
-    d = {k: dev(v) for k, v in inp.items()}
-    rot = max(1, args.rotate)
-    w_gu = [d["W_gate_up"]] + [d["W_gate_up"].clone() for _ in range(rot - 1)]
-    w_dn = [d["W_down"]] + [d["W_down"].clone() for _ in range(rot - 1)]
-    dt = moe.MOE_DT_BF16 if cfg.dtype == "bf16" else moe.MOE_DT_F32
-    s = moe.shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.S, dt)
-    ws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
-    y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16 if dt else torch.float32,
-                    device="cuda")
-    views = moe.workspace_views(s, ws)
-
-    def step(i=0):
-        moe.moe_layer_forward(s, d["x"], d["W_router"], d["bias"], w_gu[i % rot],
-                              w_dn[i % rot], y, ws)
+    L = Layer(torch, moe, cfg, seed, args.rotate)
 
     for i in range(args.warmup):
-        step(i)
+        L.step(i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    ms_per_step = el / args.steps * 1e3
-    tok_s = cfg.T * args.steps / el
-
-    counts = views["counts"].cpu().numpy()
-    ac = alg_counts(cfg, counts)
-
     # per-step kernel times (each entry point timed alone on the same buffers)
-    n = max(20, args.steps)
-    kt = {
-        "route": time_calls(torch, lambda: moe.moe_route(
-            s, d["x"], d["W_router"], d["bias"], views["topk_idx"], views["topk_w"]), n),
-        "permute": time_calls(torch, lambda: moe.moe_permute(
-            s, views["topk_idx"], views["counts"], views["offsets"], views["sorted_slot"],
-            views["slot_pos"]), n),
-        "gate_up": time_calls(torch, lambda: moe.moe_grouped_gemm_gate_up(
-            s, d["x"], views["sorted_slot"], views["offsets"], d["W_gate_up"],
-            views["act"]), n),
-        "down": time_calls(torch, lambda: moe.moe_grouped_gemm_down(
-            s, views["act"], views["offsets"], d["W_down"], views["expert_out"]), n),
-        "combine": time_calls(torch, lambda: moe.moe_combine(
-            s, views["expert_out"], views["slot_pos"], views["topk_w"], y), n),
-    }
-    torch.cuda.synchronize()
+    kt = L.kernel_times(torch, max(20, min(args.steps, 200)))
+    wall, ev = L.timed_steps(torch, args.steps)
+    ms_per_step = wall / args.steps * 1e3
+    tok_s = cfg.T * args.steps / wall
+    ac, roof, layer = L.summary(torch, kt, wall / args.steps)
+    layer["ms_per_step_hip_events"] = round(ev / args.steps * 1e3, 4)
+    layer["hbm_frac_hip_events"] = round(ac["layer_bytes"] / (ev / args.steps) / 1e9
+                                         / HBM_PEAK_GBS, 4)
 
-    decode = cfg.T <= 64 and dt == moe.MOE_DT_BF16
-    if decode or dt == moe.MOE_DT_F32:
-        bound, unit = "hbm", "GB/s"
-        achieved = ac["gate_up_bytes"] / kt["gate_up"] / 1e9
-        peak = HBM_PEAK_GBS
-    else:
-        bound, unit = "mfma", "TFLOP/s"
-        achieved = ac["gate_up_flops"] / kt["gate_up"] / 1e12
-        peak = BF16_PEAK_TFLOPS
-    roof = dict(bound=bound, kernel="grouped_gemm_gate_up", achieved=round(achieved, 2),
-                peak=peak, unit=unit, frac=round(achieved / peak, 4),
-                traffic=load_traffic(cfg.name),
-                alg_bytes_per_launch=ac["gate_up_bytes"],
-                alg_flops_per_launch=ac["gate_up_flops"],
-                avg_launch_us=round(kt["gate_up"] * 1e6, 2))
-
-    layer_s = ms_per_step * 1e-3
     out = {
         "metric": "MoE layer tokens/s",
         "value": round(tok_s, 1),
@@ -229,20 +331,17 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights)",
-        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
-                   "k": cfg.k, "shared": cfg.S, "zipf_s": cfg.zipf_s, "seed": seed,
-                   "active_experts": ac["active"], "weight_copies": rot,
-                  "parallelism": "single GPU"},
+        "config": config_dict(cfg, seed, ac, L.rot),
         "roofline": roof,
-        "layer": {"alg_bytes": ac["layer_bytes"], "alg_flops": ac["layer_flops"],
-                  "hbm_frac": round(ac["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
-                  "mfma_frac": round(ac["layer_flops"] / layer_s / 1e12 /
-                                     (BF16_PEAK_TFLOPS if dt else FP32_PEAK_TFLOPS), 4),
-                  "kernel_us": {k: round(v * 1e6, 2) for k, v in kt.items()}},
+        "layer": layer,
         "cpu_baseline": None,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(cfg, L.inp, args.cpu_seconds)
+    if not args.no_prefill and args.config != PREFILL_CONFIG:
+        del L
+        torch.cuda.empty_cache()
+        out["prefill"] = prefill_extra(torch, moe, args.prefill_steps, args.no_cpu)
     print(json.dumps(out), flush=True)
 
 

@@ -373,4 +373,50 @@ def pin_sharding_identity(orc):
     assert rel_err(full, y) <= 1e-5
 
 
+def pin_forced_natural_selection(orc):
+    """Forcing the selection the oracle makes by itself changes nothing: the
+    same experts in the same slot order give bitwise the same y and weights."""
+    for (T, d, f, E, k, S, dt, seed) in ((9, 8, 6, 6, 2, 0, "f32", 30),
+                                         (7, 8, 8, 5, 3, 1, "bf16", 31)):
+        x, Wr, Wgu, Wd = rand_layer(seed, T, d, f, E, k, S, dt)
+        bias = np.linspace(0.2, -0.1, E).astype(np.float32)
+        y0, idx0, w0 = orc.layer_forward(x, Wr, Wgu, Wd, k, S=S, bias=bias)
+        y1, idx1, w1 = orc.layer_forward(x, Wr, Wgu, Wd, k, S=S, bias=bias,
+                                         forced_idx=idx0)
+        assert np.array_equal(idx1, idx0)
+        assert np.array_equal(w1, w0) and np.array_equal(y1, y0)
+
+
+def pin_forced_other_selection(orc):
+    """A forced k-set that is not the natural top-k: the output is the dense
+    per-expert outputs (numpy, independent of the oracle) masked to the
+    forced experts, with weights = softmax over the forced experts' logits
+    (Baidu page, section 四: softmax over the picked scores), slot j holding
+    the weight of forced expert j."""
+    for (T, d, f, E, k, S, dt, seed) in ((8, 8, 6, 6, 2, 0, "f32", 32),
+                                         (6, 8, 8, 7, 3, 1, "bf16", 33)):
+        x, Wr, Wgu, Wd = rand_layer(seed, T, d, f, E, k, S, dt)
+        bias = np.linspace(-0.3, 0.3, E).astype(np.float32)
+        _, idx_nat, _, L = np_dense_layer(x, Wr, Wgu, Wd, k, S=S, bias=bias)
+        # the k lowest-ranked experts, in ascending expert order: disjoint from
+        # the natural selection whenever 2k <= E
+        forced = np.stack([np.sort(np.lexsort((np.arange(E), L[t]))[:k])
+                           for t in range(T)]).astype(np.int32)
+        assert not np.any([set(forced[t]) & set(idx_nat[t]) for t in range(T)])
+        y, idx, w = orc.layer_forward(x, Wr, Wgu, Wd, k, S=S, bias=bias, forced_idx=forced)
+        assert np.array_equal(idx, forced)
+        xd, Wgud, Wdd = wide(x), wide(Wgu), wide(Wd)
+        outs = np.stack([(np_silu(xd @ Wgud[e, :f].T) * (xd @ Wgud[e, f:].T)) @ Wdd[e].T
+                         for e in range(E + S)])
+        y_ref = np.zeros((T, d))
+        for t in range(T):
+            ls = L[t, forced[t]]
+            ws = np.exp(ls - ls.max())
+            ws /= ws.sum()
+            assert np.max(np.abs(w[t] - ws)) <= 1e-14
+            y_ref[t] = sum(ws[j] * outs[forced[t, j], t] for j in range(k))
+            y_ref[t] += sum(outs[E + s, t] for s in range(S))
+        assert rel_err(y, y_ref) <= 1e-12, rel_err(y, y_ref)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -161,6 +161,12 @@ GEMM_CASES = [
     ("tiled_1024_groups", 128, 64, 32, 1000, 2, 24, "bf16", None),
     ("f32_tiny_shape", 128, 256, 512, 8, 2, 0, "f32", None),
     ("f32_ragged_shared", 90, 72, 40, 5, 2, 2, "f32", 1.0),
+    # many n-tiles: gate_up has ceil(1160/128) = 10 (bands of 4: 4, 4, 2), down
+    # ceil(1288/256) = 6 (4, 2), so the tile order runs over several bands
+    # and a partial last band; 128-row tiles (200 rows per group on average)
+    ("tiled_bands_bm128", 600, 1288, 1160, 6, 2, 0, "bf16", None),
+    # the same n-tiling on the 256-row tiles (600 rows per group on average)
+    ("tiled_bands_bm256", 1200, 1288, 1160, 2, 1, 0, "bf16", None),
 ]
 
 

@@ -58,7 +58,29 @@ MUTANTS = {
     "shared_rows_misplaced": (
         "int64_t row = T * k + sg * T + t;",
         "int64_t row = T * k + sg * T + (T - 1 - t);"),
+    # with a forced selection, the weights renormalised over the natural
+    # top-k instead of over the forced experts
+    "forced_renormalised_over_natural_topk": [
+        ("  if (forced) {\n    for (int64_t j = 0; j < k; ++j) idx[j] = forced[j];",
+         "  for (int64_t e = 0; e < E; ++e) {\n"
+         "    order[e].logit = logit[e];\n    order[e].e = (int32_t)e;\n  }\n"
+         "  qsort(order, (size_t)E, sizeof(ranked), by_logit_then_index);\n"
+         "  if (forced) {\n    for (int64_t j = 0; j < k; ++j) idx[j] = forced[j];"),
+        ("sel += exp(logit[idx[j]] - m) / z;", "sel += exp(logit[order[j].e] - m) / z;"),
+    ],
 }
+
+
+def _edits(name):
+    spec = MUTANTS[name]
+    return spec if isinstance(spec, list) else [spec]
+
+
+def _apply(src, name):
+    for old, new in _edits(name):
+        assert src.count(old) == 1, f"mutation {name} no longer matches oracle.c"
+        src = src.replace(old, new)
+    return src
 
 
 @pytest.fixture(scope="module")
@@ -68,19 +90,17 @@ def mutant_dir(tmp_path_factory):
 
 def test_mutations_apply_to_current_source():
     src = open(SRC).read()
-    for name, (old, new) in MUTANTS.items():
-        assert src.count(old) == 1, f"mutation {name} no longer matches oracle.c"
+    for name in MUTANTS:
+        _apply(src, name)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, mutant_dir):
-    old, new = MUTANTS[name]
-    src = open(SRC).read()
-    assert src.count(old) == 1
+    src = _apply(open(SRC).read(), name)
     d = mutant_dir / name
     d.mkdir()
     shutil.copy(os.path.join(os.path.dirname(SRC), "oracle.h"), d / "oracle.h")
-    (d / "oracle.c").write_text(src.replace(old, new))
+    (d / "oracle.c").write_text(src)
     lib = obuild.build(src=str(d / "oracle.c"), lib=str(d / "liboracle.so"))
     orc = oracle.Oracle(lib)
     failed = []
