@@ -62,6 +62,33 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, f32x4 c)
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// ------------------------------------------------ global -> LDS copies
+// Buffer resource word 3 for raw (untyped, stride 0) buffers on gfx9-family
+// parts: 32-bit data format; the range check is then "offset >= num_records".
+constexpr int kRsrcWord3 = 0x00020000;
+// A byte offset that fails the range check of every resource used here
+// (each spans at most 2^31 bytes; see the launcher).
+constexpr uint32_t kOOB = 0x80000000u;
+
+// Global -> LDS copy of 16 bytes per lane: lane l of the wave writes
+// lds + 16*l with bytes [voff, voff+16) of the resource (zeros if out of
+// range).  The LDS address goes through an integer that alias analysis
+// cannot follow, so the compiler does not try to match copies in flight to
+// the LDS reads that follow (it would wait for all of them); the ring's
+// readers are ordered after the copies they need by the explicit vmcnt wait
+// and barrier of every K tile.
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform
+  asm("" : "+s"(lds));                        // opaque; emits no instruction
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, (int)voff, 0, 0, 0);
+}
+
+// D = A * B + C on a 32x32x16 bf16 tile (fp32 accumulate).
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 // silu(z) * u in fp32.  silu(z) = z / (1 + e^-z).
 __device__ __forceinline__ float swiglu(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;

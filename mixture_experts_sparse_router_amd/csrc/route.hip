@@ -14,19 +14,22 @@
 // fp64 sum in a fixed order, so identical rows give identical logits and
 // exact ties are resolved by index, independent of scheduling.
 //
-// Three logit layouts, one top-k:
+// Three logit layouts, one selection:
 //   route_small (T <= 64, decode): one workgroup per token; thread (e, ks)
 //     sums the 16-byte chunks ks, ks+KS, ... of router row e against the
-//     token row straight from global memory (coalesced across the KS lanes of
-//     an expert), then the KS partials are combined by a fixed butterfly.
+//     token row straight from global memory (all of a thread's loads issued
+//     at once), then the KS partials are combined by a fixed butterfly.
 //   route_screen (bf16, large T): bf16 MFMA screen with a rigorous error
 //     bound, fp64 logits only for the experts that can still be selected.
 //   route_tiled (fp32, large T): one workgroup per TT tokens; x and W chunks
 //     are staged through LDS and thread (ks, e) keeps TT running logits, so
 //     each router row is read once per TT tokens.
-//   topk_wave: one wave per token; each lane holds ceil(E/64) logits and k
-//     rounds of a wave-wide argmax (butterfly over (value, index)) pick the
-//     experts.
+//   Selection (one wave per token): with at most 64 contenders, each lane
+//     holds one and counts the contenders ranked above it (its rank), so the
+//     k winners are known at once; with more, k rounds of a wave-wide argmax
+//     (butterfly over (value, index)) pick them.  Either way the k
+//     exponentials are then taken in parallel, one per lane, and summed in
+//     rank order.
 #include <atomic>
 
 #include "moe_common.h"
@@ -85,26 +88,83 @@ __device__ __forceinline__ bool better(double v, int e, double bv, int be) {
   return v > bv || (v == bv && e < be);
 }
 
-// Top-k of one token's logits (LDS row of E values) by one wave; writes the
-// k expert ids in rank order and their renormalised weights.  k <= 64.
-// Lane l owns experts l, l+64, ...; each round every lane rescans its
-// unpicked logits from LDS and a butterfly over (value, index) finds the
-// wave-wide best.
-__device__ void topk_wave(const double* logits, const float* __restrict__ bias, int E,
-                          int k, int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+// The value an expert is ranked by: its fp64 logit plus the bias (if any);
+// NaN ranks last.
+__device__ __forceinline__ double rank_value(double logit, const float* __restrict__ bias,
+                                             int e) {
+  const double v = bias ? logit + (double)bias[e] : logit;
+  return v != v ? -INFINITY : v;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// LDS of one wave's selection: the k winners in rank order.
+struct SelSlots {
+  int e[64];
+  double v[64];
+};
+
+// Lanes 0..k-1 hold the winners (value v, expert e) in rank order: write
+// the ids and the renormalised weights exp(v_j - v_0) / sum_{i<k} exp(v_i - v_0),
+// the sum taken in rank order.
+__device__ __forceinline__ void emit_topk(double v, int e, int k, int32_t* __restrict__ idx_out,
+                                          float* __restrict__ w_out) {
+  const int lane = threadIdx.x & 63;
+  const double vmax = readlane_f64(v, 0);
+  const double ex = lane < k ? exp(v - vmax) : 0.0;
+  double wsum = 0.0;
+  for (int j = 0; j < k; ++j) wsum += readlane_f64(ex, j);
+  if (lane < k) {
+    idx_out[lane] = e;
+    w_out[lane] = (float)(ex / wsum);
+  }
+}
+
+// Top-k of n <= 64 contenders held one per lane (lane i < n: value v, expert
+// e; values are final ranking values).  Each lane's rank is the number of
+// contenders ranked above it; ranks form a permutation of 0..n-1.
+__device__ void topk_lanes(double v, int e, int n, int k, int32_t* __restrict__ idx_out,
+                           float* __restrict__ w_out, SelSlots* sl) {
+  const int lane = threadIdx.x & 63;
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const double vj = readlane_f64(v, j);
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    rank += better(vj, ej, v, e) ? 1 : 0;
+  }
+  if (lane < n && rank < k) {
+    sl->e[rank] = e;
+    sl->v[rank] = v;
+  }
+  // LDS operations of one wave complete in order: the reads below see the
+  // writes above once they are issued
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const double vs = lane < k ? sl->v[lane] : 0.0;
+  const int es = lane < k ? sl->e[lane] : 0;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  emit_topk(vs, es, k, idx_out, w_out);
+}
+
+// Top-k of the E final ranking values in LDS row `row` by one wave: k rounds
+// of a wave-wide argmax over (value, index) (lane l owns experts l, l+64, ...;
+// k <= 64, E <= 1024); lane j keeps the round-j winner.
+__device__ void topk_rounds(const double* row, int E, int k, int32_t* __restrict__ idx_out,
+                            float* __restrict__ w_out) {
   const int lane = threadIdx.x & 63;
   uint32_t taken = 0;
-  double sel_v0 = 0.0, wsum = 0.0;
-  double my_ex = 0.0;  // lane j keeps exp(l_j - l_0)
+  double my_v = 0.0;
   int my_e = 0;
   for (int j = 0; j < k; ++j) {
     double bv = -INFINITY;
     int be = 0x7fffffff;
     for (int m = 0, e = lane; e < E; ++m, e += 64) {
       if ((taken >> m) & 1u) continue;
-      double v = logits[e];
-      if (bias) v += (double)bias[e];
-      if (v != v) v = -INFINITY;  // NaN ranks last
+      const double v = row[e];
       if (better(v, e, bv, be)) {
         bv = v;
         be = e;
@@ -121,23 +181,27 @@ __device__ void topk_wave(const double* logits, const float* __restrict__ bias, 
     }
     // every lane now holds the winner (bv, be)
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (j == 0) sel_v0 = bv;
-    const double ex = exp(bv - sel_v0);
-    wsum += ex;
     if (lane == j) {
-      my_ex = ex;
+      my_v = bv;
       my_e = be;
     }
   }
-  if (lane < k) {
-    idx_out[lane] = my_e;
-    w_out[lane] = (float)(my_ex / wsum);
+  emit_topk(my_v, my_e, k, idx_out, w_out);
+}
+
+// Top-k of an LDS row of E final ranking values.
+__device__ void topk_row(const double* row, int E, int k, int32_t* __restrict__ idx_out,
+                         float* __restrict__ w_out, SelSlots* sl) {
+  const int lane = threadIdx.x & 63;
+  if (E <= 64) {
+    topk_lanes(lane < E ? row[lane] : -INFINITY, lane, E, k, idx_out, w_out, sl);
+  } else {
+    topk_rounds(row, E, k, idx_out, w_out);
   }
 }
 
 // ------------------------------------------------------------ route_small
 constexpr int kSmallThreads = 1024;
-
 
 template <typename In>
 __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
@@ -145,21 +209,23 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int64_t d, int E, int k,
     int KS) {
   __shared__ double logits[kMaxE];
+  __shared__ SelSlots sl;
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.x;
   const int per_pass = kSmallThreads / KS;
   const int ks = tid % KS;
   const int64_t nchunk = d / 8;
   const In* xr = x + t * d;
-  // 8-element chunks of x and W in flight per thread (128 bytes of each)
-  constexpr int kSmallBatch = sizeof(In) == 2 ? 8 : 4;
+  // 8-element chunks of x and W loaded together per thread (one round of
+  // loads covers rows of up to kSmallBatch*KS chunks)
+  constexpr int kSmallBatch = sizeof(In) == 2 ? 12 : 6;
   for (int e0 = 0; e0 < E; e0 += per_pass) {
     const int e = e0 + tid / KS;
     double acc = 0.0;
     if (e < E) {
       const In* wr = Wr + (int64_t)e * d;
-      // chunks ks, ks+KS, ... in order, kSmallBatch of them loaded at once
-      // (chunks past the row read chunk 0 and are not used)
+      // chunks ks, ks+KS, ... in order (chunks past the row read chunk 0
+      // and are not used)
       for (int64_t c = ks; c < nchunk; c += kSmallBatch * KS) {
         Raw8<In> xv[kSmallBatch], wv[kSmallBatch];
 #pragma unroll
@@ -181,10 +247,10 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
     }
     // combine the KS partials of expert e (adjacent lanes) in a fixed order
     for (int off = 1; off < KS; off <<= 1) acc += __shfl_xor(acc, off, 64);
-    if (ks == 0 && e < E) logits[e] = acc;
+    if (ks == 0 && e < E) logits[e] = rank_value(acc, bias, e);
   }
   __syncthreads();
-  if (tid < 64) topk_wave(logits, bias, E, k, topk_idx + t * k, topk_w + t * k);
+  if (tid < 64) topk_row(logits, E, k, topk_idx + t * k, topk_w + t * k, &sl);
 }
 
 // ------------------------------------------------------------ route_tiled
@@ -195,6 +261,7 @@ struct TiledSmem {
   float w[kKC][kMaxP];           // staged router weights, transposed (32 KB)
   double xs[TT][kKC];            // staged token chunk (fp64)
   double part[kThreads][TT];     // k-split partial sums (32 KB at TT=16)
+  SelSlots sl[kThreads / 64];
 };
 
 template <typename In, int TT>
@@ -264,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void route_tiled_kernel(
       for (int t = 0; t < TT; ++t) {
         double s = 0.0;
         for (int q = 0; q < KS; ++q) s += sm.part[q * P + e_loc][t];
-        sm.logits[t][e0 + e_loc] = s;
+        sm.logits[t][e0 + e_loc] = rank_value(s, bias, e0 + e_loc);
       }
     }
     __syncthreads();
@@ -273,329 +340,737 @@ __global__ __launch_bounds__(kThreads) void route_tiled_kernel(
   const int wave = tid >> 6;
   for (int t = wave; t < TT; t += kThreads / 64) {
     if (t0 + t >= T) break;
-    topk_wave(sm.logits[t], bias, E, k, topk_idx + (t0 + t) * k, topk_w + (t0 + t) * k);
+    topk_row(sm.logits[t], E, k, topk_idx + (t0 + t) * k, topk_w + (t0 + t) * k,
+             &sm.sl[wave]);
   }
 }
 
 // ----------------------------------------------------------- route_screen
 // bf16, large T.  Exact fp64 logits of every (token, expert) pair cost
 // 2*T*E*d fp64 flops; instead the experts are screened with bf16 MFMA and
-// only the few that can still be in a token's top-k get an fp64 logit:
-//   1. MFMA screen: L~[t,e] = sum over K chunks of 32 of the chunk's MFMA
-//      result (fp32, started from zero), the chunk sums added in fp64.
-//      Every bf16 product is exact in fp32, so the only error is the
-//      rounding inside each 32-term chunk sum: |L~ - L| <= b[t,e] with
-//      b = kScreenRel * ||x_t|| * ||w_e||  (Cauchy-Schwarz bounds the sum of
-//      |products|; kScreenRel = 2^-17 covers 32 roundings of 2^-23 each with
-//      a factor of two to spare, plus the fp32 norms' own rounding).
+// only the few that can still be in a token's top-k get an fp64 logit.
+// One workgroup = 16 tokens x all experts, 8 waves.
+//   1. MFMA screen.  K runs in steps of 64; a step's 16 token rows and the
+//      pass's expert rows are copied to LDS (128 bytes per row, eight lanes
+//      per row, so every group of four lanes reads one contiguous piece of
+//      a line: reading sixteen rows per instruction in the MFMA's own lane
+//      order is three times slower out of L2), and each wave reads its
+//      operand fragments back from LDS: lane (j, kb) takes 16 consecutive
+//      elements [16kb, +16) of row j and feeds their two halves to two
+//      16x16x32 MFMAs (the sum over K does not depend on how K is split
+//      between them).  The MFMA accumulates in fp32 over groups of 4 steps
+//      (256 K elements); each group's sum is added to an fp64 total.  Every
+//      bf16 product is exact in fp32, so the only error is the rounding
+//      inside each group: at most 255 roundings of at most 2^-23 relative to
+//      the running sum, bounded by 2^-15 * sum_i |x_i w_i| <= 2^-15 *
+//      ||x_t|| * ||w_e|| (Cauchy-Schwarz).  The squared norms come from the
+//      same fragments, as the diagonals of the Gram products W_blk W_blk^T
+//      and X X^T (two more MFMAs each), accumulated the same way (relative
+//      error <= 2^-15).  Screen logit L~ (+ bias), bound
+//      b = 2^-14 * fac * ||x|| * ||w|| + 1e-30 (fac covers the norms' errors
+//      and their rounding to fp32).
 //   2. With lo = L~ - b, hi = L~ + b and tau = the k-th largest lo, an
 //      expert whose hi < tau is below k others for certain; the rest are
 //      the candidates (k of them, rarely a few more).
-//   3. Candidates get their fp64 logit (same fixed summation order for every
-//      expert, so identical rows still tie exactly); the top-k and weights
-//      are taken over these exact logits by topk_wave.
+//   3. Candidates get their exact fp64 logit (same fixed summation order for
+//      every expert, so identical rows still tie exactly), in batches of up
+//      to 8 with the token row's chunks loaded once per batch.
+//   4. Top-k over the candidates' exact logits.
 // The result is the same selection and weights as the fp64-everywhere path.
-constexpr int kScreenTT = 16;                  // token rows of the screen (LDS rows)
-constexpr double kScreenRel = 7.62939453125e-06;  // 2^-17
-constexpr int kCandBatch = 4;                  // candidates per fp64 pass
+// Precondition: finite inputs whose nonzero magnitudes lie in [2^-60, 2^60]
+// (squares, products and partial sums stay normal and finite in fp32).
+//
+// Two kernels share this scheme: route_staged (E <= 256, operands staged
+// through an LDS ring by direct global -> LDS copies) and route_direct (more
+// experts: operands loaded straight into registers, 16 rows per load).
+constexpr int kScreenTT = 16;                     // tokens per workgroup (MFMA rows)
+constexpr int kScreenWaves = 8;
+constexpr int kScreenThreads = 64 * kScreenWaves;
+constexpr int kGroupSteps = 4;                    // 64-wide K steps per fp32 group
+constexpr double kScreenRel = 6.103515625e-05;   // 2^-14
+constexpr double kScreenFac = 1.0001220703125;   // 1 + 2^-13
+constexpr int kExactPre = 3;                      // exact-phase chunk rounds in flight
+constexpr int kStagedMaxE = 256;
 
-// LDS layout of route_screen (bytes), sized by E at launch:
-//   lg    [16][E] double   screen logits, then exact logits / -inf
-//   wsq   [E]     float    ||w_e||^2
-//   xsq   [16]    float    ||x_t||^2
-//   union { part [16 items][16][16] double (screen K-split partials, E < 256),
-//           cand [4 waves][E] int      (candidate lists) }
-struct ScreenLds {
-  int64_t lg, wsq, xsq, un, total;
+// One staged K step: 16 token rows (ring X) and 128*NBW expert rows (ring
+// W), 128 bytes each.
+template <int NBW>
+struct Staged {
+  static constexpr int kWRows = 128 * NBW;
+  static constexpr int kXStage = 16 * 128;
+  static constexpr int kWStage = kWRows * 128;
+  static constexpr int kStages = NBW == 1 ? 4 : 3;
+  static constexpr int kCopies = 2 + kWRows / 8;                     // 1 KB copies per step
+  static constexpr int kCpw = (kCopies + kScreenWaves - 1) / kScreenWaves;  // per wave
+  static constexpr int kXBytes = kStages * kXStage;
+  static constexpr int kWBytes = kStages * kWStage + 1024;           // + 1 KB for pad copies
+  static constexpr int kRingBytes = kXBytes + kWBytes;
+  static_assert((kStages - 1) * kCpw < 64, "vmcnt range");
 };
-__host__ __device__ inline ScreenLds screen_lds(int E) {
-  ScreenLds o;
+
+// LDS layout of the screen kernels (bytes), sized by E at launch:
+//   lg    [16][E] double    screen logits (+ bias), later exact logits / -inf
+//   wn    [E]     float     ||w_e|| (rounded up)
+//   xn    [16]    float     ||x_t|| (rounded up)
+//   xp    [8][16] double    per-item partial ||x_t||^2 (K-split passes)
+//   sl    [8]     SelSlots  per-wave selection slots
+//   un: union { ring (staged kernel's copies of K steps),
+//               part [8 items][16][16] double + wp [8 items][16] double
+//               (K-split partials, passes of fewer than 8 blocks),
+//               cand [8 waves][E] uint16 (candidate lists) }
+struct ScreenLds {
+  int64_t lg, wn, xn, xp, sl, un, total;
+};
+// split_parts: whether a pass can have fewer than 8 blocks (K-split partials
+// then share the union).
+__host__ __device__ constexpr ScreenLds screen_lds(int E, bool split_parts) {
+  ScreenLds o{};
   o.lg = 0;
-  o.wsq = o.lg + (int64_t)kScreenTT * E * 8;
-  o.xsq = o.wsq + ((int64_t)E * 4 + 15) / 16 * 16;
-  o.un = o.xsq + kScreenTT * 4;
-  const int64_t part = E < 256 ? 16 * 16 * 16 * 8 : 0;
-  const int64_t cand = (int64_t)(kThreads / 64) * E * 4;
+  o.wn = o.lg + (int64_t)kScreenTT * E * 8;
+  o.xn = o.wn + ((int64_t)E * 4 + 15) / 16 * 16;
+  o.xp = o.xn + kScreenTT * 4;
+  o.sl = o.xp + 8 * 16 * 8;
+  o.un = o.sl + (int64_t)kScreenWaves * sizeof(SelSlots);
+  const int64_t part = split_parts ? 8 * 16 * 16 * 8 + 8 * 16 * 8 : 0;
+  const int64_t cand = ((int64_t)kScreenWaves * E * 2 + 15) / 16 * 16;
   o.total = o.un + (part > cand ? part : cand);
   return o;
 }
+static_assert(screen_lds(kMaxE, true).total <= 160 * 1024, "direct screen LDS fits one CU");
+static_assert(screen_lds(kStagedMaxE, false).total + Staged<2>::kRingBytes <= 160 * 1024,
+              "staged screen LDS fits one CU");
+static_assert(screen_lds(128, true).total + Staged<1>::kRingBytes <= 160 * 1024,
+              "staged screen LDS fits one CU");
 
-__global__ __launch_bounds__(kThreads, 2) void route_screen_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int64_t T, int64_t d, int E,
-    int k, int tok) {
-  // tok (8 or 16): tokens per workgroup; screen rows past them repeat the last
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const ScreenLds L = screen_lds(E);
-  double* lg = reinterpret_cast<double*>(smem + L.lg);  // [16][E]
-  float* wsq_s = reinterpret_cast<float*>(smem + L.wsq);
-  float* xsq_s = reinterpret_cast<float*>(smem + L.xsq);
-  double* part = reinterpret_cast<double*>(smem + L.un);  // [16][16][16]
-  int* cand = reinterpret_cast<int*>(smem + L.un);        // [4][E]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int j = lane & 15, kb = lane >> 4;
-  const int64_t t0 = (int64_t)blockIdx.x * tok;
-  const int jt = j < tok ? j : tok - 1;
-  const int64_t tj = t0 + jt < T ? t0 + jt : T - 1;  // padding tokens repeat the last
-  const bf16_t* xa = x + tj * d;
-  const int64_t nch = (d + 31) / 32;               // K chunks of 32
+// fp32 value -> unsigned key with the same order (no NaN)
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key >> 31) ? (key & 0x7fffffffu) : ~key);
+}
 
-  // ---- 1. MFMA screen.  A pass covers up to 16 blocks of 16 experts; with
-  // fewer blocks (small E) K is split KS ways too.  The pass's
-  // (block, K-split) items are dealt 4 per wave; item i = q*4 + wave.
-  for (int e0 = 0; e0 < E; e0 += 256) {
-    const int nbp = min(16, (E - e0 + 15) / 16);
-    int KS = 1;  // K splits only in the single pass of E < 256 (LDS holds part then)
-    if (E < 256)
-      while (nbp * KS * 2 <= 16) KS *= 2;
-    const bf16_t* wb[4];
-    int ks_of[4];
-    bool live[4];
+// Element (r, r) of a 16x16 MFMA result, on the one lane that holds it:
+// lane (j, kb) holds rows 4kb .. 4kb+3 of column j.
+__device__ __forceinline__ bool holds_diag(int j, int kb) { return kb == (j >> 2); }
+
+// Accumulators of one wave's items in one pass: screen logits and the Gram
+// diagonals, fp32 within a group of steps and fp64 across groups.
+template <int NBW>
+struct ScreenAcc {
+  f32x4 acc[NBW], accw[NBW], accx;
+  double accD[NBW][4], wsqD[NBW][4], xsqD[4];
+  __device__ __forceinline__ void zero() {
+    accx = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int item = q * 4 + wave;
-      live[q] = item < nbp * KS;
-      const int nb = live[q] ? item % nbp : 0;
-      ks_of[q] = live[q] ? item / nbp : 0;
-      const int e = e0 + 16 * nb + j;
-      wb[q] = Wr + (int64_t)(e < E ? e : E - 1) * d;
+    for (int i = 0; i < 4; ++i) xsqD[i] = 0.0;
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+      acc[q] = accw[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) accD[q][i] = wsqD[q][i] = 0.0;
     }
-    double acc[4][4];
-    float wsq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[q][i] = 0.0;
-    // loads of K step `it` (clamped past K, zeroed at use), two register sets
-    // alternating so one step's loads are in flight while the other computes
-    auto ld = [&](int64_t it, u32x4 (&a)[4], u32x4 (&b)[4], bool (&ok)[4]) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t kk = (it * KS + ks_of[q]) * 32 + 8 * kb;
-        ok[q] = live[q] && kk < d;
-        const int64_t ka = ok[q] ? kk : 0;
-        a[q] = ldg16(xa + ka);
-        b[q] = ldg16(wb[q] + ka);
-      }
-    };
-    auto mm = [&](const u32x4 (&a)[4], const u32x4 (&b)[4], const bool (&ok)[4]) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4 aa = zero_unless(ok[q], a[q]);
-        const u32x4 bb = zero_unless(ok[q], b[q]);
-        const uint32_t bw[4] = {bb.x, bb.y, bb.z, bb.w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          wsq[q] = fmaf(bf16lo(bw[h]), bf16lo(bw[h]), wsq[q]);
-          wsq[q] = fmaf(bf16hi(bw[h]), bf16hi(bw[h]), wsq[q]);
-        }
-        const f32x4 r = mfma16(aa, bb, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[q][i] += (double)r[i];
-      }
-    };
-    const int64_t nit = (nch + KS - 1) / KS;
-    u32x4 a0[4], b0[4], a1[4], b1[4];
-    bool o0[4], o1[4];
-    ld(0, a0, b0, o0);
-    int64_t it = 0;
-    for (; it + 2 <= nit; it += 2) {
-      ld(it + 1, a1, b1, o1);
-      mm(a0, b0, o0);
-      ld(it + 2, a0, b0, o0);
-      mm(a1, b1, o1);
-    }
-    if (it < nit) mm(a0, b0, o0);
-    // partial results: lane holds token 4*kb + i, expert 16*nb + j
-    if (KS == 1) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = e0 + 16 * (q * 4 + wave) + j;
-        if (live[q] && e < E) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) lg[(4 * kb + i) * E + e] = acc[q][i];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (live[q]) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) part[((q * 4 + wave) * 16 + 4 * kb + i) * 16 + j] = acc[q][i];
-        }
-      }
-    }
-    // ||w||^2 of each K-split, summed over the 4 lanes of a column
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float sq = wsq[q] + __shfl_xor(wsq[q], 16, 64);
-      sq += __shfl_xor(sq, 32, 64);
-      wsq[q] = sq;
-    }
-    __syncthreads();
-    if (KS > 1) {
-      // add the K-split partials in split order; items nb + nbp*ks
-      for (int o = tid; o < nbp * 256; o += kThreads) {
-        const int nb = o / 256, r = (o / 16) % 16, c = o % 16;
-        const int e = e0 + 16 * nb + c;
-        double sacc = 0.0;
-        for (int ks = 0; ks < KS; ++ks) sacc += part[((nb + nbp * ks) * 16 + r) * 16 + c];
-        if (e < E) lg[r * E + e] = sacc;
-      }
-    }
-    // ||w_e||^2: the split partials, again in split order (through LDS)
-    __syncthreads();
-    float* wpart = reinterpret_cast<float*>(part);  // [16 items][16]
-    if (kb == 0) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (live[q]) wpart[(q * 4 + wave) * 16 + j] = wsq[q];
-    }
-    __syncthreads();
-    if (tid < nbp * 16) {
-      const int nb = tid / 16, c = tid % 16;
-      float sq = 0.f;
-      for (int ks = 0; ks < KS; ++ks) sq += wpart[(nb + nbp * ks) * 16 + c];
-      if (e0 + tid < E) wsq_s[e0 + tid] = sq;
-    }
-    __syncthreads();
   }
-  // ||x_t||^2 (wave 0: lane (j, kb) sums 16-byte chunks kb, kb+4, ... of
-  // token j, eight loads in flight, then across kb)
-  if (wave == 0) {
-    float xsq = 0.f;
-    const int64_t n8 = d / 8;
-    for (int64_t c0 = kb; c0 < n8; c0 += 32) {
-      u32x4 v[8];
+  // one 64-wide step: token fragments a0, a1; block q's fragments b0[q], b1[q]
+  __device__ __forceinline__ void step(const u32x4& a0, const u32x4& a1, const u32x4* b0,
+                                       const u32x4* b1) {
+    accx = mfma16(a0, a0, accx);
+    accx = mfma16(a1, a1, accx);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t c = c0 + 4 * u;
-        v[u] = zero_unless(c < n8, ldg16(xa + (c < n8 ? c : 0) * 8));
+    for (int q = 0; q < NBW; ++q) {
+      acc[q] = mfma16(a0, b0[q], acc[q]);
+      acc[q] = mfma16(a1, b1[q], acc[q]);
+      accw[q] = mfma16(b0[q], b0[q], accw[q]);
+      accw[q] = mfma16(b1[q], b1[q], accw[q]);
+    }
+  }
+  __device__ __forceinline__ void flush() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xsqD[i] += (double)accx[i];
+    accx = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        accD[q][i] += (double)acc[q][i];
+        wsqD[q][i] += (double)accw[q][i];
       }
+      acc[q] = accw[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+};
+
+// Pointers into the screen kernels' LDS.
+struct ScreenSmem {
+  double* lg;
+  float* wn;
+  float* xn;
+  double* xp;
+  SelSlots* sls;
+  double* part;
+  double* wp;
+  uint16_t* cand;
+  unsigned char* ring;
+  __device__ ScreenSmem(unsigned char* smem, const ScreenLds& L, unsigned char* ring_ = nullptr) {
+    lg = reinterpret_cast<double*>(smem + L.lg);
+    wn = reinterpret_cast<float*>(smem + L.wn);
+    xn = reinterpret_cast<float*>(smem + L.xn);
+    xp = reinterpret_cast<double*>(smem + L.xp);
+    sls = reinterpret_cast<SelSlots*>(smem + L.sl);
+    part = reinterpret_cast<double*>(smem + L.un);
+    wp = reinterpret_cast<double*>(smem + L.un + 8 * 16 * 16 * 8);
+    cand = reinterpret_cast<uint16_t*>(smem + L.un);
+    ring = ring_;
+  }
+};
+
+// End of a screen pass: the items' screen logits (+ bias), ||w_e|| and (first
+// pass) ||x_t|| go to LDS; K-split items are added in split order.  Every
+// thread of the workgroup calls it; it ends with a barrier.
+template <int NBW>
+__device__ void screen_pass_store(const ScreenAcc<NBW>& A, const ScreenSmem& S,
+                                  const float* __restrict__ bias, int E, int e0, int nb, int KS,
+                                  const bool* live, const int* blk, bool xnorm) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, kb = lane >> 4;
+  const bool diag = holds_diag(j, kb);
+  // lane holds D[4kb + i][j] of each block: token 4kb+i, expert 16*blk+j;
+  // the Gram diagonals (squared norms) sit on the lanes with kb = j/4
+  const int dq = j & 3;
+  double wsq[NBW];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t aw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+  for (int q = 0; q < NBW; ++q)
+    wsq[q] = dq == 0 ? A.wsqD[q][0] : dq == 1 ? A.wsqD[q][1] : dq == 2 ? A.wsqD[q][2] : A.wsqD[q][3];
+  const double xsq = dq == 0 ? A.xsqD[0] : dq == 1 ? A.xsqD[1] : dq == 2 ? A.xsqD[2] : A.xsqD[3];
+  if (KS == 1) {
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          xsq = fmaf(bf16lo(aw[h]), bf16lo(aw[h]), xsq);
-          xsq = fmaf(bf16hi(aw[h]), bf16hi(aw[h]), xsq);
-        }
+    for (int q = 0; q < NBW; ++q) {
+      const int e = e0 + 16 * blk[q] + j;
+      if (live[q] && e < E) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S.lg[(4 * kb + i) * E + e] = rank_value(A.accD[q][i], bias, e);
+        if (diag) S.wn[e] = __double2float_ru(sqrt(wsq[q]));
       }
     }
-    xsq += __shfl_xor(xsq, 16, 64);
-    xsq += __shfl_xor(xsq, 32, 64);
-    if (kb == 0) xsq_s[j] = xsq;
+    if (xnorm && diag) S.xp[0 * 16 + j] = xsq;
+  }
+  __syncthreads();  // part / wp / xp (K split) are written next; lg readers wait
+  if (KS > 1) {
+    const int it = wave;  // one item per wave
+    if (live[0]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S.part[(it * 16 + 4 * kb + i) * 16 + j] = A.accD[0][i];
+      if (diag) {
+        S.wp[it * 16 + j] = wsq[0];
+        if (xnorm) S.xp[it * 16 + j] = xsq;
+      }
+    }
+    __syncthreads();
+    // add the K-split partials in split order; items blk + nb*ks
+    for (int o = tid; o < nb * 256; o += kScreenThreads) {
+      const int b = o / 256, rr = (o / 16) % 16, c = o % 16;
+      const int e = e0 + 16 * b + c;
+      double sacc = 0.0;
+      for (int q = 0; q < KS; ++q) sacc += S.part[((b + nb * q) * 16 + rr) * 16 + c];
+      if (e < E) S.lg[rr * E + e] = rank_value(sacc, bias, e);
+    }
+    if (tid < nb * 16) {
+      const int b = tid / 16, c = tid % 16;
+      double sq = 0.0;
+      for (int q = 0; q < KS; ++q) sq += S.wp[(b + nb * q) * 16 + c];
+      if (e0 + tid < E) S.wn[e0 + tid] = __double2float_ru(sqrt(sq));
+    }
+  }
+  if (e0 == 0 && tid < 16) {
+    // ||x_t||^2: items with block 0 cover every K step once (split order)
+    double sq = 0.0;
+    for (int q = 0; q < KS; ++q) sq += S.xp[(nb * q) * 16 + tid];
+    S.xn[tid] = __double2float_ru(sqrt(sq));
   }
   __syncthreads();
+}
 
-  // ---- 2./3. one wave per token
-  int* mycand = cand + wave * E;
-  for (int tl = wave; tl < tok; tl += kThreads / 64) {
+// Exact fp64 logits of candidates c0 .. c0+CB-1 of one token (CB <= 8): lane
+// l sums the 16-byte chunks l, l+64, ... of the row in order, a ring of
+// kExactPre chunk rounds of loads in flight; the CB sums are then reduced
+// over the 64 lanes in a fixed order (halving exchanges leave lane l with
+// candidate u = l*CB/64, then a butterfly over the 64/CB lanes sharing it;
+// pairs are always formed over lane bit 5, then 4, ..., then 0, so every
+// candidate's sum has the same rounding).  Lane u < CB returns the sum of
+// candidate c0 + u.
+template <int CB>
+__device__ __forceinline__ double exact_batch(const bf16_t* __restrict__ xt,
+                                              const bf16_t* __restrict__ Wr,
+                                              const uint16_t* cands, int c0, int ncand,
+                                              int64_t d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n8 = d / 8;
+  const int64_t nr = (n8 + 63) / 64;  // chunk rounds
+  double a[CB];
+  const bf16_t* wr[CB];
+#pragma unroll
+  for (int u = 0; u < CB; ++u) {
+    a[u] = 0.0;
+    const int ci = c0 + u < ncand ? c0 + u : ncand - 1;
+    wr[u] = Wr + (int64_t)cands[ci] * d;
+  }
+  struct ExRegs {
+    u32x4 xv, wv[CB];
+  };
+  ExRegs rr[kExactPre];
+  // rounds past the row read chunk 0 and add nothing
+  auto eld = [&](int64_t r, ExRegs& g) {
+    const int64_t ch = 64 * r + lane;
+    const int64_t o = ch < n8 ? ch * 8 : 0;
+    g.xv = ldg16(xt + o);
+#pragma unroll
+    for (int u = 0; u < CB; ++u) g.wv[u] = ldg16(wr[u] + o);
+  };
+  auto eacc = [&](int64_t r, const ExRegs& g) {
+    if (64 * r + lane >= n8) return;
+    const uint32_t xw[4] = {g.xv.x, g.xv.y, g.xv.z, g.xv.w};
+    double xd[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      xd[2 * h] = (double)bf16lo(xw[h]);
+      xd[2 * h + 1] = (double)bf16hi(xw[h]);
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const uint32_t w[4] = {g.wv[u].x, g.wv[u].y, g.wv[u].z, g.wv[u].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        a[u] = fma(xd[2 * h], (double)bf16lo(w[h]), a[u]);
+        a[u] = fma(xd[2 * h + 1], (double)bf16hi(w[h]), a[u]);
+      }
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < kExactPre; ++q) eld(q, rr[q]);
+  for (int64_t r0 = 0; r0 < nr; r0 += kExactPre) {
+#pragma unroll
+    for (int q = 0; q < kExactPre; ++q) {
+      eacc(r0 + q, rr[q]);
+      eld(r0 + q + kExactPre, rr[q]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // halving exchanges over lane bits 5, 4, 3 (as many as CB needs)
+  constexpr int LB = CB == 8 ? 3 : CB == 4 ? 2 : CB == 2 ? 1 : 0;
+  double v = a[0];
+  if constexpr (LB >= 1) {
+    double b[CB / 2];
+    const bool h = lane & 32;
+#pragma unroll
+    for (int i = 0; i < CB / 2; ++i) {
+      const double send = h ? a[i] : a[i + CB / 2];
+      const double keep = h ? a[i + CB / 2] : a[i];
+      b[i] = keep + __shfl_xor(send, 32, 64);
+    }
+    if constexpr (LB >= 2) {
+      double c[CB / 4];
+      const bool h2 = lane & 16;
+#pragma unroll
+      for (int i = 0; i < CB / 4; ++i) {
+        const double send = h2 ? b[i] : b[i + CB / 4];
+        const double keep = h2 ? b[i + CB / 4] : b[i];
+        c[i] = keep + __shfl_xor(send, 16, 64);
+      }
+      if constexpr (LB >= 3) {
+        const bool h3 = lane & 8;
+        const double send = h3 ? c[0] : c[1];
+        const double keep = h3 ? c[1] : c[0];
+        v = keep + __shfl_xor(send, 8, 64);
+      } else {
+        v = c[0];
+      }
+    } else {
+      v = b[0];
+    }
+  }
+  // butterfly over the lanes that share a candidate (bits below 6 - LB)
+#pragma unroll
+  for (int off = 32 >> LB; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  // candidate u's sum is on lanes u*64/CB ..; lane u < CB takes it
+  return __shfl(v, lane < CB ? lane * (64 / CB) : 0, 64);
+}
+
+// Steps 2-4 for the workgroup's tokens, one wave per token, once the screen
+// logits and norms are in LDS (and the ring is no longer in use).  M: experts
+// per lane, at least ceil(E / 64).
+template <int M>
+__device__ void screen_select(const ScreenSmem& S, const bf16_t* __restrict__ x,
+                              const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
+                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                              int64_t T, int64_t d, int E, int k, int64_t t0) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint16_t* mycand = S.cand + wave * E;
+  SelSlots* sl = S.sls + wave;
+  const double rel = kScreenRel * kScreenFac;
+  for (int tl = wave; tl < kScreenTT; tl += kScreenWaves) {
     const int64_t t = t0 + tl;
     if (t >= T) break;
-    double* row = lg + (int64_t)tl * E;
-    // fp32 norms carry relative error <= d * 2^-24; the factor 1.001 covers it
-    const double xn = sqrt((double)xsq_s[tl]) * 1.001;
-    auto bound = [&](int e) { return kScreenRel * xn * sqrt((double)wsq_s[e]) + 1e-30; };
-    // tau = k-th largest lower bound (ties broken by index, as everywhere)
-    uint32_t taken = 0;
-    double tau = 0.0;
-    for (int jj = 0; jj < k; ++jj) {
-      double bv = -INFINITY;
-      int be = 0x7fffffff;
-      for (int m = 0, e = lane; e < E; ++m, e += 64) {
-        if ((taken >> m) & 1u) continue;
-        double lo = row[e] + (bias ? (double)bias[e] : 0.0) - bound(e);
-        if (lo != lo) lo = -INFINITY;
-        if (better(lo, e, bv, be)) {
-          bv = lo;
-          be = e;
-        }
-      }
+    double* row = S.lg + (int64_t)tl * E;
+    const double xn = (double)S.xn[tl];
+    // tau: a value at most the k-th largest lower bound lo = L~ - b, so the
+    // test below keeps every expert that can be selected.  lo is rounded
+    // down to fp32 and mapped to an order-preserving 32-bit key; a radix
+    // selection over the top 16 bits of the keys (bit by bit from the top,
+    // keep the bit if at least k keys have top bits >= the prefix with it
+    // set) ends on exactly the top 16 bits of the k-th largest key (a larger
+    // prefix would put k keys above it), and tau is that prefix with the low
+    // bits cleared: within 2^-7 relative of the k-th largest lo.
+    uint32_t key[M];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const double ov = __shfl_xor(bv, off, 64);
-        const int oe = __shfl_xor(be, off, 64);
-        if (better(ov, oe, bv, be)) {
-          bv = ov;
-          be = oe;
-        }
+    for (int q = 0; q < M; ++q) {
+      const int e = lane + 64 * q;
+      key[q] = 0u;  // below every real key
+      if (e < E) {
+        double lo = row[e] - (rel * xn * (double)S.wn[e] + 1e-30);
+        if (lo != lo) lo = -INFINITY;
+        key[q] = order_key(__double2float_rd(lo)) >> 16;
       }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      tau = bv;
     }
-    // candidates: hi >= tau, compacted in expert order
+    uint32_t prefix = 0u;
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t c = prefix | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int q = 0; q < M; ++q) cnt += __popcll(__ballot(key[q] >= c));
+      if (cnt >= k) prefix = c;
+    }
+    const double tau = (double)key_value(prefix << 16);
+    // candidates: hi >= tau, listed in expert order
     int ncand = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
       const int e = e0 + lane;
       bool c = false;
-      if (e < E) {
-        const double hi = row[e] + (bias ? (double)bias[e] : 0.0) + bound(e);
-        c = !(hi < tau);
-      }
-      const uint64_t m = __ballot(c);
-      if (c) mycand[ncand + __popcll(m & ((1ull << lane) - 1ull))] = e;
-      ncand += __popcll(m);
+      if (e < E) c = !(row[e] + (rel * xn * (double)S.wn[e] + 1e-30) < tau);
+      const uint64_t mk = __ballot(c);
+      if (c) mycand[ncand + __popcll(mk & ((1ull << lane) - 1ull))] = (uint16_t)e;
+      ncand += __popcll(mk);
     }
-    // every non-candidate drops out of the top-k
-    for (int e = lane; e < E; e += 64) row[e] = -INFINITY;
-    // fp64 logits of the candidates: lane l sums 16-byte chunks l, l+64, ...
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (ncand > 64) {
+      // many candidates (degenerate inputs): exact logits go back into the
+      // row, every non-candidate drops out, and the row is ranked in rounds
+      for (int e = lane; e < E; e += 64) row[e] = -INFINITY;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    // exact fp64 logits of the candidates, in batches of 8, 4, 2 or 1
     const bf16_t* xt = x + t * d;
-    const int64_t n8 = d / 8;
-    for (int c0 = 0; c0 < ncand; c0 += kCandBatch) {
-      double acc[kCandBatch];
-      const bf16_t* wr[kCandBatch];
-#pragma unroll
-      for (int u = 0; u < kCandBatch; ++u) {
-        acc[u] = 0.0;
-        const int ci = c0 + u < ncand ? c0 + u : ncand - 1;
-        wr[u] = Wr + (int64_t)mycand[ci] * d;
-      }
-      for (int64_t ch = lane; ch < n8; ch += 128) {
-        // two chunks per iteration: ch and ch + 64 (if inside the row)
-        const bool two = ch + 64 < n8;
-        const int64_t ch2 = two ? ch + 64 : ch;
-        const u32x4 xv0 = ldg16(xt + ch * 8), xv1 = ldg16(xt + ch2 * 8);
-        u32x4 wv0[kCandBatch], wv1[kCandBatch];
-#pragma unroll
-        for (int u = 0; u < kCandBatch; ++u) {
-          wv0[u] = ldg16(wr[u] + ch * 8);
-          wv1[u] = ldg16(wr[u] + ch2 * 8);
+    double my_v = -INFINITY;
+    int my_e = 0;
+    for (int c0 = 0; c0 < ncand;) {
+      const int left = ncand - c0;
+      const int cb = left >= 8 ? 8 : left >= 4 ? 4 : left >= 2 ? 2 : 1;
+      double got;  // lane u < cb: candidate c0 + u
+      if (cb == 8) got = exact_batch<8>(xt, Wr, mycand, c0, ncand, d);
+      else if (cb == 4) got = exact_batch<4>(xt, Wr, mycand, c0, ncand, d);
+      else if (cb == 2) got = exact_batch<2>(xt, Wr, mycand, c0, ncand, d);
+      else got = exact_batch<1>(xt, Wr, mycand, c0, ncand, d);
+      if (ncand > 64) {
+        if (lane < cb) {
+          const int e = mycand[c0 + lane];
+          row[e] = rank_value(got, bias, e);
         }
-        const uint32_t x0[4] = {xv0.x, xv0.y, xv0.z, xv0.w};
-        const uint32_t x1[4] = {xv1.x, xv1.y, xv1.z, xv1.w};
-#pragma unroll
-        for (int u = 0; u < kCandBatch; ++u) {
-          const uint32_t w0[4] = {wv0[u].x, wv0[u].y, wv0[u].z, wv0[u].w};
-          const uint32_t w1[4] = {wv1[u].x, wv1[u].y, wv1[u].z, wv1[u].w};
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            acc[u] = fma((double)bf16lo(x0[h]), (double)bf16lo(w0[h]), acc[u]);
-            acc[u] = fma((double)bf16hi(x0[h]), (double)bf16hi(w0[h]), acc[u]);
-          }
-          if (two) {
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              acc[u] = fma((double)bf16lo(x1[h]), (double)bf16lo(w1[h]), acc[u]);
-              acc[u] = fma((double)bf16hi(x1[h]), (double)bf16hi(w1[h]), acc[u]);
-            }
-          }
+      } else {
+        // lane c of the list holds candidate c
+        const int want = lane - c0;
+        const double v = __shfl(got, want >= 0 && want < cb ? want : 0, 64);
+        if (want >= 0 && want < cb) {
+          my_e = mycand[lane];
+          my_v = rank_value(v, bias, my_e);
         }
       }
+      c0 += cb;
+    }
+    if (ncand <= 64) {
+      topk_lanes(my_v, my_e, ncand, k, topk_idx + t * k, topk_w + t * k, sl);
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      topk_rounds(row, E, k, topk_idx + t * k, topk_w + t * k);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
+// Items of a pass: item i = wave + 8q is block i % nb, K split i / nb.
+template <int NBW>
+struct PassItems {
+  int nb, KS, ks;
+  bool live[NBW];
+  int blk[NBW];
+  bool xnorm;
+  __device__ PassItems(int E, int e0, int wave) {
+    nb = min(8 * NBW, (E - e0 + 15) / 16);
+    KS = nb >= 8 ? 1 : 8 / nb;
+    const int nitem = nb * KS;
+    ks = 0;
 #pragma unroll
-      for (int u = 0; u < kCandBatch; ++u) {
+    for (int q = 0; q < NBW; ++q) {
+      const int it = wave + 8 * q;
+      live[q] = it < nitem;
+      blk[q] = live[q] ? it % nb : 0;
+      if (q == 0) ks = live[0] ? it / nb : 0;
+    }
+    // items of block 0 (together covering every step once) keep ||x||^2
+    xnorm = e0 == 0 && live[0] && blk[0] == 0;
+  }
+};
+
+// ------------------------------------------------------------ route_staged
+template <int NBW>
+__global__ __launch_bounds__(kScreenThreads, 1) void route_staged_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int64_t T, int64_t d, int E,
+    int k) {
+  using SG = Staged<NBW>;
+  // the rings are LDS objects of their own: with more than one LDS object
+  // the compiler tags every LDS access with the object it touches, and the
+  // fragment reads then need not wait for the copies in flight (which carry
+  // no tag, their address being opaque); the kernel's own vmcnt waits and
+  // barriers order each read after the copies it needs
+  __shared__ __attribute__((aligned(1024))) unsigned char ringX[SG::kXBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char ringW[SG::kWBytes];
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  // NBW == 2 runs one pass of more than 128 experts: never a K split
+  const ScreenLds L = screen_lds(E, NBW == 1);
+  const ScreenSmem S(smem, L);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, kb = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kScreenTT;
+  const uint32_t rowb = (uint32_t)(d * 2);          // bytes per row
+  const int64_t nsteps = (d + 63) / 64;
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)(uint32_t)(T * d * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Wr, 0, (int)(uint32_t)(E * d * 2), kRsrcWord3);
+  // the rings' LDS addresses as integers for the copies, kept apart from
+  // the pointer arithmetic of the fragment reads
+  uint32_t ringx_i = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ringX;
+  uint32_t ringw_i = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ringW;
+  asm("" : "+s"(ringx_i), "+s"(ringw_i));
+  const uint32_t pad_dst = ringw_i + SG::kStages * SG::kWStage;
+
+  for (int e0 = 0; e0 < E; e0 += 128 * NBW) {
+    const PassItems<NBW> P(E, e0, wave);
+    // copy plan: copy i = wave + 8c (c < kCpw) moves stage rows 8i .. 8i+7,
+    // lane l: row 8i + l/8, LDS chunk l%8, which holds the row's 16-byte
+    // chunk (l%8) ^ (row%8) (so that the fragment reads below, 16 rows at a
+    // time, hit 8 distinct chunk positions).  Rows < 16 are tokens (the
+    // padding rows past T repeat the last token), the rest experts e0 + ...
+    // (past E: out of range, zero).  Copies i >= kCopies are padding: they
+    // land in a spare 1 KB and move nothing.
+    uint32_t base[SG::kCpw], kch[SG::kCpw], dst[SG::kCpw];
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) acc[u] += __shfl_xor(acc[u], off, 64);
+    for (int c = 0; c < SG::kCpw; ++c) {
+      const int i = wave + 8 * c;
+      const int r = 8 * i + (lane >> 3);  // stage row: tokens, then experts
+      kch[c] = (uint32_t)(((lane & 7) ^ (r & 7)) * 16);
+      uint32_t b = kOOB;
+      if (i < SG::kCopies) {
+        if (r < 16) {
+          const int64_t t = t0 + r < T ? t0 + r : T - 1;
+          b = (uint32_t)t * rowb;
+        } else if (e0 + r - 16 < E) {
+          b = (uint32_t)(e0 + r - 16) * rowb;
+        }
       }
-      if (lane == 0) {
+      base[c] = b;
+      // byte offset of the copy's 8 rows inside its ring's stage
+      dst[c] = i < 2 ? (uint32_t)(8 * i) * 128 : (uint32_t)(8 * (i - 2)) * 128;
+    }
+    auto issue = [&](int stage, int64_t s) {
+      const uint32_t koff = (uint32_t)(s * 128);
 #pragma unroll
-        for (int u = 0; u < kCandBatch; ++u)
-          if (c0 + u < ncand) row[mycand[c0 + u]] = acc[u];
+      for (int c = 0; c < SG::kCpw; ++c) {
+        const int i = wave + 8 * c;
+        const uint32_t o = (base[c] != kOOB && koff + kch[c] < rowb) ? base[c] + koff + kch[c]
+                                                                     : kOOB;
+        if (i < 2)
+          copy16(rx, o, ringx_i + (uint32_t)stage * SG::kXStage + dst[c]);
+        else if (i < SG::kCopies)
+          copy16(rw, o, ringw_i + (uint32_t)stage * SG::kWStage + dst[c]);
+        else
+          copy16(rw, kOOB, pad_dst);
+      }
+    };
+    // fragment offsets inside a stage: row j (tokens) and 16*blk[q] + j
+    // (experts), chunks 2kb and 2kb+1, swizzled by j%8 (= row%8 of both)
+    const uint32_t f0 = (uint32_t)(((2 * kb) ^ (j & 7)) * 16);
+    const uint32_t f1 = (uint32_t)(((2 * kb + 1) ^ (j & 7)) * 16);
+    uint32_t fb[NBW];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) fb[q] = (uint32_t)(16 * P.blk[q] + j) * 128;
+
+    ScreenAcc<NBW> A;
+    A.zero();
+    // ring prologue: steps 0 .. kStages-1
+#pragma unroll
+    for (int q = 0; q < SG::kStages; ++q) issue(q, q);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((SG::kStages - 1) * SG::kCpw) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    int stage = 0;
+    int64_t mine = 0;  // steps this wave has accumulated in the current group
+    for (int64_t s = 0; s < nsteps; ++s) {
+      if (P.live[0] && (P.KS == 1 || s % P.KS == P.ks)) {
+        const unsigned char* sx = ringX + (uint32_t)stage * SG::kXStage;
+        const unsigned char* sw = ringW + (uint32_t)stage * SG::kWStage;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(sx + (uint32_t)j * 128 + f0);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(sx + (uint32_t)j * 128 + f1);
+        u32x4 b0[NBW], b1[NBW];
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) {
+          b0[q] = *reinterpret_cast<const u32x4*>(sw + fb[q] + f0);
+          b1[q] = *reinterpret_cast<const u32x4*>(sw + fb[q] + f1);
+        }
+        A.step(a0, a1, b0, b1);
+        if (++mine == kGroupSteps) {
+          A.flush();
+          mine = 0;
+        }
+      }
+      // step s+1 has landed (this wave's copies, then everyone's: a plain
+      // s_barrier), and every wave's reads of step s are complete (lgkmcnt(0)
+      // before the barrier), so step s's stage can be refilled
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((SG::kStages - 2) * SG::kCpw)
+                   : "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(stage, s + SG::kStages);
+      stage = stage + 1 == SG::kStages ? 0 : stage + 1;
+    }
+    A.flush();
+    // drain the copies still in flight before the ring's LDS is reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    screen_pass_store<NBW>(A, S, bias, E, e0, P.nb, P.KS, P.live, P.blk, P.xnorm);
+  }
+  // experts per lane of the selection: 1, 2, 4 or 16
+  if (E <= 64) screen_select<1>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
+  else if (E <= 128) screen_select<2>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
+  else if (E <= 256) screen_select<4>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
+  else screen_select<16>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
+}
+
+// ------------------------------------------------------------ route_direct
+// Loads of one 64-wide K step: chunks c0 = 8s + 2kb and c0+1 of the token
+// row (A) and of each block's expert row (B), straight into registers.
+template <int NBW>
+struct StepRegs {
+  u32x4 a0, a1, b0[NBW], b1[NBW];
+};
+
+template <int NBW>
+__global__ __launch_bounds__(kScreenThreads, 1) void route_direct_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int64_t T, int64_t d, int E,
+    int k) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const ScreenLds L = screen_lds(E, true);
+  const ScreenSmem S(smem, L);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, kb = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kScreenTT;
+  const int64_t tj = t0 + j < T ? t0 + j : T - 1;  // padding rows repeat the last token
+  const bf16_t* xa = x + tj * d;
+  const int64_t n8 = d / 8;          // 8-element chunks per row
+  const int64_t nfull = n8 / 8;      // K steps with all 64 elements inside the row
+  const int64_t nsteps = (n8 + 7) / 8;
+
+  for (int e0 = 0; e0 < E; e0 += 128 * NBW) {
+    const PassItems<NBW> P(E, e0, wave);
+    const bf16_t* wb[NBW];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+      const int e = e0 + 16 * P.blk[q] + j;
+      wb[q] = Wr + (int64_t)(e < E ? e : E - 1) * d;
+    }
+    // a wave with fewer live blocks runs the missing ones on its first
+    // block's rows (the same lines, served by L1) and drops the result: no
+    // load depends on a branch, so the wait counters keep the ring in flight
+#pragma unroll
+    for (int q = 1; q < NBW; ++q)
+      if (!P.live[q]) wb[q] = wb[0];
+    const int ks = P.ks, KS = P.KS;
+    ScreenAcc<NBW> A;
+    A.zero();
+    // step s is loaded from chunk 0 where it runs past the row; only the
+    // last step can, and its chunks past the row are zeroed before use
+    auto ld = [&](int64_t s, StepRegs<NBW>& r) {
+      const int64_t c0 = 8 * s + 2 * kb;
+      const int64_t o0 = c0 < n8 ? c0 * 8 : 0, o1 = c0 + 1 < n8 ? (c0 + 1) * 8 : 0;
+      r.a0 = ldg16(xa + o0);
+      r.a1 = ldg16(xa + o1);
+#pragma unroll
+      for (int q = 0; q < NBW; ++q) {
+        r.b0[q] = ldg16(wb[q] + o0);
+        r.b1[q] = ldg16(wb[q] + o1);
+      }
+    };
+    auto mm = [&](int64_t s, StepRegs<NBW>& r, bool ragged) {
+      if (ragged) {
+        const int64_t c0 = 8 * s + 2 * kb;
+        const bool ok0 = c0 < n8, ok1 = c0 + 1 < n8;
+        r.a0 = zero_unless(ok0, r.a0);
+        r.a1 = zero_unless(ok1, r.a1);
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) {
+          r.b0[q] = zero_unless(ok0, r.b0[q]);
+          r.b1[q] = zero_unless(ok1, r.b1[q]);
+        }
+      }
+      A.step(r.a0, r.a1, r.b0, r.b1);
+    };
+    if (P.live[0]) {
+      // this wave's steps ks, ks + KS, ...: a ring of kGroupSteps register
+      // sets keeps that many steps' loads in flight; each pass of the ring
+      // is one fp32 accumulation group.  Groups whose steps all lie inside
+      // the row run without masking; the rest (at most one group and a
+      // partial one, padded with steps past the row) run masked after them.
+      // The ring's loads past the last group read chunk 0 and are not used.
+      const int64_t nmine = nsteps > ks ? (nsteps - ks + KS - 1) / KS : 0;
+      const int64_t ngroups = (nmine + kGroupSteps - 1) / kGroupSteps;
+      const int64_t nmine_full = nfull > ks ? (nfull - ks + KS - 1) / KS : 0;
+      const int64_t gfull = nmine_full / kGroupSteps;
+      StepRegs<NBW> rs[kGroupSteps];
+#pragma unroll
+      for (int q = 0; q < kGroupSteps; ++q) ld(ks + q * KS, rs[q]);
+      for (int64_t g = 0; g < gfull; ++g) {
+#pragma unroll
+        for (int q = 0; q < kGroupSteps; ++q) {
+          const int64_t st = ks + (g * kGroupSteps + q) * KS;
+          mm(st, rs[q], false);
+          ld(st + kGroupSteps * KS, rs[q]);
+          // keep each refill right after the step that frees its registers
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        A.flush();
+      }
+      for (int64_t g = gfull; g < ngroups; ++g) {
+#pragma unroll
+        for (int q = 0; q < kGroupSteps; ++q) {
+          const int64_t st = ks + (g * kGroupSteps + q) * KS;
+          mm(st, rs[q], true);
+          ld(st + kGroupSteps * KS, rs[q]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        A.flush();
       }
     }
-    topk_wave(row, bias, E, k, topk_idx + t * k, topk_w + t * k);
+    screen_pass_store<NBW>(A, S, bias, E, e0, P.nb, P.KS, P.live, P.blk, P.xnorm);
   }
+  // experts per lane of the selection: 1, 2, 4 or 16
+  if (E <= 64) screen_select<1>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
+  else if (E <= 128) screen_select<2>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
+  else if (E <= 256) screen_select<4>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
+  else screen_select<16>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
 }
 
 template <typename In>
@@ -627,39 +1102,46 @@ hipError_t launch_dt(const Shape& s, const void* x, const void* Wr, const float*
                      int32_t* idx, float* w, hipStream_t st) {
   if (s.T <= 64) return launch_small<In>(s, x, Wr, bias, idx, w, st);
   if constexpr (sizeof(In) == 2) {
-    const size_t lds = (size_t)screen_lds((int)s.E).total;
     // allow more than 64 KB of dynamic LDS, once per device (the attribute
     // belongs to the device's copy of the kernel)
     static std::atomic<bool> lds_opt_in[kMaxDevices];
-    static std::atomic<int> cu_count[kMaxDevices];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    int cus = cu_count[dev].load(std::memory_order_relaxed);
-    if (cus == 0) {
-      e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e != hipSuccess) return e;
-      cu_count[dev].store(cus, std::memory_order_relaxed);
-    }
-    // 16 tokens per workgroup; 8 when that still leaves workgroup slots (two
-    // per CU) empty and the router matrix is small enough (<= 1 MB) for the
-    // extra workgroups to re-read it cheaply (measured: E=128, d=2048 faster;
-    // E=256, d=7168 and T=8192 slower)
-    int tok = kScreenTT;
-    if ((s.T + kScreenTT - 1) / kScreenTT < 2 * (int64_t)cus && s.E * s.d * 2 <= (1 << 20))
-      tok = 8;
-    const unsigned grid = (unsigned)((s.T + tok - 1) / tok);
+    const unsigned grid = (unsigned)((s.T + kScreenTT - 1) / kScreenTT);
     if (!lds_opt_in[dev].load(std::memory_order_acquire)) {
-      e = hipFuncSetAttribute((const void*)route_screen_kernel,
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)screen_lds(1024).total);
-      if (e != hipSuccess) return e;
+      // each kernel's largest dynamic LDS (its static rings come on top)
+      const struct {
+        const void* f;
+        int64_t bytes;
+      } opt[] = {{(const void*)route_staged_kernel<1>, screen_lds(128, true).total},
+                 {(const void*)route_staged_kernel<2>, screen_lds(kStagedMaxE, false).total},
+                 {(const void*)route_direct_kernel<2>, screen_lds(kMaxE, true).total}};
+      for (const auto& o : opt) {
+        e = hipFuncSetAttribute(o.f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)o.bytes);
+        if (e != hipSuccess) return e;
+      }
       lds_opt_in[dev].store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL(route_screen_kernel, dim3(grid), dim3(kThreads), lds, st,
-                       (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, s.T, s.d, (int)s.E,
-                       (int)s.k, tok);
+    // up to 256 experts: operands staged through LDS, one block of 16
+    // experts per wave up to 128 experts, two beyond; more experts: direct
+    if (s.E <= 128) {
+      const size_t lds = (size_t)screen_lds((int)s.E, true).total;
+      hipLaunchKernelGGL(route_staged_kernel<1>, dim3(grid), dim3(kScreenThreads), lds, st,
+                         (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, s.T, s.d,
+                         (int)s.E, (int)s.k);
+    } else if (s.E <= kStagedMaxE) {
+      const size_t lds = (size_t)screen_lds((int)s.E, false).total;
+      hipLaunchKernelGGL(route_staged_kernel<2>, dim3(grid), dim3(kScreenThreads), lds, st,
+                         (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, s.T, s.d,
+                         (int)s.E, (int)s.k);
+    } else {
+      const size_t lds = (size_t)screen_lds((int)s.E, true).total;
+      hipLaunchKernelGGL(route_direct_kernel<2>, dim3(grid), dim3(kScreenThreads), lds, st,
+                         (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, s.T, s.d,
+                         (int)s.E, (int)s.k);
+    }
     return hipGetLastError();
   } else {
     if (s.E > 512) return launch_tiled<In, 8>(s, x, Wr, bias, idx, w, st);

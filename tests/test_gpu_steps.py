@@ -68,6 +68,9 @@ def _route_case(name):
             None, 2
     if name == "screen_zero_router":
         return n((50, 5, 0), (90, 96), 1.0, "bf16"), np.zeros((40, 96), np.uint16), None, 5
+    if name == "screen_zero_router_E100":
+        # every expert stays a candidate (more than 64): ranked in rounds
+        return n((52, 5, 0), (90, 96), 1.0, "bf16"), np.zeros((100, 96), np.uint16), None, 5
     if name == "screen_duplicate_rows":
         x = n((51, 5, 0), (97, 256), 1.0, "bf16")
         W = n((51, 5, 1), (64, 256), 0.05, "bf16")
@@ -83,8 +86,8 @@ def _route_case(name):
 ROUTE_CASES = ["tiny_fp32", "gpt_oss_20b_decode", "zero_router_ties", "duplicate_rows",
                "integer_exact_f32", "integer_exact_bf16", "ragged_E100_d136", "max_E1024",
                "k_equals_E", "screen_E1024", "screen_E300_ragged", "screen_E8_long_d",
-               "screen_zero_router", "screen_duplicate_rows", "fine_grained_zipf_full",
-               "deepseek_v3_full"]
+               "screen_zero_router", "screen_zero_router_E100", "screen_duplicate_rows",
+               "fine_grained_zipf_full", "deepseek_v3_full"]
 
 
 @pytest.mark.parametrize("name", ROUTE_CASES)
@@ -102,7 +105,7 @@ def test_route(name):
     amb = check_routing(host(idx_d), host(w_d), L, abs_scores(x, W), idx_ref, w_ref)
     assert len(amb) <= max(1, T // 1000), f"{len(amb)} near-tie tokens"
     if name in ("zero_router_ties", "duplicate_rows", "screen_zero_router",
-                "screen_duplicate_rows") or name.startswith("integer"):
+                "screen_zero_router_E100", "screen_duplicate_rows") or name.startswith("integer"):
         assert not amb and np.array_equal(host(idx_d), idx_ref)
 
 
