@@ -196,6 +196,31 @@ int moe_layer_forward(const moe_shape* s, const void* x, const void* W_router,
                       const void* W_down, void* y, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------- whole layer, no allocation
+ * moe_layer_forward_static: moe_layer_forward with the intermediates in a
+ * static device array of the library instead of a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  It allocates
+ * nothing and frees nothing.
+ *   - The array holds MOE_STATIC_SCRATCH_BYTES on every GPU the library
+ *     runs on (on the calling thread's current device, which must be the
+ *     stream's), from the library's load until the process ends.
+ *   - Shapes whose moe_workspace_size exceeds it are rejected with
+ *     MOE_ERR_WORKSPACE before any HIP call (e.g. decode batches fit;
+ *     large prefill batches do not).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *     time on one GPU (different streams, or different threads) race and
+ *     must be serialised by the caller.  Nothing in the array needs to start
+ *     at zero; each call overwrites what it reads.
+ * Arguments, results and errors are those of moe_layer_forward; the first
+ * call on a device also looks up the array's address there (MOE_ERR_HIP if
+ * that fails). */
+#define MOE_STATIC_SCRATCH_BYTES (32u << 20)
+
+int moe_layer_forward_static(const moe_shape* s, const void* x, const void* W_router,
+                             const float* bias, const void* W_gate_up,
+                             const void* W_down, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

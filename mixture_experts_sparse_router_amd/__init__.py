@@ -33,7 +33,10 @@ WS_NAMES = ("topk_idx", "topk_w", "counts", "offsets", "sorted_slot", "slot_pos"
 ENTRY_POINTS = ("moe_status_string", "moe_version", "moe_last_hip_error", "moe_route", "moe_permute",
                 "moe_grouped_gemm_gate_up", "moe_grouped_gemm_down", "moe_grouped_gemm",
                 "moe_combine", "moe_workspace_size", "moe_workspace_offsets",
-                "moe_layer_forward")
+                "moe_layer_forward", "moe_layer_forward_static")
+
+# size of the library's static intermediate array (include/moe.h)
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class MoeError(RuntimeError):
@@ -87,6 +90,7 @@ def _load():
         "moe_grouped_gemm": [sp, vp, vp, vp, vp, vp, vp, vp, vp],
         "moe_combine": [sp, vp, vp, vp, vp, vp],
         "moe_layer_forward": [sp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "moe_layer_forward_static": [sp, vp, vp, vp, vp, vp, vp, vp],
     }
     for name, argtypes in sigs.items():
         fn = getattr(L, name)
@@ -259,6 +263,23 @@ def moe_layer_forward(s: moe_shape, x, W_router, bias, W_gate_up, W_down, y, wor
           _ptr(W_down, s.G * s.d * s.f, fd, "W_down"),
           _ptr(y, s.T * s.d, fd, "y"),
           workspace.data_ptr(), workspace.numel(),
+          _stream(stream))
+
+
+def moe_layer_forward_static(s: moe_shape, x, W_router, bias, W_gate_up, W_down, y,
+                             stream=None):
+    """moe_layer_forward with the library's static intermediate array (no
+    workspace, no allocation; shapes up to STATIC_SCRATCH_BYTES of
+    intermediates; calls on one GPU must not overlap)."""
+    torch = _torch()
+    fd = _float_dtype(s)
+    _call("moe_layer_forward_static", ctypes.byref(s),
+          _ptr(x, s.T * s.d, fd, "x"),
+          _ptr(W_router, s.E * s.d, fd, "W_router"),
+          _ptr(bias, s.E, torch.float32, "bias", optional=True),
+          _ptr(W_gate_up, s.G * 2 * s.f * s.d, fd, "W_gate_up"),
+          _ptr(W_down, s.G * s.d * s.f, fd, "W_down"),
+          _ptr(y, s.T * s.d, fd, "y"),
           _stream(stream))
 
 

@@ -3,11 +3,22 @@
 // the pages define them are documented in include/moe.h.
 #include <string.h>
 
+#include <atomic>
+
 #include "moe_common.h"
 
 using namespace moe;
 
+// Intermediates of moe_layer_forward_static: one array per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a
+// host-side stand-in; its device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+// device address of `scratch` on each device, looked up on first use there
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
 
 constexpr int64_t kMaxGroups = 1024;
 constexpr int64_t kMaxK = 64;
@@ -39,6 +50,17 @@ int check_shape(const moe_shape* m) {
   if (m->dt == MOE_DT_BF16 && m->T > 64 &&
       (m->T * m->d >= ((int64_t)1 << 30) || m->f * m->d >= ((int64_t)1 << 29)))
     return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Tensors of the whole-layer entry points.
+int check_layer_ptrs(const Shape& s, const void* x, const void* W_router, const float* bias,
+                     const void* W_gate_up, const void* W_down, const void* y) {
+  if (!ok_ptr(x, s.T * s.d) || !ok_ptr(W_router, s.E * s.d) ||
+      !ok_ptr(W_gate_up, s.G() * 2 * s.f * s.d) || !ok_ptr(W_down, s.G() * s.d * s.f) ||
+      !ok_ptr(y, s.T * s.d))
+    return MOE_ERR_INVALID_ARG;
+  if (bias && ((uintptr_t)bias & 3u)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -183,11 +205,8 @@ int moe_layer_forward(const moe_shape* m, const void* x, const void* W_router,
   int rc = check_shape(m);
   if (rc != MOE_OK) return rc;
   const Shape s = to_shape(m);
-  if (!ok_ptr(x, s.T * s.d) || !ok_ptr(W_router, s.E * s.d) ||
-      !ok_ptr(W_gate_up, s.G() * 2 * s.f * s.d) || !ok_ptr(W_down, s.G() * s.d * s.f) ||
-      !ok_ptr(y, s.T * s.d))
-    return MOE_ERR_INVALID_ARG;
-  if (bias && ((uintptr_t)bias & 3u)) return MOE_ERR_INVALID_ARG;
+  rc = check_layer_ptrs(s, x, W_router, bias, W_gate_up, W_down, y);
+  if (rc != MOE_OK) return rc;
   size_t off[MOE_WS_COUNT], total;
   layout(s, off, &total);
   if (workspace_bytes < total) return MOE_ERR_WORKSPACE;
@@ -211,6 +230,35 @@ int moe_layer_forward(const moe_shape* m, const void* x, const void* W_router,
   if (e == hipSuccess) e = launch_down(s, act, offsets, W_down, out, st);
   if (e == hipSuccess) e = launch_combine(s, out, slot_pos, w, y, st);
   return hip_status(e);
+}
+
+int moe_layer_forward_static(const moe_shape* m, const void* x, const void* W_router,
+                             const float* bias, const void* W_gate_up, const void* W_down,
+                             void* y, void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  rc = check_layer_ptrs(s, x, W_router, bias, W_gate_up, W_down, y);
+  if (rc != MOE_OK) return rc;
+  size_t off[MOE_WS_COUNT], total;
+  layout(s, off, &total);
+  if (total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  if (s.T == 0) return MOE_OK;
+  // the calling thread's current device: look up (once) where its copy of
+  // the array lives
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  void* ws = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ws) {
+    e = hipGetSymbolAddress(&ws, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!ws) return MOE_ERR_HIP;
+    g_scratch_ptr[dev].store(ws, std::memory_order_release);
+  }
+  return moe_layer_forward(m, x, W_router, bias, W_gate_up, W_down, y, ws,
+                           (size_t)MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

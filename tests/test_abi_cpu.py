@@ -156,3 +156,29 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(16, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         moe.moe_route(s, x, x, None, x, x)
+
+
+def test_static_entry_checks_before_any_hip_call():
+    """moe_layer_forward_static rejects bad arguments and shapes whose
+    intermediates exceed its static array before touching HIP."""
+    L = moe.lib()
+    src = open(HEADER).read()
+    assert f"#define MOE_STATIC_SCRATCH_BYTES (32u << 20)" in src
+    assert moe.STATIC_SCRATCH_BYTES == 32 << 20
+    p = ctypes.c_void_p(4096)
+    big = moe.shape(4096, 2048, 768, 128, 8, 0, moe.MOE_DT_BF16)  # ~184 MB of intermediates
+    assert moe.workspace_size(big) > moe.STATIC_SCRATCH_BYTES
+    assert L.moe_layer_forward_static(ctypes.byref(big), p, p, None, p, p, p,
+                                      None) == moe.MOE_ERR_WORKSPACE
+    s = _shape()
+    assert moe.workspace_size(s) <= moe.STATIC_SCRATCH_BYTES
+    assert L.moe_layer_forward_static(None, p, p, None, p, p, p, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_static(ctypes.byref(_shape(k=0)), p, p, None, p, p, p,
+                                      None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_static(ctypes.byref(s), None, p, None, p, p, p,
+                                      None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_static(ctypes.byref(s), p, p, ctypes.c_void_p(4097), p, p, p,
+                                      None) == moe.MOE_ERR_INVALID_ARG
+    # an empty batch needs no intermediates and enqueues nothing
+    assert L.moe_layer_forward_static(ctypes.byref(_shape(T=0)), None, p, None, p, p, None,
+                                      None) == moe.MOE_OK

@@ -1,0 +1,51 @@
+"""moe_layer_forward_static, the entry point that allocates nothing (its
+intermediates live in the library's static device array), against
+moe_layer_forward with a caller workspace, through the C ABI: two calls in a
+row, the second with a smaller input, each bitwise equal to the workspace
+path (same kernels, same order of every sum) and within tolerance of the
+oracle."""
+import numpy as np
+import pytest
+
+import moe_synth
+import oracle
+import mixture_experts_sparse_router_amd as moe
+from gpu_util import (abs_scores, assert_rows_close, check_routing, dt_code, empty, host,
+                      layer_inputs_to_device, run_layer)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+CASES = [
+    # the gpt-oss-20b-shaped decode layer, then a smaller one with a shared expert
+    (moe_synth.CONFIGS[2], 2),
+    (moe_synth.LayerConfig("static_small_shared", T=5, d=320, f=192, E=12, k=3, S=1,
+                           dtype="bf16", w_std=0.05), 41),
+]
+
+
+def test_static_entry_matches_workspace_entry():
+    for cfg, seed in CASES:
+        print(f"static entry {cfg.name} seed={seed}", flush=True)
+        inp = moe_synth.make_layer_inputs(cfg, seed)
+        d = layer_inputs_to_device(inp)
+        s = moe.shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.S, dt_code(cfg.dtype))
+        assert moe.workspace_size(s) <= moe.STATIC_SCRATCH_BYTES
+        y_ws, views, _, _ = run_layer(cfg, d)
+        y_st = empty((cfg.T, cfg.d), cfg.dtype)
+        y_st.fill_(float("nan"))
+        moe.moe_layer_forward_static(s, d["x"], d["W_router"], d["bias"], d["W_gate_up"],
+                                     d["W_down"], y_st)
+        torch.cuda.synchronize()
+        assert torch.equal(y_st, y_ws), f"{cfg.name}: static and workspace paths differ"
+        L, idx_ref, w_ref = oracle.route(inp["x"], inp["W_router"], cfg.k, bias=inp["bias"])
+        amb = check_routing(host(views["topk_idx"]), host(views["topk_w"]), L,
+                            abs_scores(inp["x"], inp["W_router"]), idx_ref, w_ref)
+        forced = host(views["topk_idx"]) if amb else None
+        y_ref, _, _ = oracle.layer_forward(inp["x"], inp["W_router"], inp["W_gate_up"],
+                                           inp["W_down"], cfg.k, S=cfg.S, bias=inp["bias"],
+                                           forced_idx=forced)
+        worst = assert_rows_close(host(y_st), y_ref, cfg.dtype, cfg.name)
+        print(f"  {cfg.name}: bitwise equal to the workspace path, worst row rel err "
+              f"{worst:.3e}", flush=True)
