@@ -126,7 +126,11 @@ int moe_route(const moe_shape* s, const void* x, const void* W_router,
  *               ascending s (stable).  Rows T*k + sigma*T + t (shared expert
  *               sigma, token t) are implicit and not stored.
  *   slot_pos    [T*k]   int32 out: inverse map, row of copy s
- * topk_idx entries must lie in [0, E). */
+ * topk_idx entries should lie in [0, E).  A copy whose id lies outside it
+ * selects no expert: it is listed after all routed copies (rows up to T*k,
+ * inside the last expert's row range offsets[E-1] .. offsets[E] = T*k,
+ * though not in that expert's count) and gets slot_pos = -1, which
+ * moe_combine skips. */
 int moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* counts,
                 int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
                 void* stream);
@@ -140,7 +144,8 @@ int moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* counts,
  *                             u = W_gate_up[e, f + n, :] . x[t, :],
  *   silu(z) = z / (1 + exp(-z)), 0 <= n < f.
  *   W_gate_up [E+S, 2f, d] dt   act [R, f] dt out.
- * Experts with no rows read none of their weights. */
+ * Experts with no rows are skipped (for T <= 64 each of their column tiles
+ * may read one K step of weights, loaded before the row count is known). */
 int moe_grouped_gemm_gate_up(const moe_shape* s, const void* x,
                              const int32_t* sorted_slot, const int32_t* offsets,
                              const void* W_gate_up, void* act, void* stream);
@@ -163,13 +168,17 @@ int moe_grouped_gemm(const moe_shape* s, const void* x,
  *   y[t] = sum_{j<k} topk_w[t,j] * expert_out[slot_pos[t*k+j]]
  *        + sum_{sigma<S} expert_out[T*k + sigma*T + t]
  * accumulated in fp32 in that fixed order (no atomics), rounded to dt.
+ * Copies with slot_pos < 0 (dropped by moe_permute) add nothing.
  *   expert_out [R, d] dt,  slot_pos [T*k],  topk_w [T, k],  y [T, d] dt out. */
 int moe_combine(const moe_shape* s, const void* expert_out,
                 const int32_t* slot_pos, const float* topk_w, void* y,
                 void* stream);
 
 /* ------------------------------------------------------------- whole layer
- * moe_layer_forward: steps 1-5 enqueued back to back on one stream.
+ * moe_layer_forward: steps 1-5 enqueued back to back on one stream (for bf16
+ * batches of at most 64 tokens, the gate_up kernel finds each expert's rows
+ * from the ids and writes the permutation itself: same results, one launch
+ * fewer).
  * Intermediates live in the caller's workspace (device memory of at least
  * moe_workspace_size(s) bytes, 256-byte aligned); its layout is given by
  * moe_workspace_offsets.  y [T, d] dt out. */

@@ -225,8 +225,16 @@ int moe_layer_forward(const moe_shape* m, const void* x, const void* W_router,
 
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = launch_route(s, x, W_router, bias, idx, w, st);
-  if (e == hipSuccess) e = launch_permute(s, idx, counts, offsets, sorted_slot, slot_pos, st);
-  if (e == hipSuccess) e = launch_gate_up(s, x, sorted_slot, offsets, W_gate_up, act, st);
+  if (s.dt == MOE_DT_BF16 && s.T <= 64) {
+    // decode batches: the gate_up kernel finds its rows from the ids and
+    // writes the permutation itself (one launch fewer)
+    if (e == hipSuccess)
+      e = launch_gate_up_from_ids(s, x, idx, W_gate_up, act, counts, offsets, sorted_slot,
+                                  slot_pos, st);
+  } else {
+    if (e == hipSuccess) e = launch_permute(s, idx, counts, offsets, sorted_slot, slot_pos, st);
+    if (e == hipSuccess) e = launch_gate_up(s, x, sorted_slot, offsets, W_gate_up, act, st);
+  }
   if (e == hipSuccess) e = launch_down(s, act, offsets, W_down, out, st);
   if (e == hipSuccess) e = launch_combine(s, out, slot_pos, w, y, st);
   return hip_status(e);

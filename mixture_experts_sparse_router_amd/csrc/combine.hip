@@ -1,6 +1,7 @@
 // combine.hip -- weighted un-permute of the expert outputs back to token order.
 //
 // y[t] = sum_{j<k} w[t,j] * out[slot_pos[t*k+j]]  (+ every shared expert row)
+// (copies with slot_pos < 0, dropped by the permutation, add nothing)
 // The output is the routing-weighted sum of the selected experts' outputs
 // only (Baidu "MoE稀疏架构是什么" page, section 四), gathered and reordered
 // back to token order after the grouped GEMM (aitoday "MoEs in Transformers"
@@ -59,6 +60,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     float v[8];
     for (int j = 0; j < k; ++j) {
       const int64_t row = slot_pos[t * k + j];
+      if (row < 0) continue;  // a copy whose expert id was out of range
       const float wj = w[t * k + j];
       Vec8<T>::load(O + row * d + c, v);
 #pragma unroll

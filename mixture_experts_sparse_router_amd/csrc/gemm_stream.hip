@@ -31,12 +31,12 @@ struct StreamRegs {
   bool ok[4];  // chunk c lies inside K (else its registers are zeroed at use)
 };
 
-// Loads of one K step.  Chunks past K read a valid address (offset 0) and
-// are zeroed by a select when they are used, so the loads stay branch-free.
+// Loads of one K step: the weight rows' chunks and the token rows' chunks.
+// Chunks past K read a valid address (offset 0) and are zeroed by a select
+// when they are used, so the loads stay branch-free.
 template <bool GATED, int MB>
-__device__ __forceinline__ void stream_load(StreamRegs<GATED, MB>& r, const bf16_t* Bg,
-                                            const bf16_t* Bu, const bf16_t* const* Ap,
-                                            int64_t k0, int kb, int64_t K) {
+__device__ __forceinline__ void stream_load_w(StreamRegs<GATED, MB>& r, const bf16_t* Bg,
+                                              const bf16_t* Bu, int64_t k0, int kb, int64_t K) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int64_t kk = k0 + 32 * c + 8 * kb;
@@ -45,31 +45,134 @@ __device__ __forceinline__ void stream_load(StreamRegs<GATED, MB>& r, const bf16
     r.ok[c] = ok;
     r.bg[c] = ldg16(Bg + ka);
     if constexpr (GATED) r.bu[c] = ldg16(Bu + ka);
+  }
+}
+template <bool GATED, int MB>
+__device__ __forceinline__ void stream_load_a(StreamRegs<GATED, MB>& r, const bf16_t* const* Ap,
+                                              int64_t k0, int kb, int64_t K) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int64_t kk = k0 + 32 * c + 8 * kb;
+    const int64_t ka = kk < K ? kk : 0;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) r.a[mb][c] = ldg16(Ap[mb] + ka);
   }
 }
 
-template <bool GATED, int MB>
+// Rows of one expert group in the fused form: the copies s (ascending) whose
+// expert id is g, found from the ids themselves.  n_slots = T*k <= 4096.
+struct GroupFromIds {
+  int row_begin, rows;
+};
+// One wave's view: ballots over the ids, 64 at a time.  `list` (LDS, >= 64
+// entries) receives the group's copies in ascending order (a group has at
+// most T <= 64 of them: a token picks an expert at most once).  Ids outside
+// [0, E) count for no group.
+__device__ __forceinline__ GroupFromIds group_from_ids(const int32_t* __restrict__ idx,
+                                                       int n_slots, int g, int* list) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below_lanes = (1ull << lane) - 1ull;
+  int before = 0, found = 0;
+  for (int s0 = 0; s0 < n_slots; s0 += 64) {
+    const int s = s0 + lane;
+    const uint32_t v = s < n_slots ? (uint32_t)idx[s] : 0xffffffffu;  // unsigned: < 0 is huge
+    const uint64_t lt = __ballot(v < (uint32_t)g);
+    const uint64_t eq = __ballot(v == (uint32_t)g);
+    if ((eq >> lane) & 1ull) {
+      const int r = found + __popcll(eq & below_lanes);
+      if (r < 64) list[r] = s;
+    }
+    before += __popcll(lt);
+    found += __popcll(eq);
+  }
+  return GroupFromIds{before, found};
+}
+
+// FUSED (gate_up only): the group's rows are found from the expert ids
+// themselves instead of a permutation (decode batches: at most 64 tokens),
+// and the workgroups of column tile 0 write that permutation (counts,
+// offsets, sorted_slot, slot_pos) for the steps that follow.
+template <bool GATED, int MB, bool FUSED>
 __global__ __launch_bounds__(256) void stream_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
     bf16_t* __restrict__ out, int64_t K, int64_t N, int64_t T, int64_t Tk, int64_t k,
-    int G, int ntiles) {
+    int G, int ntiles, const int32_t* __restrict__ topk_idx, int E,
+    int32_t* __restrict__ p_counts, int32_t* __restrict__ p_offsets,
+    int32_t* __restrict__ p_sorted, int32_t* __restrict__ p_slot_pos) {
   __shared__ f32x4 red[3][MB][2][64];  // partials of waves 1..3
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int s_list[64];           // FUSED: the group's copies, ascending
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = (int)blockIdx.x / ntiles;
   if (g >= G) return;
-  const int64_t row_begin = offsets[g];
-  const int64_t rows = offsets[g + 1] - row_begin;
-  if (rows <= 0) return;  // empty expert: its weights are never read
+  const int tile = (int)blockIdx.x % ntiles;
   const int j = lane & 15, kb = lane >> 4;
-  const int64_t n0 = (int64_t)((int)blockIdx.x % ntiles) * 16;
+  const int64_t n0 = (int64_t)tile * 16;
   const int64_t col = n0 + j;
   const bool col_ok = col < N;
   const int64_t colc = col_ok ? col : N - 1;
   const bf16_t* Bg = W + ((int64_t)g * (GATED ? 2 * N : N) + colc) * K;
   const bf16_t* Bu = Bg + N * K;  // up rows (GATED only)
+  // gate_up: the weights of this wave's first K step do not depend on the
+  // group's rows, so their loads are issued before the group is looked up
+  // (measured faster; an empty group drops them unused: at most one K step
+  // per wave is read of an expert without rows)
+  StreamRegs<GATED, MB> first;
+  bool have_first = GATED;
+  if constexpr (GATED) stream_load_w<GATED, MB>(first, Bg, Bu, (int64_t)wave * 128, kb, K);
+
+  int64_t row_begin, rows;
+  if constexpr (FUSED) {
+    if (g < E) {
+      // every wave finds the group itself (its own writes to s_list are the
+      // ones it reads; the other waves write the same values).  A token
+      // picks an expert at most once, so a group has at most T <= 64 rows.
+      const GroupFromIds gi = group_from_ids(topk_idx, (int)Tk, g, s_list);
+      row_begin = gi.row_begin;
+      rows = gi.rows < 64 ? gi.rows : 64;
+    } else {
+      row_begin = Tk + (int64_t)(g - E) * T;  // shared expert g - E: every token
+      rows = T;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (tile == 0 && wave == 0) {
+      if (lane == 0) {
+        p_counts[g] = (int32_t)rows;
+        p_offsets[g] = (int32_t)row_begin;
+        if (g == G - 1) p_offsets[G] = (int32_t)(Tk + (int64_t)(G - E) * T);
+      }
+      if (g < E) {
+        for (int r = lane; r < rows && r < 64; r += 64) {
+          const int sl = s_list[r];
+          p_sorted[row_begin + r] = sl;
+          p_slot_pos[sl] = (int32_t)(row_begin + r);
+        }
+      }
+    }
+    if (g == 0 && tile == 0 && wave == 1) {
+      // copies whose expert id is outside [0, E) take no expert: they are
+      // listed after all routed rows and marked with slot_pos = -1
+      const uint64_t below_lanes = (1ull << lane) - 1ull;
+      int ndrop = 0;
+      for (int s0 = 0; s0 < (int)Tk; s0 += 64)
+        ndrop += __popcll(__ballot(s0 + lane < (int)Tk && (uint32_t)topk_idx[s0 + lane] >= (uint32_t)E));
+      int at = (int)Tk - ndrop;
+      for (int s0 = 0; s0 < (int)Tk; s0 += 64) {
+        const int sl = s0 + lane;
+        const bool drop = sl < (int)Tk && (uint32_t)topk_idx[sl] >= (uint32_t)E;
+        const uint64_t m = __ballot(drop);
+        if (drop) {
+          p_sorted[at + __popcll(m & below_lanes)] = sl;
+          p_slot_pos[sl] = -1;
+        }
+        at += __popcll(m);
+      }
+    }
+  } else {
+    row_begin = offsets[g];
+    rows = offsets[g + 1] - row_begin;
+  }
+  if (rows <= 0) return;  // empty expert: its weights are never used
 
   for (int64_t m0 = 0; m0 < rows; m0 += 16 * MB) {
     const bf16_t* Ap[MB];
@@ -78,7 +181,10 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
       int64_t r = m0 + mb * 16 + j;
       if (r >= rows) r = rows - 1;  // padding rows repeat a valid row
       const int64_t grow = row_begin + r;
-      if constexpr (GATED) {
+      if constexpr (FUSED) {
+        Ap[mb] = A + (g < E ? (int64_t)((uint32_t)s_list[r < 64 ? r : 63] / (uint32_t)k)
+                            : (int64_t)((uint32_t)(grow - Tk) % (uint32_t)T)) * K;
+      } else if constexpr (GATED) {
         Ap[mb] = A + row_token(grow, sorted_slot, Tk, k, T) * K;
       } else {
         Ap[mb] = A + grow * K;
@@ -95,7 +201,17 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
     // occupancy more than it adds bytes in flight)
     for (int64_t k0 = (int64_t)wave * 128; k0 < K; k0 += 512) {
       StreamRegs<GATED, MB> r;
-      stream_load<GATED, MB>(r, Bg, Bu, Ap, k0, kb, K);
+      if constexpr (GATED) {
+        if (have_first) {
+          r = first;
+          have_first = false;
+        } else {
+          stream_load_w<GATED, MB>(r, Bg, Bu, k0, kb, K);
+        }
+      } else {
+        stream_load_w<GATED, MB>(r, Bg, Bu, k0, kb, K);
+      }
+      stream_load_a<GATED, MB>(r, Ap, k0, kb, K);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const u32x4 bg = zero_unless(r.ok[c], r.bg[c]);
@@ -155,9 +271,10 @@ hipError_t launch_stream_gemm(bool gated, const Shape& s, const void* A,
   const unsigned grid = (unsigned)((int64_t)G * ntiles);
   const int MB = (int)((s.T + 15) / 16);
 #define MOE_STREAM(gt, mb)                                                              \
-  hipLaunchKernelGGL((stream_gemm_kernel<gt, mb>), dim3(grid), dim3(256), 0, st,       \
+  hipLaunchKernelGGL((stream_gemm_kernel<gt, mb, false>), dim3(grid), dim3(256), 0, st, \
                      (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W,          \
-                     (bf16_t*)out, K, N, s.T, s.Tk(), s.k, G, ntiles)
+                     (bf16_t*)out, K, N, s.T, s.Tk(), s.k, G, ntiles, nullptr, (int)s.E, \
+                     nullptr, nullptr, nullptr, nullptr)
   if (gated) {
     switch (MB) {
       case 1: MOE_STREAM(true, 1); break;
@@ -174,6 +291,29 @@ hipError_t launch_stream_gemm(bool gated, const Shape& s, const void* A,
     }
   }
 #undef MOE_STREAM
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_from_ids(const Shape& s, const void* x, const int32_t* topk_idx,
+                                   const void* W_gate_up, void* act, int32_t* counts,
+                                   int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
+                                   hipStream_t st) {
+  const int G = (int)s.G();
+  const int ntiles = (int)((s.f + 15) / 16);
+  const unsigned grid = (unsigned)((int64_t)G * ntiles);
+  const int MB = (int)((s.T + 15) / 16);
+#define MOE_FUSED(mb)                                                                   \
+  hipLaunchKernelGGL((stream_gemm_kernel<true, mb, true>), dim3(grid), dim3(256), 0, st, \
+                     (const bf16_t*)x, nullptr, nullptr, (const bf16_t*)W_gate_up,       \
+                     (bf16_t*)act, s.d, s.f, s.T, s.Tk(), s.k, G, ntiles, topk_idx,      \
+                     (int)s.E, counts, offsets, sorted_slot, slot_pos)
+  switch (MB) {
+    case 1: MOE_FUSED(1); break;
+    case 2: MOE_FUSED(2); break;
+    case 3: MOE_FUSED(3); break;
+    default: MOE_FUSED(4); break;
+  }
+#undef MOE_FUSED
   return hipGetLastError();
 }
 

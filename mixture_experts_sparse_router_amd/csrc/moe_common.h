@@ -137,6 +137,12 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* sorted_s
 hipError_t launch_stream_gemm(bool gated, const Shape& s, const void* A,
                               const int32_t* sorted_slot, const int32_t* offsets, const void* W,
                               void* out, int64_t K, int64_t N, hipStream_t st);
+// Decode-sized batches (T <= 64, bf16): gate_up with the group rows found
+// from the expert ids, writing the permutation on the way.
+hipError_t launch_gate_up_from_ids(const Shape& s, const void* x, const int32_t* topk_idx,
+                                   const void* W_gate_up, void* act, int32_t* counts,
+                                   int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
+                                   hipStream_t st);
 hipError_t launch_down(const Shape& s, const void* act, const int32_t* offsets,
                        const void* W_down, void* expert_out, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const void* expert_out,

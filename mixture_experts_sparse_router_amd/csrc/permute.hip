@@ -19,6 +19,13 @@
 //      and each row is turned into that wave's base position for the expert.
 //   C. position = base[w][e] + rank; sorted_slot[position] = s.
 // Integer only: the result is exact and independent of scheduling.
+//
+// Ids outside [0, E) select no expert: such a copy is ranked in a bin of its
+// own after all experts, so it lands in rows [valid, T*k) (inside the last
+// expert's row range, since offsets[E] = T*k always; that expert's count does
+// not include them) and gets slot_pos = -1, which the combine skips.  Every
+// row below T*k is thus written, every index stays in bounds, and the shared
+// rows always start at T*k.
 #include "moe_common.h"
 
 namespace moe {
@@ -60,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ slot_pos, int64_t T, int64_t k, int E, int S, int nbits) {
-  __shared__ int32_t hist[kWaves][kMaxGroups];
+  __shared__ int32_t hist[kWaves][kMaxGroups + 1];  // + the bin of dropped copies
   __shared__ int32_t tmp[2 * kWaves + 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -70,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
   const int64_t s_end = s_begin + seg < n ? s_begin + seg : n;
   const uint64_t lanes_below = (1ull << lane) - 1ull;
 
-  for (int e = lane; e < E; e += 64) hist[wave][e] = 0;
+  for (int e = lane; e <= E; e += 64) hist[wave][e] = 0;
 
   // ---- A: rank inside the wave's range; the expert ids of kBatch steps of
   // 64 copies are loaded up front so their latency overlaps
@@ -85,8 +92,9 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
     for (int u = 0; u < kBatch; ++u) {
       if (b0 + 64 * u >= s_end) break;
       const int64_t s = b0 + 64 * u + lane;
-      const bool active = v[u] >= 0 && v[u] < E;  // ids outside [0, E) are skipped
-      const int key = active ? v[u] : E;          // E: distinct dummy key
+      const bool active = s < s_end;
+      // expert id; E: the dropped bin (ids outside [0, E)); E + 1: idle lane
+      const int key = !active ? E + 1 : (v[u] >= 0 && v[u] < E) ? v[u] : E;
       uint64_t peers = ~0ull;
       for (int b = 0; b < nbits; ++b) {
         const bool bit = (key >> b) & 1;
@@ -106,7 +114,8 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
   }
   __syncthreads();
 
-  // ---- B: totals, prefix sum, per-wave bases
+  // ---- B: totals, prefix sum over the routed experts, per-wave bases; the
+  // dropped bin follows the routed rows, the shared groups start at T*k
   const int g = threadIdx.x;  // expert group handled by this thread
   int total = 0;
   if (g < E) {
@@ -114,15 +123,19 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
   } else if (g < E + S) {
     total = (int)T;
   }
-  int all = 0;
-  const int off = block_exclusive_scan(g < E + S ? total : 0, tmp, &all);
-  if (g < E + S) {
+  int valid = 0;
+  const int off = block_exclusive_scan(g < E ? total : 0, tmp, &valid);
+  const int Tk = (int)(T * k);
+  if (g < E) {
     counts[g] = total;
     offsets[g] = off;
+  } else if (g < E + S) {
+    counts[g] = total;
+    offsets[g] = Tk + (g - E) * (int)T;
   }
-  if (g == 0) offsets[E + S] = all;
-  if (g < E) {
-    int run = off;
+  if (g == 0) offsets[E + S] = Tk + S * (int)T;
+  if (g <= E) {
+    int run = g < E ? off : valid;
     for (int w = 0; w < kWaves; ++w) {
       const int c = hist[w][g];
       hist[w][g] = run;
@@ -144,14 +157,10 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
     for (int u = 0; u < kBatch; ++u) {
       const int64_t s = b0 + 64 * u + lane;
       if (s >= s_end) continue;
-      const int e = v[u];
-      if (e < 0 || e >= E) {
-        slot_pos[s] = -1;
-        continue;
-      }
-      const int pos = hist[wave][e] + r[u];
+      const bool dropped = v[u] < 0 || v[u] >= E;
+      const int pos = hist[wave][dropped ? E : v[u]] + r[u];
       sorted_slot[pos] = (int32_t)s;
-      slot_pos[s] = pos;
+      slot_pos[s] = dropped ? -1 : pos;
     }
   }
 }
@@ -162,7 +171,7 @@ hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int32_t* coun
                           int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
                           hipStream_t st) {
   int nbits = 0;
-  while ((1 << nbits) <= s.E) ++nbits;  // keys 0..E (E = idle lane)
+  while ((1 << nbits) <= s.E + 1) ++nbits;  // keys 0..E+1 (E: dropped, E+1: idle lane)
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kThreads), 0, st, topk_idx, counts,
                      offsets, sorted_slot, slot_pos, s.T, s.k, (int)s.E, (int)s.S,
                      nbits);
