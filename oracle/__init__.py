@@ -35,12 +35,16 @@ _SIGNATURES = {
     "oracle_route": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _f32p, _f64p, _i32p,
                      _f64p],
     "oracle_permute": [_i64, _i64, _i64, _i64, _i32p, _i32p, _i32p, _i32p, _i32p],
+    "oracle_permute_capacity": [_i64, _i64, _i64, _i64, _i64, _i32p, _i32p, _i32p,
+                                _i32p, _i32p],
+    "oracle_expert_capacity": [_i64, _i64, _i64, ctypes.c_double],
+    "oracle_balance": [_i64, _i64, _i64, _int, _vp, _vp, _f32p, _f64p, _f64p, _f64p],
     "oracle_gate_up_rows": [_i64, _i64p, _i32p, _i64, _i64, _int, _vp, _vp, _f64p],
     "oracle_down_rows": [_i64, _i32p, _i64, _i64, _int, _vp, _vp, _f64p],
     "oracle_combine": [_i64, _i64, _i64, _i64, _int, _vp, _i32p, _f64p, _f64p],
     "oracle_layer_forward": [_i64, _i64, _i64, _i64, _i64, _i64, _int, _vp, _vp,
-                             _f32p, _vp, _vp, _i64, _i64p, _i32p, _i32p, _f64p,
-                             _f64p],
+                             _f32p, _vp, _vp, _i64, _i64p, _i32p, _i64, _i32p,
+                             _f64p, _f64p],
     "oracle_num_threads": [],
 }
 
@@ -76,7 +80,7 @@ class Oracle:
         for name, argtypes in _SIGNATURES.items():
             fn = getattr(L, name)
             fn.argtypes = argtypes
-            fn.restype = ctypes.c_int
+            fn.restype = ctypes.c_int64 if name == "oracle_expert_capacity" else ctypes.c_int
         self.path = path
         self.L = L
 
@@ -100,19 +104,50 @@ class Oracle:
         _check(rc, "oracle_route")
         return logits, idx, w
 
-    def permute(self, idx, E, S=0):
-        """Return (counts[E+S], offsets[E+S+1], sorted_slot[T*k], slot_pos[T*k])."""
+    def permute(self, idx, E, S=0, capacity=None):
+        """Return (counts[E+S], offsets[E+S+1], sorted_slot[T*k], slot_pos[T*k]).
+        capacity: None (no limit) or the most copies one expert keeps."""
         idx = _c(idx, np.int32)
         T, k = idx.shape
         counts = np.empty(E + S, np.int32)
         offsets = np.empty(E + S + 1, np.int32)
         sorted_slot = np.empty(T * k, np.int32)
         slot_pos = np.empty(T * k, np.int32)
-        rc = self.L.oracle_permute(T, k, E, S, _p(idx, _i32p), _p(counts, _i32p),
-                                   _p(offsets, _i32p), _p(sorted_slot, _i32p),
-                                   _p(slot_pos, _i32p))
+        args = (_p(idx, _i32p), _p(counts, _i32p), _p(offsets, _i32p),
+                _p(sorted_slot, _i32p), _p(slot_pos, _i32p))
+        if capacity is None:
+            rc = self.L.oracle_permute(T, k, E, S, *args)
+        else:
+            assert capacity >= 0
+            rc = self.L.oracle_permute_capacity(T, k, E, S, int(capacity), *args)
         _check(rc, "oracle_permute")
         return counts, offsets, sorted_slot, slot_pos
+
+    def expert_capacity(self, T, k, E, factor):
+        """ceil(factor * T*k / E)."""
+        c = self.L.oracle_expert_capacity(T, k, E, float(factor))
+        _check(0 if c >= 0 else -1, "oracle_expert_capacity")
+        return int(c)
+
+    def balance(self, x, W_router, bias=None, want_probs=False):
+        """Return (importance[E] f64, loss f64) or, with want_probs, also the
+        dense softmax probs[T,E]."""
+        x = _c(x)
+        W_router = _c(W_router)
+        dt = _dt(x)
+        assert _dt(W_router) == dt
+        T, d = x.shape
+        E = W_router.shape[0]
+        b = None if bias is None else _c(bias, np.float32)
+        probs = np.empty((T, E), np.float64) if want_probs else None
+        imp = np.empty(E, np.float64)
+        loss = np.empty(1, np.float64)
+        rc = self.L.oracle_balance(T, d, E, dt, _p(x), _p(W_router), _p(b, _f32p),
+                                   _p(probs, _f64p), _p(imp, _f64p), _p(loss, _f64p))
+        _check(rc, "oracle_balance")
+        if want_probs:
+            return imp, float(loss[0]), probs
+        return imp, float(loss[0])
 
     def gate_up_rows(self, x, W_gate_up, tok, expert):
         """SwiGLU activations [n, f] (fp64) of (token, expert) pairs."""
@@ -160,9 +195,10 @@ class Oracle:
         return y
 
     def layer_forward(self, x, W_router, W_gate_up, W_down, k, S=0, bias=None,
-                      tokens=None, forced_idx=None):
+                      tokens=None, forced_idx=None, capacity=None):
         """Whole layer.  Returns (y[n,d] f64, idx[n,k] i32, w[n,k] f64) for the
-        listed tokens (all tokens when tokens is None)."""
+        listed tokens (all tokens when tokens is None).  capacity: None or the
+        most copies one expert keeps."""
         x = _c(x)
         W_router = _c(W_router)
         W_gate_up = _c(W_gate_up)
@@ -187,6 +223,7 @@ class Oracle:
         rc = self.L.oracle_layer_forward(T, d, f, E, k, S, dt, _p(x), _p(W_router),
                                          _p(b, _f32p), _p(W_gate_up), _p(W_down), n,
                                          _p(tl, _i64p), _p(fi, _i32p),
+                                         -1 if capacity is None else int(capacity),
                                          _p(idx, _i32p), _p(w, _f64p), _p(y, _f64p))
         _check(rc, "oracle_layer_forward")
         return y, idx, w
@@ -231,3 +268,11 @@ def combine(*a, **kw):
 
 def layer_forward(*a, **kw):
     return default().layer_forward(*a, **kw)
+
+
+def expert_capacity(*a, **kw):
+    return default().expert_capacity(*a, **kw)
+
+
+def balance(*a, **kw):
+    return default().balance(*a, **kw)

@@ -138,37 +138,161 @@ int oracle_route(int64_t T, int64_t d, int64_t E, int64_t k, int dt,
 
 /* ------------------------------------------------------------ permutation */
 
-int oracle_permute(int64_t T, int64_t k, int64_t E, int64_t S,
-                   const int32_t* idx, int32_t* counts, int32_t* offsets,
-                   int32_t* sorted_slot, int32_t* slot_pos) {
+/* Counting-sort permutation of the T*k token copies by expert id, with an
+ * optional expert capacity (capacity < 0: none).
+ *
+ * Expert capacity: every expert accepts at most `capacity` token copies and
+ * the overflow is dropped (yunthe "分工的艺术" page, section 3.1, expert
+ * capacity; Baidu page, section 三.2, capacity-constrained token dropping;
+ * yunthe page, sections 4.1 and 5.2, capacity factor).  Readings: an expert
+ * keeps its first `capacity` copies in slot order s = t*k + j (earlier
+ * tokens first); a dropped copy adds nothing to its token's output and the
+ * kept weights are not renormalised.
+ *
+ * Row layout of the permuted buffers:
+ *   rows [0, D)        the D dropped copies, by expert id, ascending slot
+ *                      inside one expert; their slot_pos is -1;
+ *   rows offsets[e] .. offsets[e] + counts[e]
+ *                      the copies expert e keeps, ascending slot;
+ *                      counts[e] = min(copies of e, capacity);
+ *   offsets[0] = D, offsets[E] = T*k; shared expert sigma: T rows from
+ *   T*k + sigma*T, token order. */
+int oracle_permute_capacity(int64_t T, int64_t k, int64_t E, int64_t S,
+                            int64_t capacity, const int32_t* idx,
+                            int32_t* counts, int32_t* offsets,
+                            int32_t* sorted_slot, int32_t* slot_pos) {
   if (T < 0 || k < 1 || E < 1 || S < 0) return -1;
   if (!counts || !offsets || (T > 0 && (!idx || !sorted_slot || !slot_pos)))
     return -1;
   int64_t n = T * k;
   for (int64_t s = 0; s < n; ++s)
     if (idx[s] < 0 || idx[s] >= E) return -1;
+  int64_t cap = capacity < 0 || capacity > n ? n : capacity;
 
-  /* histogram of the routed copies; every shared expert takes all T tokens */
-  for (int64_t e = 0; e < E + S; ++e) counts[e] = 0;
-  for (int64_t s = 0; s < n; ++s) counts[idx[s]] += 1;
+  /* copies per expert, then what each keeps and drops */
+  int64_t* total = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+  int64_t* drop_base = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+  int64_t* seen = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+  if (!total || !drop_base || !seen) {
+    free(total);
+    free(drop_base);
+    free(seen);
+    return -2;
+  }
+  for (int64_t s = 0; s < n; ++s) total[idx[s]] += 1;
+  int64_t dropped = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    int64_t kept = total[e] < cap ? total[e] : cap;
+    counts[e] = (int32_t)kept;
+    drop_base[e] = dropped;
+    dropped += total[e] - kept;
+  }
+  /* every shared expert takes all T tokens */
   for (int64_t sg = 0; sg < S; ++sg) counts[E + sg] = (int32_t)T;
 
-  /* exclusive prefix sum */
-  offsets[0] = 0;
+  /* exclusive prefix sum of the kept counts, after the dropped rows */
+  offsets[0] = (int32_t)dropped;
   for (int64_t e = 0; e < E + S; ++e) offsets[e + 1] = offsets[e] + counts[e];
 
   /* stable scatter: slots visited in ascending order */
-  int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
-  if (!fill) return -2;
   for (int64_t s = 0; s < n; ++s) {
     int32_t e = idx[s];
-    int32_t pos = offsets[e] + fill[e];
-    fill[e] += 1;
+    int64_t r = seen[e]++; /* earlier copies of expert e */
+    int64_t pos;
+    if (r < cap) {
+      pos = offsets[e] + r;
+      slot_pos[s] = (int32_t)pos;
+    } else {
+      pos = drop_base[e] + (r - cap);
+      slot_pos[s] = -1;
+    }
     sorted_slot[pos] = (int32_t)s;
-    slot_pos[s] = pos;
   }
-  free(fill);
+  free(total);
+  free(drop_base);
+  free(seen);
   return 0;
+}
+
+int oracle_permute(int64_t T, int64_t k, int64_t E, int64_t S,
+                   const int32_t* idx, int32_t* counts, int32_t* offsets,
+                   int32_t* sorted_slot, int32_t* slot_pos) {
+  return oracle_permute_capacity(T, k, E, S, -1, idx, counts, offsets,
+                                 sorted_slot, slot_pos);
+}
+
+int64_t oracle_expert_capacity(int64_t T, int64_t k, int64_t E,
+                               double factor) {
+  /* capacity factor times the even share T*k/E of one expert, rounded up */
+  if (T < 0 || k < 1 || E < 1 || !(factor >= 0.0)) return -1;
+  return (int64_t)ceil(factor * (double)(T * k) / (double)E);
+}
+
+/* -------------------------------------------------------- balance loss */
+
+/* Load-balance statistics of the router (yunthe page, section 3.1, the load
+ * balance loss example; the gate it averages is the softmax over all experts
+ * of that page's section 1.1 gating code):
+ *   probs[t, e]    = softmax over the E experts of token t's logits
+ *                    (logits as in routing, bias included);
+ *   importance[e]  = mean over the T tokens of probs[t, e]
+ *                    (T = 0: 0/0, NaN);
+ *   loss           = KL divergence of the uniform target u = 1/E from
+ *                    log(importance + 1e-8), batch-mean reduced over the
+ *                    E-long input, i.e.
+ *                    (1/E) * sum_e u * (log u - log(importance[e] + 1e-8)).
+ * probs ([T, E]) is optional. */
+int oracle_balance(int64_t T, int64_t d, int64_t E, int dt, const void* x,
+                   const void* W_router, const float* bias, double* probs,
+                   double* importance, double* loss) {
+  if (T < 0 || d < 1 || E < 1 || bad_dt(dt)) return -1;
+  if (!importance || !loss || (T > 0 && (!x || !W_router))) return -1;
+  double* P = probs;
+  if (!P && T > 0) {
+    P = (double*)malloc(sizeof(double) * (size_t)(T * E));
+    if (!P) return -2;
+  }
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* xt = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!xt) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t t = 0; t < T; ++t) {
+        double* pt = P + t * E;
+        for (int64_t i = 0; i < d; ++i) xt[i] = elem(x, dt, t * d + i);
+        for (int64_t e = 0; e < E; ++e) {
+          pt[e] = dot_row(W_router, dt, e, d, xt);
+          if (bias) pt[e] += (double)bias[e];
+        }
+        double m = pt[0];
+        for (int64_t e = 1; e < E; ++e)
+          if (pt[e] > m) m = pt[e];
+        double z = 0.0;
+        for (int64_t e = 0; e < E; ++e) z += exp(pt[e] - m);
+        for (int64_t e = 0; e < E; ++e) pt[e] = exp(pt[e] - m) / z;
+      }
+    }
+    free(xt);
+  }
+  if (!fail) {
+    /* mean over tokens, summed in token order */
+    for (int64_t e = 0; e < E; ++e) {
+      double s = 0.0;
+      for (int64_t t = 0; t < T; ++t) s += P[t * E + e];
+      importance[e] = s / (double)T;
+    }
+    double u = 1.0 / (double)E;
+    double kl = 0.0;
+    for (int64_t e = 0; e < E; ++e)
+      kl += u * (log(u) - log(importance[e] + 1e-8));
+    *loss = kl / (double)E;
+  }
+  if (P != probs) free(P);
+  return fail ? -2 : 0;
 }
 
 /* ------------------------------------------------------------ expert FFN */
@@ -275,10 +399,12 @@ int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
                          const float* bias, const void* W_gate_up,
                          const void* W_down, int64_t n_tok,
                          const int64_t* tok_list, const int32_t* forced_idx,
-                         int32_t* idx_out, double* w_out, double* y) {
+                         int64_t capacity, int32_t* idx_out, double* w_out,
+                         double* y) {
   if (T < 0 || d < 1 || f < 1 || E < 1 || k < 1 || k > E || S < 0 ||
       bad_dt(dt))
     return -1;
+  if (capacity >= 0 && forced_idx) return -1;
   if (!tok_list) n_tok = T;
   if (n_tok < 0) return -1;
   if (n_tok > 0 && (!x || !W_router || !W_gate_up || !W_down || !y)) return -1;
@@ -288,6 +414,30 @@ int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
   if (forced_idx)
     for (int64_t q = 0; q < n_tok * k; ++q)
       if (forced_idx[q] < 0 || forced_idx[q] >= E) return -1;
+
+  /* with an expert capacity, whether a copy is kept depends on the copies
+   * of every earlier token: route all tokens first, then walk the copies in
+   * slot order, each expert keeping its first `capacity` (the reading of
+   * oracle_permute_capacity) */
+  uint8_t* keep = NULL;
+  if (capacity >= 0 && T > 0) {
+    int32_t* idx_all = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
+    double* w_all = (double*)malloc(sizeof(double) * (size_t)(T * k));
+    int64_t* seen = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    keep = (uint8_t*)malloc((size_t)(T * k));
+    int rc = (idx_all && w_all && seen && keep) ? 0 : -2;
+    if (rc == 0)
+      rc = oracle_route(T, d, E, k, dt, x, W_router, bias, NULL, idx_all, w_all);
+    if (rc == 0)
+      for (int64_t s = 0; s < T * k; ++s) keep[s] = seen[idx_all[s]]++ < capacity;
+    free(idx_all);
+    free(w_all);
+    free(seen);
+    if (rc != 0) {
+      free(keep);
+      return rc;
+    }
+  }
 
   int fail = 0;
 #pragma omp parallel
@@ -312,8 +462,10 @@ int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
         /* route_token leaves x[t] widened in xt */
         double* yt = y + q * d;
         for (int64_t i = 0; i < d; ++i) yt[i] = 0.0;
-        /* y_t = sum_j w_j Expert_{idx_j}(x_t): selected experts only */
+        /* y_t = sum_j w_j Expert_{idx_j}(x_t): selected experts only (and
+         * of those, the copies their expert keeps) */
         for (int64_t j = 0; j < k; ++j) {
+          if (keep && !keep[t * k + j]) continue;
           expert_hidden(idx[j], d, f, dt, W_gate_up, xt, act);
           expert_down(idx[j], d, f, dt, W_down, act, out);
           for (int64_t i = 0; i < d; ++i) yt[i] += w[j] * out[i];
@@ -336,5 +488,6 @@ int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
     free(idx);
     free(w);
   }
+  free(keep);
   return fail ? -2 : 0;
 }

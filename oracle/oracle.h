@@ -35,7 +35,12 @@
  *     weight tensors, weight 1 for every token, outside the softmax;
  *   - permutation order inside one expert group: ascending slot id
  *     s = t*k + j (stable counting sort); shared groups follow the routed ones
- *     with rows T*k + sigma*T + t.
+ *     with rows T*k + sigma*T + t;
+ *   - expert capacity (optional): an expert keeps its first `capacity`
+ *     copies in slot order, dropped copies add nothing, kept weights are not
+ *     renormalised;
+ *   - balance loss: the gate averaged over tokens is the dense softmax over
+ *     all experts (bias included).
  *
  * Element types: dt = ORACLE_F32 (IEEE binary32) or ORACLE_BF16 (bfloat16,
  * passed as its raw 16-bit pattern).  Every value is widened to fp64 before
@@ -68,6 +73,26 @@ int oracle_permute(int64_t T, int64_t k, int64_t E, int64_t S,
                    const int32_t* idx, int32_t* counts, int32_t* offsets,
                    int32_t* sorted_slot, int32_t* slot_pos);
 
+/* The same with an expert capacity (capacity < 0: none): every expert keeps
+ * its first `capacity` copies in slot order, the rest are dropped.  Rows
+ * [0, D) of the permutation hold the D dropped copies (by expert id, then
+ * slot) with slot_pos = -1; kept copies follow, offsets[0] = D,
+ * offsets[E] = T*k, counts[e] = copies kept by expert e. */
+int oracle_permute_capacity(int64_t T, int64_t k, int64_t E, int64_t S,
+                            int64_t capacity, const int32_t* idx,
+                            int32_t* counts, int32_t* offsets,
+                            int32_t* sorted_slot, int32_t* slot_pos);
+
+/* Capacity from a capacity factor: ceil(factor * T*k / E); -1 if invalid. */
+int64_t oracle_expert_capacity(int64_t T, int64_t k, int64_t E, double factor);
+
+/* Router load statistics: probs[T,E] (optional) = softmax over all experts
+ * of each token's logits, importance[E] = its mean over tokens, and the
+ * KL-to-uniform balance loss (1/E) sum_e (1/E)(log(1/E) - log(imp_e + 1e-8)). */
+int oracle_balance(int64_t T, int64_t d, int64_t E, int dt, const void* x,
+                   const void* W_router, const float* bias, double* probs,
+                   double* importance, double* loss);
+
 /* SwiGLU hidden activation of n (token, expert) pairs:
  * act[r, :] = silu(Wgu[e, 0:f, :] x[t]) * (Wgu[e, f:2f, :] x[t]),
  * with t = tok[r], e = expert[r].  act is [n, f] fp64. */
@@ -91,13 +116,16 @@ int oracle_combine(int64_t T, int64_t k, int64_t S, int64_t d, int dt,
  * order).  y is [n_tok, d] fp64; idx_out / w_out ([n_tok, k], optional) get
  * the routing.  forced_idx ([n_tok, k], optional) replaces the selection by
  * the given expert ids; their weights are then the softmax over the given
- * experts' logits. */
+ * experts' logits.  capacity >= 0 applies an expert capacity (as in
+ * oracle_permute_capacity; dropped copies add nothing); it cannot be
+ * combined with forced_idx. */
 int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
                          int64_t S, int dt, const void* x, const void* W_router,
                          const float* bias, const void* W_gate_up,
                          const void* W_down, int64_t n_tok,
                          const int64_t* tok_list, const int32_t* forced_idx,
-                         int32_t* idx_out, double* w_out, double* y);
+                         int64_t capacity, int32_t* idx_out, double* w_out,
+                         double* y);
 
 /* Number of OpenMP threads the oracle uses (for reporting). */
 int oracle_num_threads(void);

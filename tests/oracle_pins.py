@@ -419,4 +419,150 @@ def pin_forced_other_selection(orc):
         assert rel_err(y, y_ref) <= 1e-12, rel_err(y, y_ref)
 
 
+# ------------------------------------------- router auxiliaries (capacity, balance)
+
+def brute_capacity(idx, E, S, C):
+    """Independent construction of the capacity permutation by sorting: a
+    copy is kept when fewer than C earlier copies (smaller slot) chose its
+    expert; dropped copies first (by expert, then slot), then the kept ones
+    (by expert, then slot)."""
+    flat = [int(v) for v in np.asarray(idx).ravel()]
+    n = len(flat)
+    T = np.asarray(idx).shape[0]
+    kept = [sum(1 for q in range(s) if flat[q] == flat[s]) < C for s in range(n)]
+    dropped = sorted((flat[s], s) for s in range(n) if not kept[s])
+    keep_list = sorted((flat[s], s) for s in range(n) if kept[s])
+    order = [s for _, s in dropped] + [s for _, s in keep_list]
+    counts = [sum(1 for (e, _) in keep_list if e == g) for g in range(E)] + [T] * S
+    offsets = [len(dropped)]
+    for c in counts:
+        offsets.append(offsets[-1] + c)
+    slot_pos = [-1] * n
+    for r, s in enumerate(order):
+        if kept[s]:
+            slot_pos[s] = r
+    return (np.array(counts, np.int32), np.array(offsets, np.int32),
+            np.array(order, np.int32), np.array(slot_pos, np.int32),
+            np.array(kept, bool).reshape(np.asarray(idx).shape))
+
+
+def pin_capacity_permutation(orc):
+    """Expert capacity (yunthe page, section 3.1): brute-force construction
+    on small inputs, the no-limit and zero-capacity special cases."""
+    rng = np.random.default_rng([40, 5, 0])
+    for (T, k, E, S) in ((30, 3, 5, 0), (17, 2, 9, 1), (1, 1, 1, 0), (24, 4, 4, 2),
+                         (0, 2, 3, 1)):
+        if T:
+            # skewed choice: low experts far more popular
+            idx = np.stack([rng.choice(E, k, replace=False, p=np.arange(E, 0, -1) / (E * (E + 1) / 2))
+                            for _ in range(T)]).astype(np.int32)
+        else:
+            idx = np.zeros((0, k), np.int32)
+        free = orc.permute(idx, E, S)
+        for C in (0, 1, 2, 5, T, T * k + 3):
+            got = orc.permute(idx, E, S, capacity=C)
+            ref = brute_capacity(idx, E, S, C)
+            for a, b, name in zip(got, ref[:4], ("counts", "offsets", "sorted_slot", "slot_pos")):
+                assert np.array_equal(a, b), (T, k, E, S, C, name)
+            assert got[1][E] == T * k and got[1][E + S] == T * k + S * T
+            assert np.all(got[0][:E] <= C)
+            if C >= T:
+                for a, b in zip(got, free):
+                    assert np.array_equal(a, b)
+            if C == 0:
+                assert np.all(got[3] == -1) and np.all(got[0][:E] == 0)
+
+
+def pin_expert_capacity(orc):
+    """Capacity from a factor: ceil(factor * T*k / E) (yunthe page, sections
+    4.1 and 5.2: the factor scales an expert's even share of the tokens)."""
+    assert orc.expert_capacity(4096, 8, 128, 1.25) == 320
+    assert orc.expert_capacity(10, 2, 3, 1.0) == 7
+    assert orc.expert_capacity(4096, 8, 256, 1.0) == 128
+    assert orc.expert_capacity(7, 1, 4, 0.0) == 0
+    assert orc.expert_capacity(8192, 2, 8, 2.0) == 4096
+
+
+def pin_capacity_layer(orc):
+    """The layer with a capacity equals the dense numpy formulation with the
+    dropped copies' terms removed and the kept weights unchanged; a capacity
+    of at least T changes nothing; capacity 0 leaves the shared experts."""
+    for (T, d, f, E, k, S, dt, seed) in ((24, 8, 6, 4, 2, 0, "f32", 41),
+                                         (20, 8, 8, 5, 3, 1, "bf16", 42)):
+        x, Wr, Wgu, Wd = rand_layer(seed, T, d, f, E, k, S, dt)
+        bias = np.linspace(0.8, -0.8, E).astype(np.float32)  # skewed load
+        _, idx, w, _ = np_dense_layer(x, Wr, Wgu, Wd, k, S=S, bias=bias)
+        xd, Wgud, Wdd = wide(x), wide(Wgu), wide(Wd)
+        outs = np.stack([(np_silu(xd @ Wgud[e, :f].T) * (xd @ Wgud[e, f:].T)) @ Wdd[e].T
+                         for e in range(E + S)])
+        y_free, _, _ = orc.layer_forward(x, Wr, Wgu, Wd, k, S=S, bias=bias)
+        for C in (0, 3, 7, T):
+            keep = brute_capacity(idx, E, S, C)[4]
+            y_ref = np.zeros((T, d))
+            for t in range(T):
+                for j in range(k):
+                    if keep[t, j]:
+                        y_ref[t] += w[t, j] * outs[idx[t, j], t]
+                y_ref[t] += sum(outs[E + s, t] for s in range(S))
+            y, idx_o, w_o = orc.layer_forward(x, Wr, Wgu, Wd, k, S=S, bias=bias, capacity=C)
+            assert np.array_equal(idx_o, idx)
+            assert rel_err(y, y_ref) <= 1e-12, (C, rel_err(y, y_ref))
+            if C >= T:
+                assert np.array_equal(y, y_free)
+            if C == 0:
+                shared = sum((outs[E + s] for s in range(S)), np.zeros((T, d)))
+                assert rel_err(y, shared) <= 1e-12 if S else np.all(y == 0.0)
+
+
+def pin_balance_closed_forms(orc):
+    """Balance loss (yunthe page, section 3.1): a zero router gives every
+    expert probability 1/E, so importance = 1/E and the loss is
+    -(1/E) log1p(E * 1e-8); a +1000 bias on one expert gives importance =
+    that expert's unit vector and the loss in closed form; no tokens: NaN."""
+    for (T, d, E, dt) in ((13, 8, 6, "f32"), (5, 16, 32, "bf16")):
+        x = moe_synth.normal((43, 5, T), (T, d), 1.0, dt)
+        Wr = np.zeros((E, d), np.float32 if dt == "f32" else np.uint16)
+        imp, loss = orc.balance(x, Wr)
+        assert np.max(np.abs(imp - 1.0 / E)) <= 1e-16
+        # the oracle's log(u) - log(u + 1e-8) cancels: a few ulps of log(u)
+        assert abs(loss - (-math.log1p(E * 1e-8) / E)) <= 4e-16 * abs(math.log(1.0 / E))
+        bias = np.zeros(E, np.float32)
+        bias[2] = 1000.0
+        Wr2 = moe_synth.normal((43, 6, T), (E, d), 0.3, dt)
+        imp, loss = orc.balance(x, Wr2, bias=bias)
+        assert imp[2] == 1.0 and np.all(np.delete(imp, 2) == 0.0)
+        u = 1.0 / E
+        ref = (u * (math.log(u) - math.log(1.0 + 1e-8))
+               + (E - 1) * u * (math.log(u) - math.log(1e-8))) / E
+        assert abs(loss - ref) <= 1e-13 * abs(ref)
+    imp, loss = orc.balance(np.zeros((0, 8), np.float32), np.ones((3, 8), np.float32))
+    assert np.all(np.isnan(imp)) and math.isnan(loss)
+
+
+def pin_balance_library(orc):
+    """Balance statistics against library routines on a random router:
+    importance = mean of scipy's softmax of numpy-matmul logits (bias added),
+    loss = torch.nn.functional.kl_div(log(importance + 1e-8), uniform,
+    reduction='batchmean'), the form the yunthe page's section 3.1 example
+    writes.  The importance sums to one."""
+    import scipy.special
+    import torch
+    for (T, d, E, dt, seed) in ((40, 16, 8, "f32", 44), (33, 24, 20, "bf16", 45)):
+        x = moe_synth.normal((seed, 5, 0), (T, d), 1.0, dt)
+        Wr = moe_synth.normal((seed, 5, 1), (E, d), 0.4, dt)
+        bias = np.linspace(0.5, -1.0, E).astype(np.float32)
+        imp, loss, probs = orc.balance(x, Wr, bias=bias, want_probs=True)
+        L = wide(x) @ wide(Wr).T + bias.astype(np.float64)[None, :]
+        p_ref = scipy.special.softmax(L, axis=1)
+        assert rel_err(probs, p_ref) <= 1e-13
+        assert rel_err(imp, p_ref.mean(0)) <= 1e-13
+        assert abs(imp.sum() - 1.0) <= 1e-13
+        ref = torch.nn.functional.kl_div(torch.log(torch.tensor(imp) + 1e-8),
+                                         torch.full((E,), 1.0 / E, dtype=torch.float64),
+                                         reduction="batchmean").item()
+        assert abs(loss - ref) <= 1e-12 * abs(ref), (loss, ref)
+        # the loss is KL(u || imp) / E up to the 1e-8 guard: zero only at uniform
+        assert loss > 0
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -2,6 +2,7 @@
 algorithmic byte / flop counts it divides by, and the rule that committed
 HBM traffic counters only count while the kernel they measured is unchanged."""
 import importlib.util
+import hashlib
 import json
 import os
 import subprocess
@@ -51,12 +52,20 @@ def test_algorithmic_counts_by_hand():
 
 def test_traffic_only_while_the_kernel_is_unchanged(tmp_path, monkeypatch):
     b = _bench()
-    data = json.load(open(b.TRAFFIC_FILE))
-    ent = data["gpt_oss_20b_decode"]
-    assert b.load_traffic("gpt_oss_20b_decode") == ent["bytes_per_launch"]
+    src_hash = hashlib.sha256(open(b.GEMM_SRC, "rb").read()).hexdigest()[:16]
+    tf = tmp_path / "traffic.json"
+    tf.write_text(json.dumps({"w": {"bytes_per_launch": 123,
+                                    "gemm_src_sha256_16": src_hash}}))
+    monkeypatch.setattr(b, "TRAFFIC_FILE", str(tf))
+    assert b.load_traffic("w") == 123
     assert b.load_traffic("no_such_workload") is None
-    # a changed kernel source invalidates the committed counters
+    # a changed kernel source invalidates the stored counters
     src = tmp_path / "gemm_stream.hip"
     src.write_bytes(open(b.GEMM_SRC, "rb").read() + b"\n// changed\n")
     monkeypatch.setattr(b, "GEMM_SRC", str(src))
-    assert b.load_traffic("gpt_oss_20b_decode") is None
+    assert b.load_traffic("w") is None
+    # the committed file parses and names the kernel it was taken on
+    data = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    for ent in data.values():
+        assert ent["bytes_per_launch"] > 0 and len(ent["gemm_src_sha256_16"]) == 16
+

@@ -43,6 +43,33 @@ MUTANTS = {
     "unstable_scatter": (
         "for (int64_t s = 0; s < n; ++s) {\n    int32_t e = idx[s];",
         "for (int64_t s = n - 1; s >= 0; --s) {\n    int32_t e = idx[s];"),
+    # capacity: the dropped rows listed in reverse
+    "capacity_dropped_rows_reversed": (
+        "pos = drop_base[e] + (r - cap);",
+        "pos = (dropped - 1) - (drop_base[e] + (r - cap));"),
+    # capacity: dropped rows not skipped by the group offsets
+    "capacity_groups_start_at_zero": (
+        "offsets[0] = (int32_t)dropped;", "offsets[0] = 0;"),
+    # layer with capacity: dropped copies still contribute
+    "capacity_ignored_in_layer": (
+        "if (keep && !keep[t * k + j]) continue;", "(void)keep;"),
+    # balance: sum over tokens instead of the mean
+    "balance_sum_not_mean": (
+        "importance[e] = s / (double)T;", "importance[e] = s;"),
+    # balance: no batch-mean division of the KL sum
+    "balance_no_batchmean": (
+        "*loss = kl / (double)E;", "*loss = kl;"),
+    # balance: the 1e-8 guard left out of the log
+    "balance_no_guard": (
+        "kl += u * (log(u) - log(importance[e] + 1e-8));",
+        "kl += u * (log(u) - log(importance[e]));"),
+    # balance: softmax without the bias
+    "balance_bias_ignored": (
+        "if (bias) pt[e] += (double)bias[e];", "(void)bias;"),
+    # balance: KL with its arguments swapped
+    "balance_kl_reversed": (
+        "kl += u * (log(u) - log(importance[e] + 1e-8));",
+        "kl += importance[e] * (log(importance[e] + 1e-8) - log(u));"),
     "bf16_shift_wrong": (
         "uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 16;",
         "uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 15;"),
