@@ -12,7 +12,9 @@ same interval also measured by HIP events on the stream the kernels run
 on), the roofline of the dominant kernel (the gate_up grouped GEMM), the
 fp64 CPU oracle's rate on the host cores, and, under "prefill", the same
 layer measurement for the Mixtral-8x7B-shaped prefill workload against the
-bf16 MFMA peak.
+bf16 MFMA peak.  Each workload also reports, under layer.aux, the router
+auxiliaries: routing with the balance statistics against routing alone, and
+the layer with an expert capacity of 1.25 times the even share.
 """
 import argparse
 import hashlib
@@ -202,6 +204,34 @@ class Layer:
                 s, v["expert_out"], v["slot_pos"], v["topk_w"], self.y), n),
         }
 
+    def aux_times(self, torch, n, factor=1.25):
+        """The router auxiliaries on this workload: moe_route_balance (routing
+        plus importance and balance loss) against moe_route, and the layer
+        with an expert capacity of `factor` times the even share."""
+        moe, s, d, v, cfg = self.moe, self.s, self.d, self.views, self.cfg
+        ws_b = torch.empty(max(1, moe.route_balance_workspace_size(s)), dtype=torch.uint8,
+                           device="cuda")
+        imp = torch.empty(cfg.E, dtype=torch.float64, device="cuda")
+        loss = torch.empty(1, dtype=torch.float64, device="cuda")
+        cap = moe.expert_capacity(cfg.T, cfg.k, cfg.E, factor)
+        ws_c = torch.empty_like(self.ws)
+        y_c = torch.empty_like(self.y)
+        t_route = time_calls(torch, lambda: moe.moe_route(
+            s, d["x"], d["W_router"], d["bias"], v["topk_idx"], v["topk_w"]), n)
+        t_bal = time_calls(torch, lambda: moe.moe_route_balance(
+            s, d["x"], d["W_router"], d["bias"], v["topk_idx"], v["topk_w"], imp, loss, ws_b),
+            n)
+        t_cap = time_calls(torch, lambda: moe.moe_layer_forward_capacity(
+            s, d["x"], d["W_router"], d["bias"], self.w_gu[0], self.w_dn[0], cap, y_c, ws_c),
+            n)
+        kept = int(moe.workspace_views(s, ws_c)["counts"][:cfg.E].sum().item())
+        return {"route_us": round(t_route * 1e6, 2),
+                "route_balance_us": round(t_bal * 1e6, 2),
+                "balance_loss": float(loss.item()),
+                "capacity_factor": factor, "capacity": cap,
+                "copies_kept": kept, "copies": cfg.T * cfg.k,
+                "layer_capacity_ms": round(t_cap * 1e3, 4)}
+
     def timed_steps(self, torch, steps):
         """Exactly `steps` layer calls between two synchronisations: wall
         clock, and HIP events recorded on the stream the calls enqueue on."""
@@ -266,6 +296,7 @@ def prefill_extra(torch, moe, steps, no_cpu):
     kt = L.kernel_times(torch, 5)
     wall, ev = L.timed_steps(torch, steps)
     ac, roof, layer = L.summary(torch, kt, ev / steps)
+    layer["aux"] = L.aux_times(torch, 5)
     out = {"workload": cfg.name, "steps": steps,
            "ms_per_step": round(wall / steps * 1e3, 4),
            "ms_per_step_hip_events": round(ev / steps * 1e3, 4),
@@ -317,6 +348,7 @@ def main(argv=None):
     layer["ms_per_step_hip_events"] = round(ev / args.steps * 1e3, 4)
     layer["hbm_frac_hip_events"] = round(ac["layer_bytes"] / (ev / args.steps) / 1e9
                                          / HBM_PEAK_GBS, 4)
+    layer["aux"] = L.aux_times(torch, max(20, min(args.steps, 100)))
 
     out = {
         "metric": "MoE layer tokens/s",

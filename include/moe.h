@@ -114,6 +114,32 @@ int moe_route(const moe_shape* s, const void* x, const void* W_router,
               const float* bias, int32_t* topk_idx, float* topk_w,
               void* stream);
 
+/* ------------------------------------------------- router load statistics
+ * moe_route_balance: moe_route plus the router's load statistics and the
+ * load-balance loss (yunthe "分工的艺术" page, section 3.1, load balance
+ * loss: the gate averaged over the batch, compared with the uniform
+ * distribution by KL divergence, batch-mean reduced; the gate is the
+ * softmax over all experts, that page's section 1.1 gating code).
+ *   topk_idx, topk_w  as moe_route (same values)
+ *   importance [E] float64 out: imp_e = (1/T) sum_t softmax(L_t)_e, the
+ *              softmax over all E experts of token t's logits (bias
+ *              included); T = 0 gives NaN
+ *   loss       [1] float64 out:
+ *              (1/E) sum_e (1/E) (log(1/E) - log(imp_e + 1e-8))
+ *   workspace  device memory of moe_route_balance_workspace_size(s) bytes,
+ *              256-byte aligned (the logits and per-block partial sums)
+ * Numerics: the logits enter the softmax rounded to fp32; every expert that
+ * can be selected has its exact fp64 logit, and on the bf16 screen path
+ * (more than 64 tokens) the others have the screen's estimate, within
+ * 2^-14 * ||x_t|| * ||w_e|| of the exact logit.  exp in fp32, sums in fp64 in
+ * a fixed order (repeated calls are bitwise identical). */
+size_t moe_route_balance_workspace_size(const moe_shape* s);
+
+int moe_route_balance(const moe_shape* s, const void* x, const void* W_router,
+                      const float* bias, int32_t* topk_idx, float* topk_w,
+                      double* importance, double* loss, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ step 3
  * moe_permute: group the T*k token copies by expert.
  * Copy s = t*k + j goes to expert topk_idx[s].
@@ -127,13 +153,37 @@ int moe_route(const moe_shape* s, const void* x, const void* W_router,
  *               sigma, token t) are implicit and not stored.
  *   slot_pos    [T*k]   int32 out: inverse map, row of copy s
  * topk_idx entries should lie in [0, E).  A copy whose id lies outside it
- * selects no expert: it is listed after all routed copies (rows up to T*k,
- * inside the last expert's row range offsets[E-1] .. offsets[E] = T*k,
- * though not in that expert's count) and gets slot_pos = -1, which
- * moe_combine skips. */
+ * selects no expert: it is dropped.  Dropped copies take the first rows,
+ * [0, D), in slot order, with slot_pos = -1, which moe_combine skips; the
+ * expert groups follow (offsets[0] = D, counts exclude them), so no group
+ * holds a dropped row, and offsets[E] = T*k still. */
 int moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* counts,
                 int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
                 void* stream);
+
+/* moe_permute_capacity: moe_permute with an expert capacity: every expert
+ * keeps at most `capacity` copies and drops the rest (yunthe page, section
+ * 3.1, expert capacity; Baidu page, section 三.2, capacity-bound token
+ * dropping).  Reading: an expert keeps its first `capacity` copies in slot
+ * order s = t*k + j (earlier tokens first); a dropped copy adds nothing to
+ * its token's output; the kept weights are not renormalised.
+ *   capacity   >= 0 (MOE_ERR_INVALID_ARG otherwise); capacity >= T keeps
+ *              every copy of a router's output (moe_permute's result)
+ *   counts[e]  copies expert e keeps, min(copies of e, capacity)
+ * Dropped rows [0, D): first the copies with ids outside [0, E) (slot
+ * order), then the copies over capacity, by expert id, slot order inside
+ * one expert; slot_pos = -1.  Kept rows: group e is offsets[e] ..
+ * offsets[e+1], ascending slot; offsets[0] = D, offsets[E] = T*k. */
+int moe_permute_capacity(const moe_shape* s, const int32_t* topk_idx,
+                         int64_t capacity, int32_t* counts, int32_t* offsets,
+                         int32_t* sorted_slot, int32_t* slot_pos, void* stream);
+
+/* Capacity from a capacity factor (yunthe page, sections 4.1 and 5.2: the
+ * factor, typically 1.0 to 2.0, scales an expert's even share of the
+ * copies): ceil(capacity_factor * T * k / E).  Host only, no HIP call.
+ * Returns -1 for T < 0, k < 1, E < 1 or a factor outside [0, 1e9]. */
+int64_t moe_expert_capacity(int64_t T, int64_t k, int64_t E,
+                            double capacity_factor);
 
 /* ------------------------------------------------------------------ step 4
  * moe_grouped_gemm_gate_up: first expert GEMM with the SwiGLU epilogue.
@@ -204,6 +254,16 @@ int moe_layer_forward(const moe_shape* s, const void* x, const void* W_router,
                       const float* bias, const void* W_gate_up,
                       const void* W_down, void* y, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* moe_layer_forward_capacity: the layer with an expert capacity (step 3 is
+ * moe_permute_capacity; dropped copies add nothing to y; shared experts are
+ * not limited).  capacity >= 0; workspace as moe_layer_forward (same size
+ * and layout). */
+int moe_layer_forward_capacity(const moe_shape* s, const void* x,
+                               const void* W_router, const float* bias,
+                               const void* W_gate_up, const void* W_down,
+                               int64_t capacity, void* y, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------- whole layer, no allocation
  * moe_layer_forward_static: moe_layer_forward with the intermediates in a

@@ -33,7 +33,10 @@ WS_NAMES = ("topk_idx", "topk_w", "counts", "offsets", "sorted_slot", "slot_pos"
 ENTRY_POINTS = ("moe_status_string", "moe_version", "moe_last_hip_error", "moe_route", "moe_permute",
                 "moe_grouped_gemm_gate_up", "moe_grouped_gemm_down", "moe_grouped_gemm",
                 "moe_combine", "moe_workspace_size", "moe_workspace_offsets",
-                "moe_layer_forward", "moe_layer_forward_static")
+                "moe_layer_forward", "moe_layer_forward_static",
+                "moe_route_balance_workspace_size", "moe_route_balance",
+                "moe_permute_capacity", "moe_expert_capacity",
+                "moe_layer_forward_capacity")
 
 # size of the library's static intermediate array (include/moe.h)
 STATIC_SCRATCH_BYTES = 32 << 20
@@ -82,6 +85,11 @@ def _load():
     L.moe_workspace_size.argtypes = [sp]
     L.moe_workspace_size.restype = ctypes.c_size_t
     L.moe_workspace_offsets.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_route_balance_workspace_size.argtypes = [sp]
+    L.moe_route_balance_workspace_size.restype = ctypes.c_size_t
+    i64 = ctypes.c_int64
+    L.moe_expert_capacity.argtypes = [i64, i64, i64, ctypes.c_double]
+    L.moe_expert_capacity.restype = i64
     sigs = {
         "moe_route": [sp, vp, vp, vp, vp, vp, vp],
         "moe_permute": [sp, vp, vp, vp, vp, vp, vp],
@@ -91,6 +99,10 @@ def _load():
         "moe_combine": [sp, vp, vp, vp, vp, vp],
         "moe_layer_forward": [sp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "moe_layer_forward_static": [sp, vp, vp, vp, vp, vp, vp, vp],
+        "moe_route_balance": [sp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "moe_permute_capacity": [sp, vp, i64, vp, vp, vp, vp, vp],
+        "moe_layer_forward_capacity": [sp, vp, vp, vp, vp, vp, i64, vp, vp, ctypes.c_size_t,
+                                       vp],
     }
     for name, argtypes in sigs.items():
         fn = getattr(L, name)
@@ -125,6 +137,15 @@ def shape(T, d, f, E, k, n_shared=0, dt=MOE_DT_BF16) -> moe_shape:
 
 def workspace_size(s: moe_shape) -> int:
     return int(_lib.moe_workspace_size(ctypes.byref(s)))
+
+
+def route_balance_workspace_size(s: moe_shape) -> int:
+    return int(_lib.moe_route_balance_workspace_size(ctypes.byref(s)))
+
+
+def expert_capacity(T, k, E, capacity_factor) -> int:
+    """ceil(capacity_factor * T*k / E) (moe_expert_capacity); -1 if invalid."""
+    return int(_lib.moe_expert_capacity(int(T), int(k), int(E), float(capacity_factor)))
 
 
 def workspace_offsets(s: moe_shape) -> dict:
@@ -188,6 +209,36 @@ def moe_route(s: moe_shape, x, W_router, bias, topk_idx, topk_w, stream=None):
           _stream(stream))
 
 
+def moe_route_balance(s: moe_shape, x, W_router, bias, topk_idx, topk_w, importance, loss,
+                      workspace, stream=None):
+    """moe_route plus importance[E] (float64) and the balance loss ([1] float64)."""
+    torch = _torch()
+    fd = _float_dtype(s)
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _call("moe_route_balance", ctypes.byref(s),
+          _ptr(x, s.T * s.d, fd, "x"),
+          _ptr(W_router, s.E * s.d, fd, "W_router"),
+          _ptr(bias, s.E, torch.float32, "bias", optional=True),
+          _ptr(topk_idx, s.T * s.k, torch.int32, "topk_idx"),
+          _ptr(topk_w, s.T * s.k, torch.float32, "topk_w"),
+          _ptr(importance, s.E, torch.float64, "importance"),
+          _ptr(loss, 1, torch.float64, "loss"),
+          ws_ptr, ws_bytes, _stream(stream))
+
+
+def moe_permute_capacity(s: moe_shape, topk_idx, capacity, counts, offsets, sorted_slot,
+                         slot_pos, stream=None):
+    i32 = _torch().int32
+    _call("moe_permute_capacity", ctypes.byref(s),
+          _ptr(topk_idx, s.T * s.k, i32, "topk_idx"),
+          int(capacity),
+          _ptr(counts, s.G, i32, "counts"),
+          _ptr(offsets, s.G + 1, i32, "offsets"),
+          _ptr(sorted_slot, s.T * s.k, i32, "sorted_slot"),
+          _ptr(slot_pos, s.T * s.k, i32, "slot_pos"),
+          _stream(stream))
+
+
 def moe_permute(s: moe_shape, topk_idx, counts, offsets, sorted_slot, slot_pos,
                 stream=None):
     i32 = _torch().int32
@@ -247,14 +298,25 @@ def moe_combine(s: moe_shape, expert_out, slot_pos, topk_w, y, stream=None):
           _stream(stream))
 
 
+def _workspace(workspace):
+    """(pointer, bytes) of a uint8 GPU workspace tensor (None: no workspace)."""
+    torch = _torch()
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 GPU tensor")
+    if workspace.data_ptr() % 256:
+        raise ValueError("workspace must be 256-byte aligned")
+    return workspace.data_ptr(), workspace.numel()
+
+
 def moe_layer_forward(s: moe_shape, x, W_router, bias, W_gate_up, W_down, y, workspace,
                       stream=None):
     torch = _torch()
     fd = _float_dtype(s)
-    if workspace is None or not workspace.is_cuda or workspace.dtype != torch.uint8:
+    if workspace is None:
         raise ValueError("workspace must be a uint8 GPU tensor")
-    if workspace.data_ptr() % 256:
-        raise ValueError("workspace must be 256-byte aligned")
+    ws_ptr, ws_bytes = _workspace(workspace)
     _call("moe_layer_forward", ctypes.byref(s),
           _ptr(x, s.T * s.d, fd, "x"),
           _ptr(W_router, s.E * s.d, fd, "W_router"),
@@ -262,7 +324,27 @@ def moe_layer_forward(s: moe_shape, x, W_router, bias, W_gate_up, W_down, y, wor
           _ptr(W_gate_up, s.G * 2 * s.f * s.d, fd, "W_gate_up"),
           _ptr(W_down, s.G * s.d * s.f, fd, "W_down"),
           _ptr(y, s.T * s.d, fd, "y"),
-          workspace.data_ptr(), workspace.numel(),
+          ws_ptr, ws_bytes,
+          _stream(stream))
+
+
+def moe_layer_forward_capacity(s: moe_shape, x, W_router, bias, W_gate_up, W_down, capacity,
+                               y, workspace, stream=None):
+    """The layer with an expert capacity (moe_layer_forward's workspace)."""
+    torch = _torch()
+    fd = _float_dtype(s)
+    if workspace is None:
+        raise ValueError("workspace must be a uint8 GPU tensor")
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _call("moe_layer_forward_capacity", ctypes.byref(s),
+          _ptr(x, s.T * s.d, fd, "x"),
+          _ptr(W_router, s.E * s.d, fd, "W_router"),
+          _ptr(bias, s.E, torch.float32, "bias", optional=True),
+          _ptr(W_gate_up, s.G * 2 * s.f * s.d, fd, "W_gate_up"),
+          _ptr(W_down, s.G * s.d * s.f, fd, "W_down"),
+          int(capacity),
+          _ptr(y, s.T * s.d, fd, "y"),
+          ws_ptr, ws_bytes,
           _stream(stream))
 
 

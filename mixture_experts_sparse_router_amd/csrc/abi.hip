@@ -1,6 +1,7 @@
 // abi.hip -- the C entry points of libmoe: argument checks, workspace layout
 // and the stream-ordered launch sequence of the layer.  The steps and where
 // the pages define them are documented in include/moe.h.
+#include <math.h>
 #include <string.h>
 
 #include <atomic>
@@ -74,6 +75,14 @@ inline int hip_status(hipError_t e) {
 
 inline size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Workspace of moe_route_balance: logits [T, E] fp32, then the per-block
+// partial importances [balance_partials(T), E] fp64.
+size_t balance_layout(const Shape& s, size_t* logits_off, size_t* partial_off) {
+  *logits_off = 0;
+  *partial_off = round_up((size_t)s.T * (size_t)s.E * 4);
+  return *partial_off + round_up((size_t)balance_partials(s.T) * (size_t)s.E * 8);
+}
+
 void layout(const Shape& s, size_t* off, size_t* total) {
   const size_t Tk = (size_t)s.Tk();
   const size_t R = (size_t)s.R();
@@ -133,7 +142,52 @@ int moe_route(const moe_shape* m, const void* x, const void* W_router, const flo
       !ok_ptr(topk_idx, s.Tk()) || !ok_ptr(topk_w, s.Tk()))
     return MOE_ERR_INVALID_ARG;
   if (bias && ((uintptr_t)bias & 3u)) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_route(s, x, W_router, bias, topk_idx, topk_w, (hipStream_t)stream));
+  return hip_status(
+      launch_route(s, x, W_router, bias, topk_idx, topk_w, nullptr, (hipStream_t)stream));
+}
+
+size_t moe_route_balance_workspace_size(const moe_shape* m) {
+  if (check_shape(m) != MOE_OK) return 0;
+  size_t lo, part;
+  return balance_layout(to_shape(m), &lo, &part);
+}
+
+int moe_route_balance(const moe_shape* m, const void* x, const void* W_router,
+                      const float* bias, int32_t* topk_idx, float* topk_w, double* importance,
+                      double* loss, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(x, s.T * s.d) || !ok_ptr(W_router, s.E * s.d) ||
+      !ok_ptr(topk_idx, s.Tk()) || !ok_ptr(topk_w, s.Tk()) || !ok_ptr(importance, s.E) ||
+      !ok_ptr(loss, 1))
+    return MOE_ERR_INVALID_ARG;
+  if (bias && ((uintptr_t)bias & 3u)) return MOE_ERR_INVALID_ARG;
+  size_t lo_off, part_off;
+  const size_t total = balance_layout(s, &lo_off, &part_off);
+  if (workspace_bytes < total) return MOE_ERR_WORKSPACE;
+  if (total > 0 && (!workspace || ((uintptr_t)workspace & 255u))) return MOE_ERR_INVALID_ARG;
+  char* ws = (char*)workspace;
+  float* lg = total ? (float*)(ws + lo_off) : nullptr;
+  double* part = total ? (double*)(ws + part_off) : nullptr;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_route(s, x, W_router, bias, topk_idx, topk_w, lg, st);
+  if (e == hipSuccess) e = launch_balance(s, lg, part, importance, loss, st);
+  return hip_status(e);
+}
+
+int moe_permute_capacity(const moe_shape* m, const int32_t* topk_idx, int64_t capacity,
+                         int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                         int32_t* slot_pos, void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (!ok_ptr(topk_idx, s.Tk()) || !ok_ptr(counts, s.G()) || !ok_ptr(offsets, s.G() + 1) ||
+      !ok_ptr(sorted_slot, s.Tk()) || !ok_ptr(slot_pos, s.Tk()))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_permute(s, topk_idx, capacity, counts, offsets, sorted_slot,
+                                   slot_pos, (hipStream_t)stream));
 }
 
 int moe_permute(const moe_shape* m, const int32_t* topk_idx, int32_t* counts,
@@ -144,8 +198,14 @@ int moe_permute(const moe_shape* m, const int32_t* topk_idx, int32_t* counts,
   if (!ok_ptr(topk_idx, s.Tk()) || !ok_ptr(counts, s.G()) || !ok_ptr(offsets, s.G() + 1) ||
       !ok_ptr(sorted_slot, s.Tk()) || !ok_ptr(slot_pos, s.Tk()))
     return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_permute(s, topk_idx, counts, offsets, sorted_slot, slot_pos,
+  return hip_status(launch_permute(s, topk_idx, -1, counts, offsets, sorted_slot, slot_pos,
                                    (hipStream_t)stream));
+}
+
+int64_t moe_expert_capacity(int64_t T, int64_t k, int64_t E, double capacity_factor) {
+  if (T < 0 || k < 1 || E < 1 || !(capacity_factor >= 0.0) || capacity_factor > 1e9)
+    return -1;
+  return (int64_t)ceil(capacity_factor * (double)(T * k) / (double)E);
 }
 
 int moe_grouped_gemm_gate_up(const moe_shape* m, const void* x, const int32_t* sorted_slot,
@@ -199,9 +259,14 @@ int moe_combine(const moe_shape* m, const void* expert_out, const int32_t* slot_
   return hip_status(launch_combine(s, expert_out, slot_pos, topk_w, y, (hipStream_t)stream));
 }
 
-int moe_layer_forward(const moe_shape* m, const void* x, const void* W_router,
-                      const float* bias, const void* W_gate_up, const void* W_down, void* y,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The layer, with an expert capacity (capacity < 0: none).
+int layer_forward(const moe_shape* m, const void* x, const void* W_router, const float* bias,
+                  const void* W_gate_up, const void* W_down, int64_t capacity, void* y,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_shape(m);
   if (rc != MOE_OK) return rc;
   const Shape s = to_shape(m);
@@ -224,20 +289,41 @@ int moe_layer_forward(const moe_shape* m, const void* x, const void* W_router,
   void* out = ws + off[MOE_WS_EXPERT_OUT];
 
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_route(s, x, W_router, bias, idx, w, st);
-  if (s.dt == MOE_DT_BF16 && s.T <= 64) {
+  hipError_t e = launch_route(s, x, W_router, bias, idx, w, nullptr, st);
+  if (s.dt == MOE_DT_BF16 && s.T <= 64 && capacity < 0) {
     // decode batches: the gate_up kernel finds its rows from the ids and
     // writes the permutation itself (one launch fewer)
     if (e == hipSuccess)
       e = launch_gate_up_from_ids(s, x, idx, W_gate_up, act, counts, offsets, sorted_slot,
                                   slot_pos, st);
   } else {
-    if (e == hipSuccess) e = launch_permute(s, idx, counts, offsets, sorted_slot, slot_pos, st);
+    if (e == hipSuccess)
+      e = launch_permute(s, idx, capacity, counts, offsets, sorted_slot, slot_pos, st);
     if (e == hipSuccess) e = launch_gate_up(s, x, sorted_slot, offsets, W_gate_up, act, st);
   }
   if (e == hipSuccess) e = launch_down(s, act, offsets, W_down, out, st);
   if (e == hipSuccess) e = launch_combine(s, out, slot_pos, w, y, st);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward(const moe_shape* m, const void* x, const void* W_router,
+                      const float* bias, const void* W_gate_up, const void* W_down, void* y,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return layer_forward(m, x, W_router, bias, W_gate_up, W_down, -1, y, workspace,
+                       workspace_bytes, stream);
+}
+
+int moe_layer_forward_capacity(const moe_shape* m, const void* x, const void* W_router,
+                               const float* bias, const void* W_gate_up, const void* W_down,
+                               int64_t capacity, void* y, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  return layer_forward(m, x, W_router, bias, W_gate_up, W_down, capacity, y, workspace,
+                       workspace_bytes, stream);
 }
 
 int moe_layer_forward_static(const moe_shape* m, const void* x, const void* W_router,

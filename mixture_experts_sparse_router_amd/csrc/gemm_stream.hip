@@ -67,17 +67,21 @@ struct GroupFromIds {
 // One wave's view: ballots over the ids, 64 at a time.  `list` (LDS, >= 64
 // entries) receives the group's copies in ascending order (a group has at
 // most T <= 64 of them: a token picks an expert at most once).  Ids outside
-// [0, E) count for no group.
+// [0, E) count for no group; their copies take the first rows (the layout
+// of the permutation step), so group g starts after them and after the
+// copies of the groups below g.
 __device__ __forceinline__ GroupFromIds group_from_ids(const int32_t* __restrict__ idx,
-                                                       int n_slots, int g, int* list) {
+                                                       int n_slots, int g, int E, int* list) {
   const int lane = threadIdx.x & 63;
   const uint64_t below_lanes = (1ull << lane) - 1ull;
   int before = 0, found = 0;
   for (int s0 = 0; s0 < n_slots; s0 += 64) {
     const int s = s0 + lane;
-    const uint32_t v = s < n_slots ? (uint32_t)idx[s] : 0xffffffffu;  // unsigned: < 0 is huge
-    const uint64_t lt = __ballot(v < (uint32_t)g);
-    const uint64_t eq = __ballot(v == (uint32_t)g);
+    const bool in = s < n_slots;
+    const uint32_t v = in ? (uint32_t)idx[s] : 0u;  // unsigned: ids < 0 are huge
+    // copies placed before group g: ids below g, and ids outside [0, E)
+    const uint64_t lt = __ballot(in && (v < (uint32_t)g || v >= (uint32_t)E));
+    const uint64_t eq = __ballot(in && v == (uint32_t)g);
     if ((eq >> lane) & 1ull) {
       const int r = found + __popcll(eq & below_lanes);
       if (r < 64) list[r] = s;
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
       // every wave finds the group itself (its own writes to s_list are the
       // ones it reads; the other waves write the same values).  A token
       // picks an expert at most once, so a group has at most T <= 64 rows.
-      const GroupFromIds gi = group_from_ids(topk_idx, (int)Tk, g, s_list);
+      const GroupFromIds gi = group_from_ids(topk_idx, (int)Tk, g, E, s_list);
       row_begin = gi.row_begin;
       rows = gi.rows < 64 ? gi.rows : 64;
     } else {
@@ -151,12 +155,9 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
     }
     if (g == 0 && tile == 0 && wave == 1) {
       // copies whose expert id is outside [0, E) take no expert: they are
-      // listed after all routed rows and marked with slot_pos = -1
+      // listed first, in slot order, and marked with slot_pos = -1
       const uint64_t below_lanes = (1ull << lane) - 1ull;
-      int ndrop = 0;
-      for (int s0 = 0; s0 < (int)Tk; s0 += 64)
-        ndrop += __popcll(__ballot(s0 + lane < (int)Tk && (uint32_t)topk_idx[s0 + lane] >= (uint32_t)E));
-      int at = (int)Tk - ndrop;
+      int at = 0;
       for (int s0 = 0; s0 < (int)Tk; s0 += 64) {
         const int sl = s0 + lane;
         const bool drop = sl < (int)Tk && (uint32_t)topk_idx[sl] >= (uint32_t)E;

@@ -124,12 +124,20 @@ inline Shape to_shape(const moe_shape* s) {
 
 // Launchers (return hipSuccess or the launch error).  Argument checking is
 // done by the ABI layer before any of these is called.
+// logits_out: NULL, or [T, E] fp32 that receives the logits (bias included).
 hipError_t launch_route(const Shape& s, const void* x, const void* W_router,
                         const float* bias, int32_t* topk_idx, float* topk_w,
-                        hipStream_t st);
-hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int32_t* counts,
-                          int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
-                          hipStream_t st);
+                        float* logits_out, hipStream_t st);
+// capacity < 0: none.
+hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int64_t capacity,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                          int32_t* slot_pos, hipStream_t st);
+// Router load statistics from the logits: importance[E] (mean softmax
+// probability) and the balance loss; partial holds balance_partials(T) * E
+// doubles.
+int64_t balance_partials(int64_t T);
+hipError_t launch_balance(const Shape& s, const float* logits, double* partial,
+                          double* importance, double* loss, hipStream_t st);
 hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* sorted_slot,
                           const int32_t* offsets, const void* W_gate_up, void* act,
                           hipStream_t st);

@@ -15,16 +15,26 @@
 //      and the highest peer lane advances that expert's running count in the
 //      wave's LDS histogram row (one wave's LDS operations run in program
 //      order, so the next 64 see the update).  The rank is parked in slot_pos.
-//   B. per expert: total over the 16 rows, block-wide exclusive scan -> offsets,
-//      and each row is turned into that wave's base position for the expert.
-//   C. position = base[w][e] + rank; sorted_slot[position] = s.
+//   B. per expert: total over the 16 rows, block-wide exclusive scans ->
+//      offsets, and each row is turned into the rank (among all copies of
+//      the expert) of that wave's first copy of it.
+//   C. rank = that base + the rank inside the wave range; position = the
+//      first row of the expert's kept (or dropped) copies + rank;
+//      sorted_slot[position] = s.
 // Integer only: the result is exact and independent of scheduling.
 //
-// Ids outside [0, E) select no expert: such a copy is ranked in a bin of its
-// own after all experts, so it lands in rows [valid, T*k) (inside the last
-// expert's row range, since offsets[E] = T*k always; that expert's count does
-// not include them) and gets slot_pos = -1, which the combine skips.  Every
-// row below T*k is thus written, every index stays in bounds, and the shared
+// Expert capacity (optional): every expert keeps at most `cap` copies, its
+// first ones in slot order, and drops the rest (yunthe "分工的艺术" page,
+// section 3.1, expert capacity; Baidu page, section 三.2, capacity-bound
+// token dropping).  A copy's rank among its expert's copies is its wave
+// base plus its rank inside the wave range, so the test is one compare.
+//
+// Dropped copies take the rows at the front, [0, D): first the copies whose
+// id lies outside [0, E) (they select no expert), in slot order, then the
+// copies over capacity, by expert, in slot order; their slot_pos is -1,
+// which the combine skips.  Kept copies follow from offsets[0] = D, so no
+// expert group contains a dropped row and offsets[E] = T*k always: every
+// row below T*k is written, every index stays in bounds, and the shared
 // rows always start at T*k.
 #include "moe_common.h"
 
@@ -66,8 +76,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
 __global__ __launch_bounds__(kThreads) void permute_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
-    int32_t* __restrict__ slot_pos, int64_t T, int64_t k, int E, int S, int nbits) {
-  __shared__ int32_t hist[kWaves][kMaxGroups + 1];  // + the bin of dropped copies
+    int32_t* __restrict__ slot_pos, int64_t T, int64_t k, int E, int S, int nbits, int cap) {
+  __shared__ int32_t hist[kWaves][kMaxGroups + 1];  // + the bin of invalid ids
+  __shared__ int32_t row_kept[kMaxGroups];           // first row of expert e's kept copies
+  __shared__ int32_t row_over[kMaxGroups];           // first row of its copies over capacity
   __shared__ int32_t tmp[2 * kWaves + 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -93,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
       if (b0 + 64 * u >= s_end) break;
       const int64_t s = b0 + 64 * u + lane;
       const bool active = s < s_end;
-      // expert id; E: the dropped bin (ids outside [0, E)); E + 1: idle lane
+      // expert id; E: the bin of invalid ids (outside [0, E)); E + 1: idle lane
       const int key = !active ? E + 1 : (v[u] >= 0 && v[u] < E) ? v[u] : E;
       uint64_t peers = ~0ull;
       for (int b = 0; b < nbits; ++b) {
@@ -114,31 +126,46 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
   }
   __syncthreads();
 
-  // ---- B: totals, prefix sum over the routed experts, per-wave bases; the
-  // dropped bin follows the routed rows, the shared groups start at T*k
+  // ---- B: per expert, kept = min(copies, cap) and over = the rest; the
+  // invalid ids' rows, then every expert's rows over capacity, then the kept
+  // rows (prefix sum of kept); the shared groups start at T*k
   const int g = threadIdx.x;  // expert group handled by this thread
   int total = 0;
-  if (g < E) {
+  if (g < E)
     for (int w = 0; w < kWaves; ++w) total += hist[w][g];
-  } else if (g < E + S) {
-    total = (int)T;
-  }
-  int valid = 0;
-  const int off = block_exclusive_scan(g < E ? total : 0, tmp, &valid);
+  int n_inv = 0;
+  for (int w = 0; w < kWaves; ++w) n_inv += hist[w][E];
+  const int kept = g < E ? (total < cap ? total : cap) : 0;
+  int n_over = 0, n_kept = 0;
+  const int over_base = n_inv + block_exclusive_scan(g < E ? total - kept : 0, tmp, &n_over);
+  const int kept_off = block_exclusive_scan(kept, tmp, &n_kept);
+  const int n_drop = n_inv + n_over;
   const int Tk = (int)(T * k);
   if (g < E) {
-    counts[g] = total;
-    offsets[g] = off;
+    counts[g] = kept;
+    offsets[g] = n_drop + kept_off;
   } else if (g < E + S) {
-    counts[g] = total;
+    counts[g] = (int)T;
     offsets[g] = Tk + (g - E) * (int)T;
   }
   if (g == 0) offsets[E + S] = Tk + S * (int)T;
-  if (g <= E) {
-    int run = g < E ? off : valid;
+  // per wave and expert: the rank (among the expert's copies) of the wave's
+  // first copy of it
+  if (g < E) {
+    row_kept[g] = n_drop + kept_off;
+    row_over[g] = over_base;
+    int run = 0;
     for (int w = 0; w < kWaves; ++w) {
       const int c = hist[w][g];
       hist[w][g] = run;
+      run += c;
+    }
+  }
+  if (g == 0) {
+    int run = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = hist[w][E];
+      hist[w][E] = run;
       run += c;
     }
   }
@@ -157,24 +184,28 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
     for (int u = 0; u < kBatch; ++u) {
       const int64_t s = b0 + 64 * u + lane;
       if (s >= s_end) continue;
-      const bool dropped = v[u] < 0 || v[u] >= E;
-      const int pos = hist[wave][dropped ? E : v[u]] + r[u];
+      const bool valid = v[u] >= 0 && v[u] < E;
+      const int rank = hist[wave][valid ? v[u] : E] + r[u];  // among the same key's copies
+      const bool keep = valid && rank < cap;
+      const int pos = !valid ? rank : keep ? row_kept[v[u]] + rank : row_over[v[u]] + rank - cap;
       sorted_slot[pos] = (int32_t)s;
-      slot_pos[s] = dropped ? -1 : pos;
+      slot_pos[s] = keep ? pos : -1;
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int32_t* counts,
-                          int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
-                          hipStream_t st) {
+hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int64_t capacity,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                          int32_t* slot_pos, hipStream_t st) {
   int nbits = 0;
-  while ((1 << nbits) <= s.E + 1) ++nbits;  // keys 0..E+1 (E: dropped, E+1: idle lane)
+  while ((1 << nbits) <= s.E + 1) ++nbits;  // keys 0..E+1 (E: invalid id, E+1: idle lane)
+  // no capacity, or one no expert can reach: every copy of a valid id is kept
+  const int cap = capacity < 0 || capacity > s.Tk() ? (int)s.Tk() : (int)capacity;
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kThreads), 0, st, topk_idx, counts,
                      offsets, sorted_slot, slot_pos, s.T, s.k, (int)s.E, (int)s.S,
-                     nbits);
+                     nbits, cap);
   return hipGetLastError();
 }
 

@@ -24,6 +24,10 @@
 //   route_tiled (fp32, large T): one workgroup per TT tokens; x and W chunks
 //     are staged through LDS and thread (ks, e) keeps TT running logits, so
 //     each router row is read once per TT tokens.
+//   Logits out (optional, for the router's load statistics): the ranking
+//   value of every (token, expert) pair rounded to fp32 -- exact for every
+//   expert that could be selected; on the screen path the others get their
+//   screen value, within the screen's bound of the exact one.
 //   Selection (one wave per token): with at most 64 contenders, each lane
 //     holds one and counts the contenders ranked above it (its rank), so the
 //     k winners are known at once; with more, k rounds of a wave-wide argmax
@@ -206,8 +210,8 @@ constexpr int kSmallThreads = 1024;
 template <typename In>
 __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
     const In* __restrict__ x, const In* __restrict__ Wr, const float* __restrict__ bias,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int64_t d, int E, int k,
-    int KS) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ logits_out,
+    int64_t d, int E, int k, int KS) {
   __shared__ double logits[kMaxE];
   __shared__ SelSlots sl;
   const int tid = threadIdx.x;
@@ -247,7 +251,10 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
     }
     // combine the KS partials of expert e (adjacent lanes) in a fixed order
     for (int off = 1; off < KS; off <<= 1) acc += __shfl_xor(acc, off, 64);
-    if (ks == 0 && e < E) logits[e] = rank_value(acc, bias, e);
+    if (ks == 0 && e < E) {
+      logits[e] = rank_value(acc, bias, e);
+      if (logits_out) logits_out[t * E + e] = (float)logits[e];
+    }
   }
   __syncthreads();
   if (tid < 64) topk_row(logits, E, k, topk_idx + t * k, topk_w + t * k, &sl);
@@ -267,8 +274,8 @@ struct TiledSmem {
 template <typename In, int TT>
 __global__ __launch_bounds__(kThreads) void route_tiled_kernel(
     const In* __restrict__ x, const In* __restrict__ Wr, const float* __restrict__ bias,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int64_t T, int64_t d,
-    int E, int k, int P) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ logits_out,
+    int64_t T, int64_t d, int E, int k, int P) {
   __shared__ TiledSmem<TT> sm;
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * TT;
@@ -332,6 +339,8 @@ __global__ __launch_bounds__(kThreads) void route_tiled_kernel(
         double s = 0.0;
         for (int q = 0; q < KS; ++q) s += sm.part[q * P + e_loc][t];
         sm.logits[t][e0 + e_loc] = rank_value(s, bias, e0 + e_loc);
+        if (logits_out && t0 + t < T)
+          logits_out[(t0 + t) * E + e0 + e_loc] = (float)sm.logits[t][e0 + e_loc];
       }
     }
     __syncthreads();
@@ -704,7 +713,8 @@ template <int M>
 __device__ void screen_select(const ScreenSmem& S, const bf16_t* __restrict__ x,
                               const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
                               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                              int64_t T, int64_t d, int E, int k, int64_t t0) {
+                              float* __restrict__ logits_out, int64_t T, int64_t d, int E,
+                              int k, int64_t t0) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint16_t* mycand = S.cand + wave * E;
   SelSlots* sl = S.sls + wave;
@@ -748,6 +758,9 @@ __device__ void screen_select(const ScreenSmem& S, const bf16_t* __restrict__ x,
       const int e = e0 + lane;
       bool c = false;
       if (e < E) c = !(row[e] + (rel * xn * (double)S.wn[e] + 1e-30) < tau);
+      // logits asked for: the screen value of every expert ruled out (the
+      // candidates' exact values follow below)
+      if (logits_out && e < E && !c) logits_out[t * E + e] = (float)row[e];
       const uint64_t mk = __ballot(c);
       if (c) mycand[ncand + __popcll(mk & ((1ull << lane) - 1ull))] = (uint16_t)e;
       ncand += __popcll(mk);
@@ -775,6 +788,7 @@ __device__ void screen_select(const ScreenSmem& S, const bf16_t* __restrict__ x,
         if (lane < cb) {
           const int e = mycand[c0 + lane];
           row[e] = rank_value(got, bias, e);
+          if (logits_out) logits_out[t * E + e] = (float)row[e];
         }
       } else {
         // lane c of the list holds candidate c
@@ -783,6 +797,7 @@ __device__ void screen_select(const ScreenSmem& S, const bf16_t* __restrict__ x,
         if (want >= 0 && want < cb) {
           my_e = mycand[lane];
           my_v = rank_value(v, bias, my_e);
+          if (logits_out) logits_out[t * E + my_e] = (float)my_v;
         }
       }
       c0 += cb;
@@ -825,8 +840,8 @@ struct PassItems {
 template <int NBW>
 __global__ __launch_bounds__(kScreenThreads, 1) void route_staged_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int64_t T, int64_t d, int E,
-    int k) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ logits_out,
+    int64_t T, int64_t d, int E, int k) {
   using SG = Staged<NBW>;
   // the rings are LDS objects of their own: with more than one LDS object
   // the compiler tags every LDS access with the object it touches, and the
@@ -952,10 +967,10 @@ __global__ __launch_bounds__(kScreenThreads, 1) void route_staged_kernel(
     screen_pass_store<NBW>(A, S, bias, E, e0, P.nb, P.KS, P.live, P.blk, P.xnorm);
   }
   // experts per lane of the selection: 1, 2, 4 or 16
-  if (E <= 64) screen_select<1>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
-  else if (E <= 128) screen_select<2>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
-  else if (E <= 256) screen_select<4>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
-  else screen_select<16>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
+  if (E <= 64) screen_select<1>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
+  else if (E <= 128) screen_select<2>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
+  else if (E <= 256) screen_select<4>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
+  else screen_select<16>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
 }
 
 // ------------------------------------------------------------ route_direct
@@ -969,8 +984,8 @@ struct StepRegs {
 template <int NBW>
 __global__ __launch_bounds__(kScreenThreads, 1) void route_direct_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int64_t T, int64_t d, int E,
-    int k) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ logits_out,
+    int64_t T, int64_t d, int E, int k) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const ScreenLds L = screen_lds(E, true);
   const ScreenSmem S(smem, L);
@@ -1067,40 +1082,40 @@ __global__ __launch_bounds__(kScreenThreads, 1) void route_direct_kernel(
     screen_pass_store<NBW>(A, S, bias, E, e0, P.nb, P.KS, P.live, P.blk, P.xnorm);
   }
   // experts per lane of the selection: 1, 2, 4 or 16
-  if (E <= 64) screen_select<1>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
-  else if (E <= 128) screen_select<2>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
-  else if (E <= 256) screen_select<4>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
-  else screen_select<16>(S, x, Wr, bias, topk_idx, topk_w, T, d, E, k, t0);
+  if (E <= 64) screen_select<1>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
+  else if (E <= 128) screen_select<2>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
+  else if (E <= 256) screen_select<4>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
+  else screen_select<16>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
 }
 
 template <typename In>
 hipError_t launch_small(const Shape& s, const void* x, const void* Wr, const float* bias,
-                        int32_t* idx, float* w, hipStream_t st) {
+                        int32_t* idx, float* w, float* lo, hipStream_t st) {
   // split each router row over KS lanes so that the E rows fill the block
   int KS = 1;
   while (KS < 64 && (int64_t)(kSmallThreads / (KS * 2)) >= s.E) KS *= 2;
   hipLaunchKernelGGL((route_small_kernel<In>), dim3((unsigned)s.T), dim3(kSmallThreads), 0, st,
-                     (const In*)x, (const In*)Wr, bias, idx, w, s.d, (int)s.E, (int)s.k, KS);
+                     (const In*)x, (const In*)Wr, bias, idx, w, lo, s.d, (int)s.E, (int)s.k, KS);
   return hipGetLastError();
 }
 
 template <typename In, int TT>
 hipError_t launch_tiled(const Shape& s, const void* x, const void* Wr, const float* bias,
-                        int32_t* idx, float* w, hipStream_t st) {
+                        int32_t* idx, float* w, float* lo, hipStream_t st) {
   int P = 1;
   while (P < s.E && P < kMaxP) P <<= 1;
   if (P < 32) P = 32;  // keep the chunk split at most 8 ways
   const unsigned grid = (unsigned)((s.T + TT - 1) / TT);
   hipLaunchKernelGGL((route_tiled_kernel<In, TT>), dim3(grid), dim3(kThreads), 0, st,
-                     (const In*)x, (const In*)Wr, bias, idx, w, s.T, s.d, (int)s.E,
+                     (const In*)x, (const In*)Wr, bias, idx, w, lo, s.T, s.d, (int)s.E,
                      (int)s.k, P);
   return hipGetLastError();
 }
 
 template <typename In>
 hipError_t launch_dt(const Shape& s, const void* x, const void* Wr, const float* bias,
-                     int32_t* idx, float* w, hipStream_t st) {
-  if (s.T <= 64) return launch_small<In>(s, x, Wr, bias, idx, w, st);
+                     int32_t* idx, float* w, float* lo, hipStream_t st) {
+  if (s.T <= 64) return launch_small<In>(s, x, Wr, bias, idx, w, lo, st);
   if constexpr (sizeof(In) == 2) {
     // allow more than 64 KB of dynamic LDS, once per device (the attribute
     // belongs to the device's copy of the kernel)
@@ -1129,23 +1144,23 @@ hipError_t launch_dt(const Shape& s, const void* x, const void* Wr, const float*
     if (s.E <= 128) {
       const size_t lds = (size_t)screen_lds((int)s.E, true).total;
       hipLaunchKernelGGL(route_staged_kernel<1>, dim3(grid), dim3(kScreenThreads), lds, st,
-                         (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, s.T, s.d,
+                         (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, lo, s.T, s.d,
                          (int)s.E, (int)s.k);
     } else if (s.E <= kStagedMaxE) {
       const size_t lds = (size_t)screen_lds((int)s.E, false).total;
       hipLaunchKernelGGL(route_staged_kernel<2>, dim3(grid), dim3(kScreenThreads), lds, st,
-                         (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, s.T, s.d,
+                         (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, lo, s.T, s.d,
                          (int)s.E, (int)s.k);
     } else {
       const size_t lds = (size_t)screen_lds((int)s.E, true).total;
       hipLaunchKernelGGL(route_direct_kernel<2>, dim3(grid), dim3(kScreenThreads), lds, st,
-                         (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, s.T, s.d,
+                         (const bf16_t*)x, (const bf16_t*)Wr, bias, idx, w, lo, s.T, s.d,
                          (int)s.E, (int)s.k);
     }
     return hipGetLastError();
   } else {
-    if (s.E > 512) return launch_tiled<In, 8>(s, x, Wr, bias, idx, w, st);
-    return launch_tiled<In, 16>(s, x, Wr, bias, idx, w, st);
+    if (s.E > 512) return launch_tiled<In, 8>(s, x, Wr, bias, idx, w, lo, st);
+    return launch_tiled<In, 16>(s, x, Wr, bias, idx, w, lo, st);
   }
 }
 
@@ -1153,11 +1168,11 @@ hipError_t launch_dt(const Shape& s, const void* x, const void* Wr, const float*
 
 hipError_t launch_route(const Shape& s, const void* x, const void* W_router,
                         const float* bias, int32_t* topk_idx, float* topk_w,
-                        hipStream_t st) {
+                        float* logits_out, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   if (s.dt == MOE_DT_BF16)
-    return launch_dt<bf16_t>(s, x, W_router, bias, topk_idx, topk_w, st);
-  return launch_dt<float>(s, x, W_router, bias, topk_idx, topk_w, st);
+    return launch_dt<bf16_t>(s, x, W_router, bias, topk_idx, topk_w, logits_out, st);
+  return launch_dt<float>(s, x, W_router, bias, topk_idx, topk_w, logits_out, st);
 }
 
 }  // namespace moe

@@ -182,3 +182,53 @@ def test_static_entry_checks_before_any_hip_call():
     # an empty batch needs no intermediates and enqueues nothing
     assert L.moe_layer_forward_static(ctypes.byref(_shape(T=0)), None, p, None, p, p, None,
                                       None) == moe.MOE_OK
+
+
+def test_expert_capacity_matches_oracle():
+    import oracle
+    for (T, k, E, f) in ((4096, 8, 128, 1.25), (4096, 8, 256, 1.0), (10, 2, 3, 1.0),
+                         (7, 1, 4, 0.0), (8192, 2, 8, 2.0), (0, 3, 5, 1.5), (1, 1, 1, 1e-9)):
+        assert moe.expert_capacity(T, k, E, f) == oracle.expert_capacity(T, k, E, f)
+    for bad in ((-1, 1, 1, 1.0), (1, 0, 1, 1.0), (1, 1, 0, 1.0), (1, 1, 1, -0.5),
+                (1, 1, 1, float("nan")), (1, 1, 1, 1e10)):
+        assert moe.expert_capacity(*bad) == -1
+
+
+def test_route_balance_workspace_and_checks():
+    L = moe.lib()
+    for dims in ((4096, 7168, 2048, 256, 8, 1, 1), (100, 64, 64, 7, 2, 0, 0), (0, 64, 64, 4, 1, 0, 1)):
+        s = moe.shape(*dims)
+        nb = (s.T + 31) // 32
+        expect = (s.T * s.E * 4 + 255) // 256 * 256 + (nb * s.E * 8 + 255) // 256 * 256
+        assert moe.route_balance_workspace_size(s) == expect
+    assert moe.route_balance_workspace_size(_shape(k=0)) == 0
+    s = _shape()
+    p = ctypes.c_void_p(4096)
+    need = moe.route_balance_workspace_size(s)
+    args = lambda imp, ws, nbytes: (ctypes.byref(s), p, p, None, p, p, imp, p, ws, nbytes, None)
+    assert L.moe_route_balance(*args(p, p, need - 1)) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_route_balance(*args(None, p, need)) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route_balance(*args(p, ctypes.c_void_p(4096 + 64), need)) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route_balance(*args(p, None, need)) == moe.MOE_ERR_INVALID_ARG
+    bad = _shape(E=0)
+    assert L.moe_route_balance(ctypes.byref(bad), p, p, None, p, p, p, p, p, 1 << 30,
+                               None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_capacity_entry_points_check_arguments():
+    L = moe.lib()
+    s = _shape()
+    p = ctypes.c_void_p(4096)
+    assert L.moe_permute_capacity(ctypes.byref(s), p, -1, p, p, p, p, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_permute_capacity(ctypes.byref(_shape(k=0)), p, 4, p, p, p, p,
+                                  None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_permute_capacity(ctypes.byref(s), p, 4, p, None, p, p,
+                                  None) == moe.MOE_ERR_INVALID_ARG
+    need = moe.workspace_size(s)
+    assert L.moe_layer_forward_capacity(ctypes.byref(s), p, p, None, p, p, -1, p, p, need,
+                                        None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_capacity(ctypes.byref(s), p, p, None, p, p, 3, p, p, need - 1,
+                                        None) == moe.MOE_ERR_WORKSPACE
+    # an empty batch needs no work at all
+    assert L.moe_layer_forward_capacity(ctypes.byref(_shape(T=0)), None, p, None, p, p, 0, None,
+                                        p, moe.workspace_size(_shape(T=0)), None) == moe.MOE_OK
