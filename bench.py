@@ -47,6 +47,8 @@ def parse(argv=None):
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the Mixtral-shaped prefill measurement")
     p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--no-aux", action="store_true",
+                   help="skip the router-auxiliary timings (balance loss, capacity)")
     p.add_argument("--rotate", type=int, default=1,
                    help="use N device copies of the expert weights in turn, so that no step "
                         "finds the previous step's weights in a cache (default 1)")
@@ -285,7 +287,7 @@ def config_dict(cfg, seed, ac, rot):
             "parallelism": "single GPU"}
 
 
-def prefill_extra(torch, moe, steps, no_cpu):
+def prefill_extra(torch, moe, steps, no_cpu, no_aux=False):
     """The Mixtral-8x7B-shaped prefill layer (T=8192, d=4096, f=14336, E=8,
     top-2): layer tokens/s and its fraction of the bf16 MFMA peak."""
     import moe_synth
@@ -296,7 +298,8 @@ def prefill_extra(torch, moe, steps, no_cpu):
     kt = L.kernel_times(torch, 5)
     wall, ev = L.timed_steps(torch, steps)
     ac, roof, layer = L.summary(torch, kt, ev / steps)
-    layer["aux"] = L.aux_times(torch, 5)
+    if not no_aux:
+        layer["aux"] = L.aux_times(torch, 5)
     out = {"workload": cfg.name, "steps": steps,
            "ms_per_step": round(wall / steps * 1e3, 4),
            "ms_per_step_hip_events": round(ev / steps * 1e3, 4),
@@ -348,7 +351,8 @@ def main(argv=None):
     layer["ms_per_step_hip_events"] = round(ev / args.steps * 1e3, 4)
     layer["hbm_frac_hip_events"] = round(ac["layer_bytes"] / (ev / args.steps) / 1e9
                                          / HBM_PEAK_GBS, 4)
-    layer["aux"] = L.aux_times(torch, max(20, min(args.steps, 100)))
+    if not args.no_aux:
+        layer["aux"] = L.aux_times(torch, max(20, min(args.steps, 100)))
 
     out = {
         "metric": "MoE layer tokens/s",
@@ -373,7 +377,8 @@ def main(argv=None):
     if not args.no_prefill and args.config != PREFILL_CONFIG:
         del L
         torch.cuda.empty_cache()
-        out["prefill"] = prefill_extra(torch, moe, args.prefill_steps, args.no_cpu)
+        out["prefill"] = prefill_extra(torch, moe, args.prefill_steps, args.no_cpu,
+                                       args.no_aux)
     print(json.dumps(out), flush=True)
 
 

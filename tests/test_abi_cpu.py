@@ -198,7 +198,7 @@ def test_route_balance_workspace_and_checks():
     L = moe.lib()
     for dims in ((4096, 7168, 2048, 256, 8, 1, 1), (100, 64, 64, 7, 2, 0, 0), (0, 64, 64, 4, 1, 0, 1)):
         s = moe.shape(*dims)
-        nb = (s.T + 31) // 32
+        nb = (s.T + 15) // 16
         expect = (s.T * s.E * 4 + 255) // 256 * 256 + (nb * s.E * 8 + 255) // 256 * 256
         assert moe.route_balance_workspace_size(s) == expect
     assert moe.route_balance_workspace_size(_shape(k=0)) == 0
