@@ -17,7 +17,12 @@ Recipe (the same for every workload):
     deviation); draws in float32, then rounded to nearest-even bfloat16 for
     bf16 workloads (stored as raw uint16 bit patterns);
   - optional Zipf(s) router prior: bias_e = -s * ln(e + 1) in float32, i.e.
-    the prior routing probability of expert e is proportional to (e+1)^-s.
+    the prior routing probability of expert e is proportional to (e+1)^-s;
+  - MXFP4 expert weights (the quantised decode variant): tensor_id 6
+    (gate_up) and 7 (down), part = expert index; uniformly random bytes of
+    packed FP4 codes and E8M0 block scales drawn uniformly from
+    MXFP4_SCALE_RANGE, which puts the values at the size of N(0, 0.02)
+    weights (|value| mostly 2^-8 .. 2^-4).
 """
 from __future__ import annotations
 
@@ -144,6 +149,38 @@ def make_layer_inputs(cfg: LayerConfig, seed: int, threads=None,
             list(ex.map(one, range(n)))
         out["W_gate_up"] = wgu
         out["W_down"] = wd
+    return out
+
+
+MXFP4_SCALE_RANGE = (119, 121)   # E8M0 exponents 2^-8 .. 2^-6
+
+
+def mxfp4(key, rows: int, K: int, scale_range=MXFP4_SCALE_RANGE):
+    """Seeded MXFP4 matrix [rows, K]: (packed codes uint8 [rows, K/2],
+    E8M0 scales uint8 [rows, K/32]).  Raw bytes only: the decoding is the
+    oracle's and the kernels' business."""
+    assert K % 32 == 0
+    rng = np.random.default_rng(list(key))
+    q = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    sc = rng.integers(scale_range[0], scale_range[1] + 1, size=(rows, K // 32), dtype=np.uint8)
+    return q, sc
+
+
+def make_mxfp4_experts(cfg: LayerConfig, seed: int, threads=None) -> dict:
+    """MXFP4 expert weights of a layer: Wq_gate_up [E+S, 2f, d/2],
+    Ws_gate_up [E+S, 2f, d/32], Wq_down [E+S, d, f/2], Ws_down [E+S, d, f/32]."""
+    n = cfg.E + cfg.S
+    out = {"Wq_gate_up": np.empty((n, 2 * cfg.f, cfg.d // 2), np.uint8),
+           "Ws_gate_up": np.empty((n, 2 * cfg.f, cfg.d // 32), np.uint8),
+           "Wq_down": np.empty((n, cfg.d, cfg.f // 2), np.uint8),
+           "Ws_down": np.empty((n, cfg.d, cfg.f // 32), np.uint8)}
+
+    def one(e):
+        out["Wq_gate_up"][e], out["Ws_gate_up"][e] = mxfp4((seed, 6, e), 2 * cfg.f, cfg.d)
+        out["Wq_down"][e], out["Ws_down"][e] = mxfp4((seed, 7, e), cfg.d, cfg.f)
+
+    with ThreadPoolExecutor(_workers(threads)) as ex:
+        list(ex.map(one, range(n)))
     return out
 
 

@@ -39,6 +39,7 @@ _SIGNATURES = {
                                 _i32p, _i32p],
     "oracle_expert_capacity": [_i64, _i64, _i64, ctypes.c_double],
     "oracle_balance": [_i64, _i64, _i64, _int, _vp, _vp, _f32p, _f64p, _f64p, _f64p],
+    "oracle_dequant_mxfp4": [_i64, _i64, _vp, _vp, _f64p],
     "oracle_gate_up_rows": [_i64, _i64p, _i32p, _i64, _i64, _int, _vp, _vp, _f64p],
     "oracle_down_rows": [_i64, _i32p, _i64, _i64, _int, _vp, _vp, _f64p],
     "oracle_combine": [_i64, _i64, _i64, _i64, _int, _vp, _i32p, _f64p, _f64p],
@@ -122,6 +123,20 @@ class Oracle:
             rc = self.L.oracle_permute_capacity(T, k, E, S, int(capacity), *args)
         _check(rc, "oracle_permute")
         return counts, offsets, sorted_slot, slot_pos
+
+    def dequant_mxfp4(self, q, scales):
+        """fp64 values [..., K] of MXFP4 weights: q [..., K/2] uint8 (two FP4
+        elements per byte, even element in the low nibble), scales [..., K/32]
+        uint8 (E8M0)."""
+        q = _c(q, np.uint8)
+        scales = _c(scales, np.uint8)
+        K = q.shape[-1] * 2
+        assert scales.shape[:-1] == q.shape[:-1] and scales.shape[-1] * 32 == K
+        rows = int(np.prod(q.shape[:-1]))
+        out = np.empty(q.shape[:-1] + (K,), np.float64)
+        rc = self.L.oracle_dequant_mxfp4(rows, K, _p(q), _p(scales), _p(out, _f64p))
+        _check(rc, "oracle_dequant_mxfp4")
+        return out
 
     def expert_capacity(self, T, k, E, factor):
         """ceil(factor * T*k / E)."""
@@ -276,3 +291,7 @@ def expert_capacity(*a, **kw):
 
 def balance(*a, **kw):
     return default().balance(*a, **kw)
+
+
+def dequant_mxfp4(*a, **kw):
+    return default().dequant_mxfp4(*a, **kw)

@@ -367,6 +367,39 @@ int oracle_down_rows(int64_t n, const int32_t* expert, int64_t d, int64_t f,
   return fail ? -2 : 0;
 }
 
+/* ------------------------------------------------------- MXFP4 weights */
+
+/* One FP4 (E2M1) element: bit 3 sign, bits 2-1 exponent e, bit 0 mantissa
+ * m; e = 0 encodes m * 1/2 (subnormal), otherwise 2^(e-1) * (1 + m/2). */
+static double e2m1_value(unsigned code) {
+  unsigned e = (code >> 1) & 3u, m = code & 1u;
+  double mag = e == 0 ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+  return (code & 8u) ? -mag : mag;
+}
+
+/* Dequantise an MXFP4 matrix [rows, K] (the OCP Microscaling format that
+ * the aitoday page names as the model's native quantisation, section "From
+ * Dense to Sparse"; its layout is the OCP specification's, which the pages
+ * do not give): each run of 32 consecutive elements of a row shares one
+ * E8M0 scale byte X, value 2^(X - 127) (X = 255: NaN); elements are FP4
+ * E2M1, two per byte, element 2i in the low nibble of byte i.
+ * q: [rows, K/2] bytes, scales: [rows, K/32] bytes, out: [rows, K] fp64. */
+int oracle_dequant_mxfp4(int64_t rows, int64_t K, const uint8_t* q,
+                         const uint8_t* scales, double* out) {
+  if (rows < 0 || K < 0 || K % 32 != 0) return -1;
+  if (rows > 0 && K > 0 && (!q || !scales || !out)) return -1;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t i = 0; i < K; ++i) {
+      uint8_t byte = q[r * (K / 2) + i / 2];
+      unsigned code = (i % 2 == 0) ? (byte & 15u) : (byte >> 4);
+      uint8_t x = scales[r * (K / 32) + i / 32];
+      double scale = x == 255 ? NAN : ldexp(1.0, (int)x - 127);
+      out[r * K + i] = e2m1_value(code) * scale;
+    }
+  }
+  return 0;
+}
+
 /* ---------------------------------------------------------------- combine */
 
 int oracle_combine(int64_t T, int64_t k, int64_t S, int64_t d, int dt,

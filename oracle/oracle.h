@@ -105,6 +105,13 @@ int oracle_gate_up_rows(int64_t n, const int64_t* tok, const int32_t* expert,
 int oracle_down_rows(int64_t n, const int32_t* expert, int64_t d, int64_t f,
                      int dt, const void* act, const void* W_down, double* out);
 
+/* MXFP4 weights (OCP Microscaling, FP4 E2M1 elements, one E8M0 scale per
+ * 32 consecutive elements of a row, element 2i in the low nibble of byte
+ * i): dequantise q [rows, K/2] with scales [rows, K/32] into out [rows, K]
+ * fp64.  K must be a multiple of 32. */
+int oracle_dequant_mxfp4(int64_t rows, int64_t K, const uint8_t* q,
+                         const uint8_t* scales, double* out);
+
 /* Weighted combine of expert-output rows stored in permuted order
  * (element type dt, [T*k + S*T, d]):
  * y[t] = sum_j w[t,j] * O[slot_pos[t*k+j]] + sum_sigma O[T*k + sigma*T + t]. */

@@ -565,4 +565,78 @@ def pin_balance_library(orc):
         assert loss > 0
 
 
+# --------------------------------------------------------- MXFP4 weights
+
+# FP4 E2M1 magnitudes of codes 0..7 as the OCP Microscaling specification
+# tabulates them (code | 8 is the negative)
+E2M1_TABLE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def np_dequant_mxfp4(q, sc):
+    """Table lookup: codes from the nibbles (even element low), magnitudes
+    from the specification's table, times 2^(X - 127) per 32-element block."""
+    q = np.asarray(q, np.uint8)
+    codes = np.stack([q & 15, q >> 4], axis=-1).reshape(q.shape[:-1] + (q.shape[-1] * 2,))
+    mag = E2M1_TABLE[codes & 7]
+    val = np.where(codes & 8, -mag, mag)
+    scale = np.where(sc == 255, np.nan, np.ldexp(1.0, sc.astype(np.int64) - 127))
+    return val * np.repeat(scale, 32, axis=-1)
+
+
+def pin_mxfp4_codes_and_scales(orc):
+    """Every byte value in both nibble positions against the table; every
+    E8M0 exponent (255 is NaN); one scale per 32-element block."""
+    q = np.arange(256, dtype=np.uint8).reshape(8, 32)        # K = 64 per row
+    sc = np.array([[127, 127]] * 8, np.uint8)
+    got = orc.dequant_mxfp4(q, sc)
+    assert np.array_equal(got, np_dequant_mxfp4(q, sc))
+    assert got[0, 2] == 0.5 and got[0, 3] == 0.0                # byte 0x01
+    assert got[0, 34] == 0.5 and got[0, 35] == 0.5              # byte 0x11
+    assert got[1, 30] == -6.0 and got[1, 31] == 1.0             # byte 0x2f
+    b = q.reshape(-1)
+    lo = np.where(b & 8, -E2M1_TABLE[b & 7], E2M1_TABLE[b & 7])
+    hi = np.where((b >> 4) & 8, -E2M1_TABLE[(b >> 4) & 7], E2M1_TABLE[(b >> 4) & 7])
+    flat = got.reshape(-1)
+    assert np.array_equal(flat[0::2], lo) and np.array_equal(flat[1::2], hi)
+    # scales: code 2 (1.0) everywhere, exponent X in every block
+    X = np.arange(256, dtype=np.uint8).reshape(4, 64)
+    q1 = np.full((4, 64 * 16), 0x22, np.uint8)                  # K = 2048 per row
+    v = orc.dequant_mxfp4(q1, X)
+    want = np.repeat(np.where(X == 255, np.nan, 2.0 ** (X.astype(np.float64) - 127)), 32, axis=1)
+    assert np.array_equal(np.isnan(v), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(v[ok], want[ok])
+    # blocks are 32 elements of one row: changing one scale byte moves
+    # exactly that block
+    q2 = np.full((2, 32), 0x44, np.uint8)                       # 2.0 everywhere, K = 64
+    s2 = np.array([[127, 127], [127, 127]], np.uint8)
+    base = orc.dequant_mxfp4(q2, s2)
+    s2[1, 0] = 128
+    moved = orc.dequant_mxfp4(q2, s2)
+    diff = moved != base
+    assert diff[1, :32].all() and not diff[1, 32:].any() and not diff[0].any()
+
+
+def pin_mxfp4_layer(orc):
+    """A layer with MXFP4 expert weights is the bf16 layer on the dequantised
+    weights; the dequantised values of the synthetic scale range are exact in
+    float32, and the numpy table lookup agrees with the oracle everywhere."""
+    cfg = moe_synth.tiny_config(T=9, d=64, f=32, E=5, k=2, S=1, dtype="bf16")
+    inp = moe_synth.make_layer_inputs(cfg, 46, experts=False)
+    mx = moe_synth.make_mxfp4_experts(cfg, 46)
+    wgu = orc.dequant_mxfp4(mx["Wq_gate_up"], mx["Ws_gate_up"])
+    wd = orc.dequant_mxfp4(mx["Wq_down"], mx["Ws_down"])
+    assert np.array_equal(wgu, np_dequant_mxfp4(mx["Wq_gate_up"], mx["Ws_gate_up"]))
+    assert np.array_equal(wd, np_dequant_mxfp4(mx["Wq_down"], mx["Ws_down"]))
+    assert np.array_equal(wgu.astype(np.float32).astype(np.float64), wgu)
+    x32 = moe_synth.bf16_bits_to_f32(inp["x"])
+    wr32 = moe_synth.bf16_bits_to_f32(inp["W_router"])
+    y, idx, w = orc.layer_forward(x32, wr32, wgu.astype(np.float32), wd.astype(np.float32),
+                                  cfg.k, S=cfg.S)
+    y_ref, idx_ref, w_ref, _ = np_dense_layer(x32, wr32, wgu.astype(np.float32),
+                                              wd.astype(np.float32), cfg.k, S=cfg.S)
+    assert np.array_equal(idx, idx_ref)
+    assert rel_err(y, y_ref) <= 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

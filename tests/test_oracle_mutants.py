@@ -66,6 +66,19 @@ MUTANTS = {
     # balance: softmax without the bias
     "balance_bias_ignored": (
         "if (bias) pt[e] += (double)bias[e];", "(void)bias;"),
+    # MXFP4: the odd element taken from the low nibble
+    "mxfp4_nibbles_swapped": (
+        "unsigned code = (i % 2 == 0) ? (byte & 15u) : (byte >> 4);",
+        "unsigned code = (i % 2 == 0) ? (byte >> 4) : (byte & 15u);"),
+    # MXFP4: the subnormal code read as m * 1 instead of m * 1/2
+    "mxfp4_subnormal_wrong": (
+        "double mag = e == 0 ? 0.5 * (double)m :", "double mag = e == 0 ? 1.0 * (double)m :"),
+    # MXFP4: E8M0 bias off by one
+    "mxfp4_scale_bias": (
+        "ldexp(1.0, (int)x - 127);", "ldexp(1.0, (int)x - 126);"),
+    # MXFP4: one scale per 16 elements instead of 32
+    "mxfp4_block_16": (
+        "uint8_t x = scales[r * (K / 32) + i / 32];", "uint8_t x = scales[r * (K / 32) + (i / 16) % (K / 32)];"),
     # balance: KL with its arguments swapped
     "balance_kl_reversed": (
         "kl += u * (log(u) - log(importance[e] + 1e-8));",
