@@ -12,7 +12,8 @@ same interval also measured by HIP events on the stream the kernels run
 on), the roofline of the dominant kernel (the gate_up grouped GEMM), the
 fp64 CPU oracle's rate on the host cores, and, under "prefill", the same
 layer measurement for the Mixtral-8x7B-shaped prefill workload against the
-bf16 MFMA peak.  Each workload also reports, under layer.aux, the router
+bf16 MFMA peak; for decode workloads, under "mxfp4", the same layer with
+MXFP4 expert weights.  Each workload also reports, under layer.aux, the router
 auxiliaries: routing with the balance statistics against routing alone, and
 the layer with an expert capacity of 1.25 times the even share.
 """
@@ -49,6 +50,8 @@ def parse(argv=None):
     p.add_argument("--prefill-steps", type=int, default=20)
     p.add_argument("--no-aux", action="store_true",
                    help="skip the router-auxiliary timings (balance loss, capacity)")
+    p.add_argument("--no-mxfp4", action="store_true",
+                   help="skip the MXFP4-weight decode measurement")
     p.add_argument("--rotate", type=int, default=1,
                    help="use N device copies of the expert weights in turn, so that no step "
                         "finds the previous step's weights in a cache (default 1)")
@@ -280,6 +283,52 @@ class Layer:
         return ac, roof, layer
 
 
+def mxfp4_extra(torch, moe, L, steps):
+    """The same decode layer with MXFP4 expert weights (FP4 E2M1 codes, one
+    E8M0 scale per 32 weights, 0.53125 bytes per weight): layer time over
+    `steps` calls (HIP events), each GEMM alone, and the gate_up GEMM's
+    fraction of HBM peak on its algorithmic bytes."""
+    import moe_synth
+    cfg, s, d, v = L.cfg, L.s, L.d, L.views
+    mx = moe_synth.make_mxfp4_experts(cfg, L.seed)
+    dm = {k: torch.from_numpy(a).cuda() for k, a in mx.items()}
+    ws = torch.empty_like(L.ws)
+    y = torch.empty_like(L.y)
+    views = moe.workspace_views(s, ws)
+
+    def step():
+        moe.moe_layer_forward_mxfp4(s, d["x"], d["W_router"], d["bias"], dm["Wq_gate_up"],
+                                    dm["Ws_gate_up"], dm["Wq_down"], dm["Ws_down"], y, ws)
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    t_layer = time_calls(torch, step, steps)
+    n = max(20, min(steps, 200))
+    t_gu = time_calls(torch, lambda: moe.moe_grouped_gemm_gate_up_mxfp4(
+        s, d["x"], views["sorted_slot"], views["offsets"], dm["Wq_gate_up"], dm["Ws_gate_up"],
+        views["act"]), n)
+    t_dn = time_calls(torch, lambda: moe.moe_grouped_gemm_down_mxfp4(
+        s, views["act"], views["offsets"], dm["Wq_down"], dm["Ws_down"], views["expert_out"]), n)
+    counts = views["counts"].cpu().numpy()
+    G = cfg.E + cfg.S
+    active = int(sum(1 for g in range(G) if counts[g] > 0))
+    R = cfg.T * cfg.k + cfg.S * cfg.T
+    per_w = 0.5 + 1.0 / 32.0
+    gu_bytes = int(active * 2 * cfg.f * cfg.d * per_w) + cfg.T * cfg.d * 2 + R * cfg.f * 2
+    dn_bytes = int(active * cfg.d * cfg.f * per_w) + R * cfg.f * 2 + R * cfg.d * 2
+    layer_bytes = (int(active * 3 * cfg.f * cfg.d * per_w) + cfg.E * cfg.d * 2
+                   + 2 * cfg.T * cfg.d * 2)
+    return {"weights": "MXFP4 (FP4 E2M1, E8M0 scale per 32)", "active_experts": active,
+            "ms_per_step_hip_events": round(t_layer * 1e3, 4),
+            "tokens_per_s": round(cfg.T / t_layer, 1),
+            "layer_alg_bytes": layer_bytes,
+            "layer_hbm_frac": round(layer_bytes / t_layer / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_us": {"gate_up": round(t_gu * 1e6, 2), "down": round(t_dn * 1e6, 2)},
+            "gate_up_alg_bytes": gu_bytes,
+            "gate_up_hbm_frac": round(gu_bytes / t_gu / 1e9 / HBM_PEAK_GBS, 4),
+            "down_hbm_frac": round(dn_bytes / t_dn / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def config_dict(cfg, seed, ac, rot):
     return {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
             "k": cfg.k, "shared": cfg.S, "zipf_s": cfg.zipf_s, "seed": seed,
@@ -353,6 +402,10 @@ def main(argv=None):
                                          / HBM_PEAK_GBS, 4)
     if not args.no_aux:
         layer["aux"] = L.aux_times(torch, max(20, min(args.steps, 100)))
+    mx = None
+    if not args.no_mxfp4 and cfg.T <= 64 and cfg.dtype == "bf16" and cfg.d % 32 == 0 \
+            and cfg.f % 32 == 0:
+        mx = mxfp4_extra(torch, moe, L, args.steps)
 
     out = {
         "metric": "MoE layer tokens/s",
@@ -372,6 +425,8 @@ def main(argv=None):
         "layer": layer,
         "cpu_baseline": None,
     }
+    if mx is not None:
+        out["mxfp4"] = mx
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, L.inp, args.cpu_seconds)
     if not args.no_prefill and args.config != PREFILL_CONFIG:

@@ -265,6 +265,47 @@ int moe_layer_forward_capacity(const moe_shape* s, const void* x,
                                int64_t capacity, void* y, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------- MXFP4 expert weights
+ * The expert GEMMs and the whole layer with expert weights in MXFP4 (the
+ * model-native quantisation that the aitoday "MoEs in Transformers" page,
+ * section "From Dense to Sparse", expects faster kernels from; per-expert
+ * quantisation in the packed layout: section "Dynamic Weight Loading with
+ * WeightConverter").  Weight-only: x, act, expert_out, y and the router stay
+ * bf16, so results are those of the bf16 entry points on the dequantised
+ * weights (exact bf16 numbers).
+ * Format (OCP Microscaling; the pages name it without defining it): FP4
+ * E2M1 elements (bit 3 sign, bits 2-1 exponent e, bit 0 mantissa m: e = 0
+ * gives m/2, else 2^(e-1)(1 + m/2)), two per byte with the even element in
+ * the low nibble; one E8M0 scale byte X per 32 consecutive elements of a
+ * weight row, factor 2^(X-127).  X = 255 (NaN in the format) is not
+ * supported: the kernels read it as 2^128 and give inf or NaN.
+ *   Wq_gate_up [E+S, 2f, d/2] uint8, Ws_gate_up [E+S, 2f, d/32] uint8
+ *   Wq_down    [E+S, d, f/2]  uint8, Ws_down    [E+S, d, f/32]  uint8
+ * (the packed bf16 layouts with each row's K elements packed).
+ * Shapes: dt = MOE_DT_BF16, T <= 64 (decode batches), d and f multiples of
+ * 32; others get MOE_ERR_UNSUPPORTED.  Weight tensors 16-byte aligned.
+ * Experts without rows read none of their weights. */
+int moe_grouped_gemm_gate_up_mxfp4(const moe_shape* s, const void* x,
+                                   const int32_t* sorted_slot,
+                                   const int32_t* offsets,
+                                   const uint8_t* Wq_gate_up,
+                                   const uint8_t* Ws_gate_up, void* act,
+                                   void* stream);
+
+int moe_grouped_gemm_down_mxfp4(const moe_shape* s, const void* act,
+                                const int32_t* offsets, const uint8_t* Wq_down,
+                                const uint8_t* Ws_down, void* expert_out,
+                                void* stream);
+
+/* Steps 1-5 with MXFP4 expert weights (route, permute, the two MXFP4
+ * GEMMs, combine); workspace as moe_layer_forward (same size and layout). */
+int moe_layer_forward_mxfp4(const moe_shape* s, const void* x,
+                            const void* W_router, const float* bias,
+                            const uint8_t* Wq_gate_up, const uint8_t* Ws_gate_up,
+                            const uint8_t* Wq_down, const uint8_t* Ws_down,
+                            void* y, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* ------------------------------------------- whole layer, no allocation
  * moe_layer_forward_static: moe_layer_forward with the intermediates in a
  * static device array of the library instead of a caller workspace, for

@@ -36,7 +36,8 @@ ENTRY_POINTS = ("moe_status_string", "moe_version", "moe_last_hip_error", "moe_r
                 "moe_layer_forward", "moe_layer_forward_static",
                 "moe_route_balance_workspace_size", "moe_route_balance",
                 "moe_permute_capacity", "moe_expert_capacity",
-                "moe_layer_forward_capacity")
+                "moe_layer_forward_capacity", "moe_grouped_gemm_gate_up_mxfp4",
+                "moe_grouped_gemm_down_mxfp4", "moe_layer_forward_mxfp4")
 
 # size of the library's static intermediate array (include/moe.h)
 STATIC_SCRATCH_BYTES = 32 << 20
@@ -103,6 +104,10 @@ def _load():
         "moe_permute_capacity": [sp, vp, i64, vp, vp, vp, vp, vp],
         "moe_layer_forward_capacity": [sp, vp, vp, vp, vp, vp, i64, vp, vp, ctypes.c_size_t,
                                        vp],
+        "moe_grouped_gemm_gate_up_mxfp4": [sp, vp, vp, vp, vp, vp, vp, vp],
+        "moe_grouped_gemm_down_mxfp4": [sp, vp, vp, vp, vp, vp, vp],
+        "moe_layer_forward_mxfp4": [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                    vp],
     }
     for name, argtypes in sigs.items():
         fn = getattr(L, name)
@@ -363,6 +368,53 @@ def moe_layer_forward_static(s: moe_shape, x, W_router, bias, W_gate_up, W_down,
           _ptr(W_down, s.G * s.d * s.f, fd, "W_down"),
           _ptr(y, s.T * s.d, fd, "y"),
           _stream(stream))
+
+
+def moe_grouped_gemm_gate_up_mxfp4(s: moe_shape, x, sorted_slot, offsets, Wq_gate_up,
+                                   Ws_gate_up, act, stream=None):
+    torch = _torch()
+    i32, u8, fd = torch.int32, torch.uint8, _float_dtype(s)
+    _call("moe_grouped_gemm_gate_up_mxfp4", ctypes.byref(s),
+          _ptr(x, s.T * s.d, fd, "x"),
+          _ptr(sorted_slot, s.T * s.k, i32, "sorted_slot"),
+          _ptr(offsets, s.G + 1, i32, "offsets"),
+          _ptr(Wq_gate_up, s.G * 2 * s.f * (s.d // 2), u8, "Wq_gate_up"),
+          _ptr(Ws_gate_up, s.G * 2 * s.f * (s.d // 32), u8, "Ws_gate_up"),
+          _ptr(act, s.R * s.f, fd, "act"),
+          _stream(stream))
+
+
+def moe_grouped_gemm_down_mxfp4(s: moe_shape, act, offsets, Wq_down, Ws_down, expert_out,
+                                stream=None):
+    torch = _torch()
+    i32, u8, fd = torch.int32, torch.uint8, _float_dtype(s)
+    _call("moe_grouped_gemm_down_mxfp4", ctypes.byref(s),
+          _ptr(act, s.R * s.f, fd, "act"),
+          _ptr(offsets, s.G + 1, i32, "offsets"),
+          _ptr(Wq_down, s.G * s.d * (s.f // 2), u8, "Wq_down"),
+          _ptr(Ws_down, s.G * s.d * (s.f // 32), u8, "Ws_down"),
+          _ptr(expert_out, s.R * s.d, fd, "expert_out"),
+          _stream(stream))
+
+
+def moe_layer_forward_mxfp4(s: moe_shape, x, W_router, bias, Wq_gate_up, Ws_gate_up, Wq_down,
+                            Ws_down, y, workspace, stream=None):
+    """The layer with MXFP4 expert weights (moe_layer_forward's workspace)."""
+    torch = _torch()
+    u8, fd = torch.uint8, _float_dtype(s)
+    if workspace is None:
+        raise ValueError("workspace must be a uint8 GPU tensor")
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _call("moe_layer_forward_mxfp4", ctypes.byref(s),
+          _ptr(x, s.T * s.d, fd, "x"),
+          _ptr(W_router, s.E * s.d, fd, "W_router"),
+          _ptr(bias, s.E, torch.float32, "bias", optional=True),
+          _ptr(Wq_gate_up, s.G * 2 * s.f * (s.d // 2), u8, "Wq_gate_up"),
+          _ptr(Ws_gate_up, s.G * 2 * s.f * (s.d // 32), u8, "Ws_gate_up"),
+          _ptr(Wq_down, s.G * s.d * (s.f // 2), u8, "Wq_down"),
+          _ptr(Ws_down, s.G * s.d * (s.f // 32), u8, "Ws_down"),
+          _ptr(y, s.T * s.d, fd, "y"),
+          ws_ptr, ws_bytes, _stream(stream))
 
 
 def workspace_views(s: moe_shape, workspace) -> dict:

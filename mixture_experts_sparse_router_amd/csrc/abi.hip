@@ -54,6 +54,16 @@ int check_shape(const moe_shape* m) {
   return MOE_OK;
 }
 
+// Shapes of the MXFP4 entry points: bf16 activations, decode-sized batches,
+// d and f multiples of the 32-element scale block.
+int check_mxfp4_shape(const moe_shape* m) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  if (m->dt != MOE_DT_BF16 || m->T > 64 || m->d % 32 != 0 || m->f % 32 != 0)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 // Tensors of the whole-layer entry points.
 int check_layer_ptrs(const Shape& s, const void* x, const void* W_router, const float* bias,
                      const void* W_gate_up, const void* W_down, const void* y) {
@@ -324,6 +334,74 @@ int moe_layer_forward_capacity(const moe_shape* m, const void* x, const void* W_
   if (capacity < 0) return MOE_ERR_INVALID_ARG;
   return layer_forward(m, x, W_router, bias, W_gate_up, W_down, capacity, y, workspace,
                        workspace_bytes, stream);
+}
+
+int moe_grouped_gemm_gate_up_mxfp4(const moe_shape* m, const void* x,
+                                   const int32_t* sorted_slot, const int32_t* offsets,
+                                   const uint8_t* Wq_gate_up, const uint8_t* Ws_gate_up,
+                                   void* act, void* stream) {
+  int rc = check_mxfp4_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(x, s.T * s.d) || !ok_ptr(sorted_slot, s.Tk()) || !ok_ptr(offsets, s.G() + 1) ||
+      !ok_ptr(Wq_gate_up, s.G() * 2 * s.f * s.d / 2) || !ok_ptr(Ws_gate_up, s.G() * 2 * s.f) ||
+      !ok_ptr(act, s.R() * s.f))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_stream_mx(true, s, x, sorted_slot, offsets, Wq_gate_up, Ws_gate_up,
+                                     act, s.d, s.f, (hipStream_t)stream));
+}
+
+int moe_grouped_gemm_down_mxfp4(const moe_shape* m, const void* act, const int32_t* offsets,
+                                const uint8_t* Wq_down, const uint8_t* Ws_down,
+                                void* expert_out, void* stream) {
+  int rc = check_mxfp4_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(act, s.R() * s.f) || !ok_ptr(offsets, s.G() + 1) ||
+      !ok_ptr(Wq_down, s.G() * s.d * s.f / 2) || !ok_ptr(Ws_down, s.G() * s.d) ||
+      !ok_ptr(expert_out, s.R() * s.d))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_stream_mx(false, s, act, nullptr, offsets, Wq_down, Ws_down,
+                                     expert_out, s.f, s.d, (hipStream_t)stream));
+}
+
+int moe_layer_forward_mxfp4(const moe_shape* m, const void* x, const void* W_router,
+                            const float* bias, const uint8_t* Wq_gate_up,
+                            const uint8_t* Ws_gate_up, const uint8_t* Wq_down,
+                            const uint8_t* Ws_down, void* y, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int rc = check_mxfp4_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(x, s.T * s.d) || !ok_ptr(W_router, s.E * s.d) || !ok_ptr(y, s.T * s.d) ||
+      !ok_ptr(Wq_gate_up, s.G() * 2 * s.f * s.d / 2) || !ok_ptr(Ws_gate_up, s.G() * 2 * s.f) ||
+      !ok_ptr(Wq_down, s.G() * s.d * s.f / 2) || !ok_ptr(Ws_down, s.G() * s.d))
+    return MOE_ERR_INVALID_ARG;
+  if (bias && ((uintptr_t)bias & 3u)) return MOE_ERR_INVALID_ARG;
+  size_t off[MOE_WS_COUNT], total;
+  layout(s, off, &total);
+  if (workspace_bytes < total) return MOE_ERR_WORKSPACE;
+  if (total > 0 && (!workspace || ((uintptr_t)workspace & 255u))) return MOE_ERR_INVALID_ARG;
+  if (s.T == 0) return MOE_OK;
+  char* ws = (char*)workspace;
+  int32_t* idx = (int32_t*)(ws + off[MOE_WS_TOPK_IDX]);
+  float* w = (float*)(ws + off[MOE_WS_TOPK_W]);
+  int32_t* counts = (int32_t*)(ws + off[MOE_WS_COUNTS]);
+  int32_t* offsets = (int32_t*)(ws + off[MOE_WS_OFFSETS]);
+  int32_t* sorted_slot = (int32_t*)(ws + off[MOE_WS_SORTED_SLOT]);
+  int32_t* slot_pos = (int32_t*)(ws + off[MOE_WS_SLOT_POS]);
+  void* act = ws + off[MOE_WS_ACT];
+  void* out = ws + off[MOE_WS_EXPERT_OUT];
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_route(s, x, W_router, bias, idx, w, nullptr, st);
+  if (e == hipSuccess) e = launch_permute(s, idx, -1, counts, offsets, sorted_slot, slot_pos, st);
+  if (e == hipSuccess)
+    e = launch_stream_mx(true, s, x, sorted_slot, offsets, Wq_gate_up, Ws_gate_up, act, s.d,
+                         s.f, st);
+  if (e == hipSuccess)
+    e = launch_stream_mx(false, s, act, nullptr, offsets, Wq_down, Ws_down, out, s.f, s.d, st);
+  if (e == hipSuccess) e = launch_combine(s, out, slot_pos, w, y, st);
+  return hip_status(e);
 }
 
 int moe_layer_forward_static(const moe_shape* m, const void* x, const void* W_router,

@@ -1,0 +1,207 @@
+// gemm_mx.hip -- grouped expert GEMMs with MXFP4 expert weights, for
+// decode-sized batches (at most 64 tokens), where the layer is bound by
+// reading the active experts' weights.
+//
+// The aitoday "MoEs in Transformers" page (section "From Dense to Sparse")
+// notes that generation would be faster still with kernels for the model's
+// native mxfp4 quantisation, and (section "Dynamic Weight Loading with
+// WeightConverter") that per-expert quantisation relies on the packed expert
+// layout.  Format (OCP Microscaling, which the pages name but do not
+// define): FP4 E2M1 elements, two per byte (even element in the low nibble),
+// and one E8M0 scale byte X (factor 2^(X-127)) for each run of 32
+// consecutive elements of a weight row.  Tensors keep the packed expert
+// layout of the bf16 weights:
+//   gate_up: Wq [G, 2f, d/2], Ws [G, 2f, d/32]   down: Wq [G, d, f/2], Ws [G, d, f/32]
+// Weight-only: activations stay bf16, so the layer computes exactly what the
+// bf16 layer computes on the dequantised weights (every dequantised value is
+// a bf16 number: 2 significant bits times a power of two).
+//
+// Same work split as the bf16 decode kernel (gemm_stream.hip): one
+// workgroup = 16 output columns of one expert for all of its rows, 4 waves
+// splitting K into 128-wide steps.  Lane (j = l%16, kb = l/16) loads, per K
+// step, the 32-element block [k0 + 32kb, +32) of weight row n0 + j: 16
+// contiguous bytes and its one scale byte (so 4 lanes cover 64 contiguous
+// bytes of a row).  gfx950 converts FP4 to bf16 with the scale applied in
+// one instruction per byte (v_cvt_scalef32_pk_bf16_fp4: byte -> two bf16,
+// low nibble first, times 2^(X-127) taken from the exponent field of the
+// fp32 scale operand); dword c of the block feeds 16x16x32 MFMA c, whose
+// token operand is the same lane's elements [k0 + 32kb + 8c, +8).  U steps
+// are loaded before any is used (U * MB bounded by 4), to keep enough bytes
+// in flight with a quarter of the bf16 kernel's weight bytes per step.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// Eight FP4 elements (one dword) times 2^(X-127) -> eight bf16 (one MFMA
+// operand).  scale: fp32 whose exponent field is X.
+__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t w, float scale) {
+  return u32x4{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3))};
+}
+
+template <bool GATED, int MB>
+struct MxStep {
+  u32x4 qg, qu;      // 32 packed FP4 elements of the gate (and up) row
+  uint32_t sg, su;   // their E8M0 scale bytes
+  u32x4 a[MB][4];    // token rows' elements [k0 + 32kb + 8c, +8), c = 0..3
+  bool ok;           // the block lies inside K (else used as zeros)
+};
+
+template <bool GATED, int MB, int U>
+__global__ __launch_bounds__(256) void stream_mx_kernel(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
+    const int32_t* __restrict__ offsets, const uint8_t* __restrict__ Wq,
+    const uint8_t* __restrict__ Ws, bf16_t* __restrict__ out, int64_t K, int64_t N,
+    int64_t T, int64_t Tk, int64_t k, int G, int ntiles) {
+  __shared__ f32x4 red[3][MB][2][64];  // partials of waves 1..3
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = (int)blockIdx.x / ntiles;
+  if (g >= G) return;
+  const int tile = (int)blockIdx.x % ntiles;
+  const int j = lane & 15, kb = lane >> 4;
+  const int64_t col = (int64_t)tile * 16 + j;
+  const bool col_ok = col < N;
+  const int64_t colc = col_ok ? col : N - 1;
+  const int64_t row_begin = offsets[g];
+  const int64_t rows = offsets[g + 1] - row_begin;
+  if (rows <= 0) return;  // empty expert: its weights are never read
+
+  const int64_t wrow = (int64_t)g * (GATED ? 2 * N : N) + colc;  // gate (or down) row
+  const uint8_t* qg = Wq + wrow * (K / 2);
+  const uint8_t* qu = qg + N * (K / 2);  // up row (GATED only)
+  const uint8_t* sgp = Ws + wrow * (K / 32);
+  const uint8_t* sup = sgp + N * (K / 32);
+
+  for (int64_t m0 = 0; m0 < rows; m0 += 16 * MB) {
+    const bf16_t* Ap[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      int64_t r = m0 + mb * 16 + j;
+      if (r >= rows) r = rows - 1;  // padding rows repeat a valid row
+      const int64_t grow = row_begin + r;
+      Ap[mb] = A + (GATED ? row_token(grow, sorted_slot, Tk, k, T) : grow) * K;
+    }
+    f32x4 accg[MB], accu[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      accg[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accu[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // wave w takes the K steps w, w+4, ...; U of them per round
+    for (int64_t k0 = (int64_t)wave * 128; k0 < K; k0 += 512 * U) {
+      MxStep<GATED, MB> st[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t kk = k0 + 512 * u + 32 * kb;  // the lane's 32-element block
+        st[u].ok = kk < K;
+        const int64_t ka = st[u].ok ? kk : 0;  // past K: block 0, zeroed at use
+        st[u].qg = ldg16(qg + ka / 2);
+        st[u].sg = sgp[ka / 32];
+        if constexpr (GATED) {
+          st[u].qu = ldg16(qu + ka / 2);
+          st[u].su = sup[ka / 32];
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) st[u].a[mb][c] = ldg16(Ap[mb] + ka + 8 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = st[u].ok;
+        const float scg = __uint_as_float(st[u].sg << 23);
+        const float scu = __uint_as_float(st[u].su << 23);
+        const uint32_t wg[4] = {st[u].qg.x, st[u].qg.y, st[u].qg.z, st[u].qg.w};
+        const uint32_t wu[4] = {st[u].qu.x, st[u].qu.y, st[u].qu.z, st[u].qu.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 bg = zero_unless(ok, fp4x8_to_bf16(wg[c], scg));
+          u32x4 bu = bg;
+          if constexpr (GATED) bu = zero_unless(ok, fp4x8_to_bf16(wu[c], scu));
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const u32x4 a = zero_unless(ok, st[u].a[mb][c]);
+            accg[mb] = mfma16(a, bg, accg[mb]);
+            if constexpr (GATED) accu[mb] = mfma16(a, bu, accu[mb]);
+          }
+        }
+      }
+    }
+    // add the four K-split partials in wave order
+    if (wave > 0) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        red[wave - 1][mb][0][lane] = accg[mb];
+        if constexpr (GATED) red[wave - 1][mb][1][lane] = accu[mb];
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          accg[mb] += red[w][mb][0][lane];
+          if constexpr (GATED) accu[mb] += red[w][mb][1][lane];
+        }
+      }
+      // lane holds D[4*kb + q][j], q = 0..3
+      if (col_ok) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t r = m0 + mb * 16 + kb * 4 + q;
+            if (r < rows) {
+              const float v = GATED ? swiglu(accg[mb][q], accu[mb][q]) : accg[mb][q];
+              out[(row_begin + r) * N + col] = f32_to_bf16(v);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();  // red is reused by the next row pass
+  }
+}
+
+}  // namespace
+
+hipError_t launch_stream_mx(bool gated, const Shape& s, const void* A,
+                            const int32_t* sorted_slot, const int32_t* offsets,
+                            const uint8_t* Wq, const uint8_t* Ws, void* out, int64_t K,
+                            int64_t N, hipStream_t st) {
+  if (s.R() == 0) return hipSuccess;
+  const int G = (int)s.G();
+  const int ntiles = (int)((N + 15) / 16);
+  const unsigned grid = (unsigned)((int64_t)G * ntiles);
+  const int MB = (int)((s.T + 15) / 16);
+#define MOE_MX(gt, mb, u)                                                                  \
+  hipLaunchKernelGGL((stream_mx_kernel<gt, mb, u>), dim3(grid), dim3(256), 0, st,          \
+                     (const bf16_t*)A, sorted_slot, offsets, Wq, Ws, (bf16_t*)out, K, N, s.T, \
+                     s.Tk(), s.k, G, ntiles)
+  if (gated) {
+    switch (MB) {
+      case 1: MOE_MX(true, 1, 4); break;
+      case 2: MOE_MX(true, 2, 2); break;
+      case 3: MOE_MX(true, 3, 1); break;
+      default: MOE_MX(true, 4, 1); break;
+    }
+  } else {
+    switch (MB) {
+      case 1: MOE_MX(false, 1, 4); break;
+      case 2: MOE_MX(false, 2, 2); break;
+      case 3: MOE_MX(false, 3, 1); break;
+      default: MOE_MX(false, 4, 1); break;
+    }
+  }
+#undef MOE_MX
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -132,6 +132,12 @@ hipError_t launch_route(const Shape& s, const void* x, const void* W_router,
 hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int64_t capacity,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
                           int32_t* slot_pos, hipStream_t st);
+// MXFP4 expert weights (Wq packed FP4, Ws E8M0 scales), T <= 64, bf16
+// activations; gated selects the gate_up form.  K % 32 == 0.
+hipError_t launch_stream_mx(bool gated, const Shape& s, const void* A,
+                            const int32_t* sorted_slot, const int32_t* offsets,
+                            const uint8_t* Wq, const uint8_t* Ws, void* out, int64_t K,
+                            int64_t N, hipStream_t st);
 // Router load statistics from the logits: importance[E] (mean softmax
 // probability) and the balance loss; partial holds balance_partials(T) * E
 // doubles.

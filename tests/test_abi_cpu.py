@@ -16,12 +16,12 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def exported_functions():
     out = os.popen(f"nm -D --defined-only {moe.LIB_PATH}").read()
-    return sorted(set(re.findall(r" T (moe_[a-z_]+)$", out, flags=re.M)))
+    return sorted(set(re.findall(r" T (moe_[a-z0-9_]+)$", out, flags=re.M)))
 
 
 def test_header_and_library_agree():
@@ -232,3 +232,29 @@ def test_capacity_entry_points_check_arguments():
     # an empty batch needs no work at all
     assert L.moe_layer_forward_capacity(ctypes.byref(_shape(T=0)), None, p, None, p, p, 0, None,
                                         p, moe.workspace_size(_shape(T=0)), None) == moe.MOE_OK
+
+
+def test_mxfp4_entry_points_check_shapes_and_pointers():
+    L = moe.lib()
+    p = ctypes.c_void_p(4096)
+    good = moe.shape(16, 64, 96, 8, 2, 0, moe.MOE_DT_BF16)
+    need = moe.workspace_size(good)
+    for bad in (moe.shape(16, 64, 96, 8, 2, 0, moe.MOE_DT_F32),   # fp32 activations
+                moe.shape(65, 64, 96, 8, 2, 0, moe.MOE_DT_BF16),  # past decode size
+                moe.shape(16, 48, 96, 8, 2, 0, moe.MOE_DT_BF16),  # d not a multiple of 32
+                moe.shape(16, 64, 104, 8, 2, 0, moe.MOE_DT_BF16)):  # f not a multiple of 32
+        assert L.moe_grouped_gemm_gate_up_mxfp4(ctypes.byref(bad), p, p, p, p, p, p,
+                                                None) == moe.MOE_ERR_UNSUPPORTED
+        assert L.moe_grouped_gemm_down_mxfp4(ctypes.byref(bad), p, p, p, p, p,
+                                             None) == moe.MOE_ERR_UNSUPPORTED
+        assert L.moe_layer_forward_mxfp4(ctypes.byref(bad), p, p, None, p, p, p, p, p, p,
+                                         1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    odd = ctypes.c_void_p(4096 + 8)
+    assert L.moe_grouped_gemm_gate_up_mxfp4(ctypes.byref(good), p, p, p, odd, p, p,
+                                            None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_gemm_down_mxfp4(ctypes.byref(good), p, p, p, None, p,
+                                         None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_mxfp4(ctypes.byref(good), p, p, None, p, p, p, p, p, p,
+                                     need - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_layer_forward_mxfp4(ctypes.byref(_shape(k=0)), p, p, None, p, p, p, p, p, p,
+                                     need, None) == moe.MOE_ERR_INVALID_ARG
