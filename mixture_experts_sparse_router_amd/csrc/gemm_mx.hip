@@ -26,8 +26,11 @@
 // low nibble first, times 2^(X-127) taken from the exponent field of the
 // fp32 scale operand); dword c of the block feeds 16x16x32 MFMA c, whose
 // token operand is the same lane's elements [k0 + 32kb + 8c, +8).  U steps
-// are loaded before any is used (U * MB bounded by 4), to keep enough bytes
-// in flight with a quarter of the bf16 kernel's weight bytes per step.
+// are loaded before any is used, to keep enough bytes in flight with a
+// quarter of the bf16 kernel's weight bytes per step: for one block of 16
+// rows, U is the smallest of 2, 4, 6 whose round covers K (measured: at
+// K = 2880 one round of U = 6 beats two rounds of U = 4 by 20%, and U = 8
+// lowers occupancy); more rows leave fewer registers for steps.
 #include "moe_common.h"
 
 namespace moe {
@@ -53,13 +56,13 @@ struct MxStep {
   bool ok;           // the block lies inside K (else used as zeros)
 };
 
-template <bool GATED, int MB, int U>
-__global__ __launch_bounds__(256) void stream_mx_kernel(
+template <bool GATED, int MB, int U, int NW>
+__global__ __launch_bounds__(64 * NW) void stream_mx_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const uint8_t* __restrict__ Wq,
     const uint8_t* __restrict__ Ws, bf16_t* __restrict__ out, int64_t K, int64_t N,
     int64_t T, int64_t Tk, int64_t k, int G, int ntiles) {
-  __shared__ f32x4 red[3][MB][2][64];  // partials of waves 1..3
+  __shared__ f32x4 red[NW - 1][MB][2][64];  // partials of waves 1..NW-1
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = (int)blockIdx.x / ntiles;
   if (g >= G) return;
@@ -93,12 +96,12 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(
       accg[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
       accu[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // wave w takes the K steps w, w+4, ...; U of them per round
-    for (int64_t k0 = (int64_t)wave * 128; k0 < K; k0 += 512 * U) {
+    // wave w takes the K steps w, w+NW, ...; U of them per round
+    for (int64_t k0 = (int64_t)wave * 128; k0 < K; k0 += 128 * NW * U) {
       MxStep<GATED, MB> st[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t kk = k0 + 512 * u + 32 * kb;  // the lane's 32-element block
+        const int64_t kk = k0 + 128 * NW * u + 32 * kb;  // the lane's 32-element block
         st[u].ok = kk < K;
         const int64_t ka = st[u].ok ? kk : 0;  // past K: block 0, zeroed at use
         st[u].qg = ldg16(qg + ka / 2);
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(
         }
       }
     }
-    // add the four K-split partials in wave order
+    // add the NW K-split partials in wave order
     if (wave > 0) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-      for (int w = 0; w < 3; ++w) {
+      for (int w = 0; w < NW - 1; ++w) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           accg[mb] += red[w][mb][0][lane];
@@ -182,22 +185,33 @@ hipError_t launch_stream_mx(bool gated, const Shape& s, const void* A,
   const unsigned grid = (unsigned)((int64_t)G * ntiles);
   const int MB = (int)((s.T + 15) / 16);
 #define MOE_MX(gt, mb, u)                                                                  \
-  hipLaunchKernelGGL((stream_mx_kernel<gt, mb, u>), dim3(grid), dim3(256), 0, st,          \
+  hipLaunchKernelGGL((stream_mx_kernel<gt, mb, u, 4>), dim3(grid), dim3(256), 0, st,       \
                      (const bf16_t*)A, sorted_slot, offsets, Wq, Ws, (bf16_t*)out, K, N, s.T, \
                      s.Tk(), s.k, G, ntiles)
+  const int u1 = K <= 1024 ? 2 : K <= 2048 ? 4 : 6;  // steps per round, one row block
   if (gated) {
-    switch (MB) {
-      case 1: MOE_MX(true, 1, 4); break;
-      case 2: MOE_MX(true, 2, 2); break;
-      case 3: MOE_MX(true, 3, 1); break;
-      default: MOE_MX(true, 4, 1); break;
+    if (MB == 1) {
+      if (u1 == 2) MOE_MX(true, 1, 2);
+      else if (u1 == 4) MOE_MX(true, 1, 4);
+      else MOE_MX(true, 1, 6);
+    } else if (MB == 2) {
+      MOE_MX(true, 2, 2);
+    } else if (MB == 3) {
+      MOE_MX(true, 3, 1);
+    } else {
+      MOE_MX(true, 4, 1);
     }
   } else {
-    switch (MB) {
-      case 1: MOE_MX(false, 1, 4); break;
-      case 2: MOE_MX(false, 2, 2); break;
-      case 3: MOE_MX(false, 3, 1); break;
-      default: MOE_MX(false, 4, 1); break;
+    if (MB == 1) {
+      if (u1 == 2) MOE_MX(false, 1, 2);
+      else if (u1 == 4) MOE_MX(false, 1, 4);
+      else MOE_MX(false, 1, 6);
+    } else if (MB == 2) {
+      MOE_MX(false, 2, 2);
+    } else if (MB == 3) {
+      MOE_MX(false, 3, 1);
+    } else {
+      MOE_MX(false, 4, 1);
     }
   }
 #undef MOE_MX
