@@ -40,6 +40,9 @@ _SIGNATURES = {
     "oracle_expert_capacity": [_i64, _i64, _i64, ctypes.c_double],
     "oracle_balance": [_i64, _i64, _i64, _int, _vp, _vp, _f32p, _f64p, _f64p, _f64p],
     "oracle_dequant_mxfp4": [_i64, _i64, _vp, _vp, _f64p],
+    "oracle_layer_backward": [_i64, _i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _f32p, _vp,
+                              _vp, _vp, _i64, _i64p, _f64p, _i64, _i32p, _f64p, _f64p,
+                              _f64p, _f64p, _f64p],
     "oracle_gate_up_rows": [_i64, _i64p, _i32p, _i64, _i64, _int, _vp, _vp, _f64p],
     "oracle_down_rows": [_i64, _i32p, _i64, _i64, _int, _vp, _vp, _f64p],
     "oracle_combine": [_i64, _i64, _i64, _i64, _int, _vp, _i32p, _f64p, _f64p],
@@ -123,6 +126,44 @@ class Oracle:
             rc = self.L.oracle_permute_capacity(T, k, E, S, int(capacity), *args)
         _check(rc, "oracle_permute")
         return counts, offsets, sorted_slot, slot_pos
+
+    def layer_backward(self, x, W_router, W_gate_up, W_down, dy, k, S=0, bias=None,
+                       tokens=None, experts=(), router=True):
+        """Gradients of sum(y * dy).  Returns a dict: dx [n_tok, d] for the
+        listed tokens (all when tokens is None), dW_gate_up [n, 2f, d] and
+        dW_down [n, d, f] for the listed experts, and with router=True dW_router
+        [E, d], db [E], dw [T, k]; all fp64."""
+        x, W_router, W_gate_up, W_down, dy = (_c(a) for a in (x, W_router, W_gate_up,
+                                                               W_down, dy))
+        dt = _dt(x)
+        for a in (W_router, W_gate_up, W_down, dy):
+            assert _dt(a) == dt
+        T, d = x.shape
+        E = W_router.shape[0]
+        f = W_gate_up.shape[1] // 2
+        assert W_gate_up.shape == (E + S, 2 * f, d) and W_down.shape == (E + S, d, f)
+        assert dy.shape == (T, d)
+        b = None if bias is None else _c(bias, np.float32)
+        tl = None if tokens is None else _c(tokens, np.int64)
+        n_tok = T if tl is None else tl.shape[0]
+        el = _c(np.asarray(experts, np.int32).reshape(-1), np.int32)
+        n_exp = el.shape[0]
+        out = {"dx": np.empty((n_tok, d), np.float64),
+               "dW_gate_up": np.empty((n_exp, 2 * f, d), np.float64),
+               "dW_down": np.empty((n_exp, d, f), np.float64)}
+        if router:
+            out.update(dW_router=np.empty((E, d), np.float64), db=np.empty(E, np.float64),
+                       dw=np.empty((T, k), np.float64))
+        rc = self.L.oracle_layer_backward(
+            T, d, f, E, k, S, dt, _p(x), _p(W_router), _p(b, _f32p), _p(W_gate_up),
+            _p(W_down), _p(dy), n_tok, _p(tl, _i64p), _p(out["dx"], _f64p), n_exp,
+            _p(el, _i32p) if n_exp else None,
+            _p(out["dW_gate_up"], _f64p) if n_exp else None,
+            _p(out["dW_down"], _f64p) if n_exp else None,
+            _p(out.get("dW_router"), _f64p), _p(out.get("db"), _f64p),
+            _p(out.get("dw"), _f64p))
+        _check(rc, "oracle_layer_backward")
+        return out
 
     def dequant_mxfp4(self, q, scales):
         """fp64 values [..., K] of MXFP4 weights: q [..., K/2] uint8 (two FP4
@@ -295,3 +336,7 @@ def balance(*a, **kw):
 
 def dequant_mxfp4(*a, **kw):
     return default().dequant_mxfp4(*a, **kw)
+
+
+def layer_backward(*a, **kw):
+    return default().layer_backward(*a, **kw)

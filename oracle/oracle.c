@@ -524,3 +524,191 @@ int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
   free(keep);
   return fail ? -2 : 0;
 }
+
+/* --------------------------------------------------------------- backward */
+
+/* Gradients of the layer, the backward pass that grouped-GEMM training runs
+ * (aitoday "MoEs in Transformers" page, section "Training MoEs with
+ * Transformers").  They are the derivatives of the forward defined above
+ * by the chain rule, for a loss whose gradient with respect to y is dy:
+ *   y_t = sum_j w_tj O_tj + sum_s O_ts,   O = Wd_e a,   a = silu(g) * u,
+ *   [g; u] = Wgu_e x_t,   w_tj = exp(l_tj) / sum_{i<k} exp(l_ti),
+ *   l_te = Wr_e . x_t + b_e;
+ *   dO_tj = w_tj dy_t (shared experts: dy_t),  dw_tj = dy_t . O_tj,
+ *   da = Wd_e^T dO,  dg = da * u * silu'(g),  du = da * silu(g),
+ *   silu'(g) = s (1 + g (1 - s)) with s = 1 / (1 + e^-g),
+ *   dx_t += Wgu_e^T [dg; du],  dWd_e += dO a^T,  dWgu_e += [dg; du] x_t^T,
+ *   dl_tj = w_tj (dw_tj - sum_i w_ti dw_ti)   (softmax over the k selected),
+ *   dx_t += sum_j dl_tj Wr_{e_tj},  dWr_e += dl x_t,  db_e += dl.
+ * The choice of the k experts is piecewise constant in the logits: it has
+ * no gradient, and unselected experts get none.
+ * Outputs (fp64, each optional):
+ *   dx [n_tok, d] for the listed tokens (tok_list NULL: all T);
+ *   dWgu [n_exp, 2f, d] and dWd [n_exp, d, f] for the listed experts
+ *   (indices 0 .. E+S-1; shared experts after the routed ones);
+ *   dWr [E, d], db [E], dw [T, k].
+ * Tokens are visited in order and every sum is serial, in ascending index
+ * order (experts in slot order, then the shared ones, then the router). */
+int oracle_layer_backward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
+                          int64_t S, int dt, const void* x, const void* W_router,
+                          const float* bias, const void* W_gate_up,
+                          const void* W_down, const void* dy, int64_t n_tok,
+                          const int64_t* tok_list, double* dx, int64_t n_exp,
+                          const int32_t* exp_list, double* dWgu, double* dWd,
+                          double* dWr, double* db, double* dw) {
+  if (T < 0 || d < 1 || f < 1 || E < 1 || k < 1 || k > E || S < 0 || bad_dt(dt))
+    return -1;
+  if (!tok_list) n_tok = T;
+  if (n_tok < 0 || n_exp < 0) return -1;
+  if (T > 0 && (!x || !W_router || !W_gate_up || !W_down || !dy)) return -1;
+  if (n_tok > 0 && !dx) return -1;
+  if (n_exp > 0 && (!exp_list || !dWgu || !dWd)) return -1;
+  int64_t G = E + S;
+  int64_t* tok_pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
+  int64_t* exp_pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)G);
+  double* xt = (double*)malloc(sizeof(double) * (size_t)d);
+  double* lg = (double*)malloc(sizeof(double) * (size_t)E);
+  ranked* order = (ranked*)malloc(sizeof(ranked) * (size_t)E);
+  int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  double* w = (double*)malloc(sizeof(double) * (size_t)k);
+  double* dwt = (double*)malloc(sizeof(double) * (size_t)k);
+  double* g = (double*)malloc(sizeof(double) * (size_t)f);
+  double* u = (double*)malloc(sizeof(double) * (size_t)f);
+  double* a = (double*)malloc(sizeof(double) * (size_t)f);
+  double* da = (double*)malloc(sizeof(double) * (size_t)f);
+  double* dg = (double*)malloc(sizeof(double) * (size_t)f);
+  double* du = (double*)malloc(sizeof(double) * (size_t)f);
+  double* O = (double*)malloc(sizeof(double) * (size_t)d);
+  double* dO = (double*)malloc(sizeof(double) * (size_t)d);
+  double* dxt = (double*)malloc(sizeof(double) * (size_t)d);
+  int rc = 0;
+  if (!tok_pos || !exp_pos || !xt || !lg || !order || !idx || !w || !dwt || !g || !u ||
+      !a || !da || !dg || !du || !O || !dO || !dxt) {
+    rc = -2;
+    goto done;
+  }
+  for (int64_t t = 0; t < T; ++t) tok_pos[t] = -1;
+  for (int64_t q = 0; q < n_tok; ++q) {
+    int64_t t = tok_list ? tok_list[q] : q;
+    if (t < 0 || t >= T || tok_pos[t] >= 0) {
+      rc = -1;
+      goto done;
+    }
+    tok_pos[t] = q;
+  }
+  for (int64_t e = 0; e < G; ++e) exp_pos[e] = -1;
+  for (int64_t q = 0; q < n_exp; ++q) {
+    if (exp_list[q] < 0 || exp_list[q] >= G || exp_pos[exp_list[q]] >= 0) {
+      rc = -1;
+      goto done;
+    }
+    exp_pos[exp_list[q]] = q;
+  }
+  if (n_tok > 0) memset(dx, 0, sizeof(double) * (size_t)(n_tok * d));
+  if (n_exp > 0) {
+    memset(dWgu, 0, sizeof(double) * (size_t)(n_exp * 2 * f * d));
+    memset(dWd, 0, sizeof(double) * (size_t)(n_exp * d * f));
+  }
+  if (dWr) memset(dWr, 0, sizeof(double) * (size_t)(E * d));
+  if (db) memset(db, 0, sizeof(double) * (size_t)E);
+  int router_grads = dWr || db || dw;
+
+  for (int64_t t = 0; t < T; ++t) {
+    int listed = tok_pos[t] >= 0;
+    if (!listed && n_exp == 0 && !router_grads) continue;
+    route_token(t, d, E, k, dt, x, W_router, bias, NULL, xt, lg, order, idx, w);
+    for (int64_t c = 0; c < d; ++c) dxt[c] = 0.0;
+    for (int64_t j = 0; j < k + S; ++j) {
+      int routed = j < k;
+      int64_t e = routed ? idx[j] : E + (j - k);
+      double wj = routed ? w[j] : 1.0;
+      int want_e = exp_pos[e] >= 0;
+      int need_O = routed && (listed || router_grads);
+      if (!listed && !want_e && !need_O) continue;
+      /* forward through expert e: [g; u] = Wgu_e x_t, a = silu(g) * u */
+      int64_t base = 2 * f * e; /* first gate_up row of expert e */
+      for (int64_t n = 0; n < f; ++n) {
+        g[n] = dot_row(W_gate_up, dt, base + n, d, xt);
+        u[n] = dot_row(W_gate_up, dt, base + f + n, d, xt);
+        a[n] = g[n] / (1.0 + exp(-g[n])) * u[n];
+      }
+      if (need_O) {
+        /* dw_tj = dy_t . O_tj */
+        double acc = 0.0;
+        for (int64_t i = 0; i < d; ++i) {
+          O[i] = dot_row(W_down, dt, e * d + i, f, a);
+          acc += elem(dy, dt, t * d + i) * O[i];
+        }
+        dwt[j] = acc;
+      }
+      if (!listed && !want_e) continue;
+      /* dO = w dy_t; da = Wd_e^T dO; SwiGLU backward */
+      for (int64_t i = 0; i < d; ++i) dO[i] = wj * elem(dy, dt, t * d + i);
+      for (int64_t n = 0; n < f; ++n) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < d; ++i) acc += elem(W_down, dt, (e * d + i) * f + n) * dO[i];
+        da[n] = acc;
+        double sg = 1.0 / (1.0 + exp(-g[n]));
+        dg[n] = da[n] * u[n] * (sg * (1.0 + g[n] * (1.0 - sg)));
+        du[n] = da[n] * (g[n] * sg);
+      }
+      if (listed) {
+        /* dx_t += Wgu_e^T [dg; du] */
+        for (int64_t c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int64_t n = 0; n < f; ++n) {
+            acc += elem(W_gate_up, dt, (base + n) * d + c) * dg[n];
+            acc += elem(W_gate_up, dt, (base + f + n) * d + c) * du[n];
+          }
+          dxt[c] += acc;
+        }
+      }
+      if (want_e) {
+        double* gd = dWd + exp_pos[e] * d * f;
+        double* gu = dWgu + exp_pos[e] * 2 * f * d;
+        for (int64_t i = 0; i < d; ++i)
+          for (int64_t n = 0; n < f; ++n) gd[i * f + n] += dO[i] * a[n];
+        for (int64_t n = 0; n < f; ++n)
+          for (int64_t c = 0; c < d; ++c) {
+            gu[n * d + c] += dg[n] * xt[c];
+            gu[(f + n) * d + c] += du[n] * xt[c];
+          }
+      }
+    }
+    if (listed || router_grads) {
+      /* softmax over the k selected logits: dl_j = w_j (dw_j - sum_i w_i dw_i) */
+      double sw = 0.0;
+      for (int64_t j = 0; j < k; ++j) sw += w[j] * dwt[j];
+      for (int64_t j = 0; j < k; ++j) {
+        double dl = w[j] * (dwt[j] - sw);
+        int64_t e = idx[j];
+        if (listed)
+          for (int64_t c = 0; c < d; ++c) dxt[c] += dl * elem(W_router, dt, e * d + c);
+        if (dWr)
+          for (int64_t c = 0; c < d; ++c) dWr[e * d + c] += dl * xt[c];
+        if (db) db[e] += dl;
+        if (dw) dw[t * k + j] = dwt[j];
+      }
+    }
+    if (listed) memcpy(dx + tok_pos[t] * d, dxt, sizeof(double) * (size_t)d);
+  }
+done:
+  free(tok_pos);
+  free(exp_pos);
+  free(xt);
+  free(lg);
+  free(order);
+  free(idx);
+  free(w);
+  free(dwt);
+  free(g);
+  free(u);
+  free(a);
+  free(da);
+  free(dg);
+  free(du);
+  free(O);
+  free(dO);
+  free(dxt);
+  return rc;
+}

@@ -134,6 +134,20 @@ int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
                          int64_t capacity, int32_t* idx_out, double* w_out,
                          double* y);
 
+/* Backward pass: gradients of sum(y * dy) (dy [T, d], element type dt) with
+ * respect to x (listed tokens; tok_list NULL: all T), the listed experts'
+ * gate_up and down weights (exp_list, indices 0 .. E+S-1), the router
+ * weights and bias, and the routing weights (dw [T, k]); all fp64, each
+ * optional.  dx [n_tok, d], dWgu [n_exp, 2f, d], dWd [n_exp, d, f],
+ * dWr [E, d], db [E]. */
+int oracle_layer_backward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
+                          int64_t S, int dt, const void* x, const void* W_router,
+                          const float* bias, const void* W_gate_up,
+                          const void* W_down, const void* dy, int64_t n_tok,
+                          const int64_t* tok_list, double* dx, int64_t n_exp,
+                          const int32_t* exp_list, double* dWgu, double* dWd,
+                          double* dWr, double* db, double* dw);
+
 /* Number of OpenMP threads the oracle uses (for reporting). */
 int oracle_num_threads(void);
 

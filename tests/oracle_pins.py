@@ -639,4 +639,117 @@ def pin_mxfp4_layer(orc):
     assert rel_err(y, y_ref) <= 1e-12
 
 
+# ------------------------------------------------------------- backward
+
+def torch_dense_grads(x, Wr, Wgu, Wd, dy, k, S=0, bias=None):
+    """Independent gradients: the layer written densely in torch (fp64 on
+    the CPU, every expert evaluated on every token, the top-k taken by
+    torch.topk on detached logits, softmax over the selected logits) and
+    differentiated by autograd."""
+    import torch
+    t = lambda a: torch.tensor(wide(a), dtype=torch.float64, requires_grad=True)
+    X, WR, WGU, WD = t(x), t(Wr), t(Wgu), t(Wd)
+    B = torch.tensor(np.asarray(bias, np.float64) if bias is not None
+                     else np.zeros(Wr.shape[0]), dtype=torch.float64, requires_grad=True)
+    DY = torch.tensor(wide(dy), dtype=torch.float64)
+    E = Wr.shape[0]
+    f = Wgu.shape[1] // 2
+    L = X @ WR.T + B
+    sel = torch.topk(L.detach(), k, dim=1).indices
+    w = torch.softmax(torch.gather(L, 1, sel), dim=1)
+    outs = []
+    for e in range(E + S):
+        g = X @ WGU[e, :f].T
+        u = X @ WGU[e, f:].T
+        outs.append((torch.nn.functional.silu(g) * u) @ WD[e].T)
+    outs = torch.stack(outs, 1)                                   # [T, E+S, d]
+    y = (w.unsqueeze(2) * torch.gather(outs[:, :E], 1,
+                                       sel.unsqueeze(2).expand(-1, -1, outs.shape[2]))).sum(1)
+    if S:
+        y = y + outs[:, E:].sum(1)
+    w.retain_grad()
+    (y * DY).sum().backward()
+    return dict(dx=X.grad.numpy(), dW_gate_up=WGU.grad.numpy(), dW_down=WD.grad.numpy(),
+                dW_router=WR.grad.numpy(), db=B.grad.numpy(), dw=w.grad.numpy(),
+                sel=sel.numpy())
+
+
+def pin_backward_autograd(orc):
+    """Every gradient against torch autograd on a dense formulation, fp32
+    and bf16 inputs, with a shared expert and a router bias."""
+    for (T, d, f, E, k, S, dt, seed) in ((10, 8, 6, 5, 2, 0, "f32", 50),
+                                         (7, 16, 8, 6, 3, 1, "bf16", 51)):
+        x, Wr, Wgu, Wd = rand_layer(seed, T, d, f, E, k, S, dt)
+        dy = moe_synth.normal((seed, 6, 0), (T, d), 1.0, dt)
+        bias = np.linspace(0.3, -0.2, E).astype(np.float32)
+        ref = torch_dense_grads(x, Wr, Wgu, Wd, dy, k, S, bias)
+        got = orc.layer_backward(x, Wr, Wgu, Wd, dy, k, S=S, bias=bias,
+                                 experts=np.arange(E + S))
+        _, idx, _ = orc.route(x, Wr, k, bias=bias)
+        assert np.array_equal(np.sort(idx, 1), np.sort(ref["sel"], 1))
+        for name in ("dx", "dW_gate_up", "dW_down", "dW_router", "db"):
+            assert rel_err(got[name], ref[name]) <= 1e-12, (name, rel_err(got[name], ref[name]))
+        # dw: slot order of the oracle (rank order) vs torch.topk's order
+        for t in range(T):
+            order = [list(ref["sel"][t]).index(e) for e in idx[t]]
+            assert np.max(np.abs(got["dw"][t] - ref["dw"][t, order])) <= 1e-12
+
+
+def pin_backward_finite_differences(orc):
+    """Central differences of L = sum(y * dy) through the oracle's own
+    forward: perturbations by 2^-12, exact in float32, that move no expert
+    in or out of any token's top-k."""
+    T, d, f, E, k, S = 6, 8, 6, 4, 2, 1
+    x, Wr, Wgu, Wd = rand_layer(52, T, d, f, E, k, S, "f32")
+    Wr = Wr * 3.0                       # clear logit gaps: the selection holds
+    dy = moe_synth.normal((52, 6, 0), (T, d), 1.0, "f32")
+    bias = np.linspace(0.2, -0.1, E).astype(np.float32)
+    got = orc.layer_backward(x, Wr, Wgu, Wd, dy, k, S=S, bias=bias, experts=np.arange(E + S))
+    _, idx0, _ = orc.route(x, Wr, k, bias=bias)
+    h = 2.0 ** -12
+
+    def loss(x_, Wr_, Wgu_, Wd_, b_):
+        _, idx, _ = orc.route(x_, Wr_, k, bias=b_)
+        assert np.array_equal(idx, idx0), "perturbation changed the selection"
+        y, _, _ = orc.layer_forward(x_, Wr_, Wgu_, Wd_, k, S=S, bias=b_)
+        return float((y * wide(dy)).sum())
+
+    rng = np.random.default_rng([52, 9])
+    args = dict(x=x, Wr=Wr, Wgu=Wgu, Wd=Wd, b=bias)
+    grads = dict(x=got["dx"], Wr=got["dW_router"], Wgu=got["dW_gate_up"], Wd=got["dW_down"],
+                 b=got["db"])
+    for name in ("x", "Wr", "Wgu", "Wd", "b"):
+        for _ in range(4):
+            pos = tuple(int(rng.integers(0, n)) for n in args[name].shape)
+            plus = {kk: v.copy() for kk, v in args.items()}
+            minus = {kk: v.copy() for kk, v in args.items()}
+            plus[name][pos] += np.float32(h)
+            minus[name][pos] -= np.float32(h)
+            fd = (loss(plus["x"], plus["Wr"], plus["Wgu"], plus["Wd"], plus["b"])
+                  - loss(minus["x"], minus["Wr"], minus["Wgu"], minus["Wd"], minus["b"])) / (2 * h)
+            g = grads[name][pos]
+            assert abs(fd - g) <= 1e-5 * (1.0 + abs(g)), (name, pos, fd, g)
+
+
+def pin_backward_structure(orc):
+    """Experts that no token selects get zero weight gradients; the router
+    bias gradient sums to zero over the experts (each token's softmax
+    gradient over its k selected logits sums to zero); listing tokens or
+    experts changes nothing."""
+    T, d, f, E, k = 12, 8, 6, 6, 2
+    x, Wr, Wgu, Wd = rand_layer(53, T, d, f, E, k)
+    dy = moe_synth.normal((53, 6, 0), (T, d), 1.0, "f32")
+    bias = np.zeros(E, np.float32)
+    bias[4:] = -100.0                   # experts 4, 5 never selected
+    full = orc.layer_backward(x, Wr, Wgu, Wd, dy, k, bias=bias, experts=np.arange(E))
+    assert np.all(full["dW_gate_up"][4:] == 0) and np.all(full["dW_down"][4:] == 0)
+    assert np.all(full["dW_router"][4:] == 0) and np.all(full["db"][4:] == 0)
+    assert abs(full["db"].sum()) <= 1e-12 * np.abs(full["db"]).sum()
+    part = orc.layer_backward(x, Wr, Wgu, Wd, dy, k, bias=bias, tokens=[7, 2],
+                              experts=[3, 0], router=False)
+    assert np.array_equal(part["dx"], full["dx"][[7, 2]])
+    assert np.array_equal(part["dW_gate_up"], full["dW_gate_up"][[3, 0]])
+    assert np.array_equal(part["dW_down"], full["dW_down"][[3, 0]])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -79,6 +79,26 @@ MUTANTS = {
     # MXFP4: one scale per 16 elements instead of 32
     "mxfp4_block_16": (
         "uint8_t x = scales[r * (K / 32) + i / 32];", "uint8_t x = scales[r * (K / 32) + (i / 16) % (K / 32)];"),
+    # backward: silu' without its g (1 - s) term
+    "bwd_silu_prime": (
+        "dg[n] = da[n] * u[n] * (sg * (1.0 + g[n] * (1.0 - sg)));",
+        "dg[n] = da[n] * u[n] * sg;"),
+    # backward: gate and up gradients fed to the wrong weight rows
+    "bwd_gate_up_rows_swapped": [
+        ("acc += elem(W_gate_up, dt, (base + n) * d + c) * dg[n];",
+         "acc += elem(W_gate_up, dt, (base + n) * d + c) * du[n];"),
+        ("acc += elem(W_gate_up, dt, (base + f + n) * d + c) * du[n];",
+         "acc += elem(W_gate_up, dt, (base + f + n) * d + c) * dg[n];")],
+    # backward: softmax Jacobian without the subtracted mean
+    "bwd_router_jacobian": (
+        "double dl = w[j] * (dwt[j] - sw);", "double dl = w[j] * dwt[j];"),
+    # backward: expert output gradient not scaled by the routing weight
+    "bwd_unweighted_dO": (
+        "for (int64_t i = 0; i < d; ++i) dO[i] = wj * elem(dy, dt, t * d + i);",
+        "for (int64_t i = 0; i < d; ++i) dO[i] = elem(dy, dt, t * d + i);"),
+    # backward: down-weight gradient against the wrong activation column
+    "bwd_dWd_misindexed": (
+        "gd[i * f + n] += dO[i] * a[n];", "gd[i * f + n] += dO[i] * a[(n + 1) % f];"),
     # balance: KL with its arguments swapped
     "balance_kl_reversed": (
         "kl += u * (log(u) - log(importance[e] + 1e-8));",
