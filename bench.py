@@ -15,7 +15,8 @@ layer measurement for the Mixtral-8x7B-shaped prefill workload against the
 bf16 MFMA peak; for decode workloads, under "mxfp4", the same layer with
 MXFP4 expert weights.  Each workload also reports, under layer.aux, the router
 auxiliaries: routing with the balance statistics against routing alone, and
-the layer with an expert capacity of 1.25 times the even share.
+the layer with an expert capacity of 1.25 times the even share; and, under
+layer.backward, the backward pass (all gradients) after one forward.
 """
 import argparse
 import hashlib
@@ -237,6 +238,39 @@ class Layer:
                 "copies_kept": kept, "copies": cfg.T * cfg.k,
                 "layer_capacity_ms": round(t_cap * 1e3, 4)}
 
+    def backward_time(self, torch, n):
+        """moe_layer_backward after one forward call: average time over n
+        calls (HIP events), and its MFMA fraction on the expert GEMMs'
+        16 * R * d * f flops (H recomputed 4, dA 2, dX 4, dW_down 2,
+        dW_gate_up 4)."""
+        moe, s, d, cfg = self.moe, self.s, self.d, self.cfg
+        if s.dt != moe.MOE_DT_BF16:
+            return None
+        self.step(0)
+        G = cfg.E + cfg.S
+        f32 = dict(dtype=torch.float32, device="cuda")
+        g = {"dx": torch.empty(cfg.T, cfg.d, **f32), "dWr": torch.empty(cfg.E, cfg.d, **f32),
+             "db": torch.empty(cfg.E, **f32),
+             "dWgu": torch.empty(G, 2 * cfg.f, cfg.d, **f32),
+             "dWd": torch.empty(G, cfg.d, cfg.f, **f32), "dw": torch.empty(cfg.T, cfg.k, **f32)}
+        dy = torch.randn(cfg.T, cfg.d, device="cuda").to(torch.bfloat16)
+        bws = torch.empty(moe.backward_workspace_size(s), dtype=torch.uint8, device="cuda")
+
+        def bwd():
+            moe.moe_layer_backward(s, d["x"], d["W_router"], self.w_gu[0], self.w_dn[0], dy,
+                                   self.ws, g["dx"], g["dWr"], g["db"], g["dWgu"], g["dWd"],
+                                   g["dw"], bws)
+        bwd()
+        torch.cuda.synchronize()
+        t = time_calls(torch, bwd, n)
+        R = cfg.T * cfg.k + cfg.S * cfg.T
+        flops = 16 * R * cfg.d * cfg.f
+        out = {"ms": round(t * 1e3, 4), "expert_gemm_flops": flops,
+               "mfma_frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del g, bws
+        torch.cuda.empty_cache()
+        return out
+
     def timed_steps(self, torch, steps):
         """Exactly `steps` layer calls between two synchronisations: wall
         clock, and HIP events recorded on the stream the calls enqueue on."""
@@ -349,6 +383,7 @@ def prefill_extra(torch, moe, steps, no_cpu, no_aux=False):
     ac, roof, layer = L.summary(torch, kt, ev / steps)
     if not no_aux:
         layer["aux"] = L.aux_times(torch, 5)
+        layer["backward"] = L.backward_time(torch, 3)
     out = {"workload": cfg.name, "steps": steps,
            "ms_per_step": round(wall / steps * 1e3, 4),
            "ms_per_step_hip_events": round(ev / steps * 1e3, 4),
@@ -402,6 +437,7 @@ def main(argv=None):
                                          / HBM_PEAK_GBS, 4)
     if not args.no_aux:
         layer["aux"] = L.aux_times(torch, max(20, min(args.steps, 100)))
+        layer["backward"] = L.backward_time(torch, 10 if cfg.T > 64 else 50)
     mx = None
     if not args.no_mxfp4 and cfg.T <= 64 and cfg.dtype == "bf16" and cfg.d % 32 == 0 \
             and cfg.f % 32 == 0:

@@ -306,6 +306,41 @@ int moe_layer_forward_mxfp4(const moe_shape* s, const void* x,
                             void* y, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* ------------------------------------------------------------- backward
+ * moe_layer_backward: the gradients of a loss L with respect to the layer's
+ * input and weights, given dL/dy (grouped-GEMM training: aitoday "MoEs in
+ * Transformers" page, section "Training MoEs with Transformers").  The
+ * chain rule through the forward above:
+ *   dO = w dy_t per routed copy (dy_t per shared row), dw_tj = dy_t . O_tj,
+ *   da = Wd_e^T dO, dg = da u silu'(g), du = da silu(g) with [g; u] = Wgu_e x_t
+ *   (recomputed), dx_t = sum over its rows of Wgu_e^T [dg; du]
+ *   + sum_j dl_tj Wr_{e_tj}, dWd_e = sum dO a^T, dWgu_e = sum [dg; du] x^T,
+ *   dl_tj = w_tj (dw_tj - sum_i w_ti dw_ti) (softmax over the k selected
+ *   logits), dWr_e = sum dl x, db_e = sum dl.
+ * The selection of the k experts has no gradient; unselected experts get
+ * zero gradients.
+ *   x, W_router, W_gate_up, W_down  the forward's inputs (dt = MOE_DT_BF16
+ *                only; MOE_ERR_UNSUPPORTED otherwise)
+ *   dy           [T, d] bf16
+ *   fwd_workspace the workspace of the moe_layer_forward (or
+ *                moe_layer_forward_capacity) call on the same inputs: its
+ *                routing, permutation, act and expert_out are used
+ *   dx [T, d], dW_router [E, d], db [E], dW_gate_up [E+S, 2f, d],
+ *   dW_down [E+S, d, f]: float32 out (every element written)
+ *   dw           [T, k] float32 out (dL/d topk_w), or NULL
+ *   workspace    moe_backward_workspace_size(s) bytes, 256-byte aligned
+ * Intermediates dO and dH are bf16 (GEMM operands), everything else fp32;
+ * sums in a fixed order (repeated calls are bitwise identical).  Copies
+ * dropped by a capacity (slot_pos < 0) contribute nothing. */
+size_t moe_backward_workspace_size(const moe_shape* s);
+
+int moe_layer_backward(const moe_shape* s, const void* x, const void* W_router,
+                       const void* W_gate_up, const void* W_down, const void* dy,
+                       const void* fwd_workspace, size_t fwd_workspace_bytes,
+                       float* dx, float* dW_router, float* db, float* dW_gate_up,
+                       float* dW_down, float* dw, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------- whole layer, no allocation
  * moe_layer_forward_static: moe_layer_forward with the intermediates in a
  * static device array of the library instead of a caller workspace, for

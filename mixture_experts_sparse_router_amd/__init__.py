@@ -37,7 +37,8 @@ ENTRY_POINTS = ("moe_status_string", "moe_version", "moe_last_hip_error", "moe_r
                 "moe_route_balance_workspace_size", "moe_route_balance",
                 "moe_permute_capacity", "moe_expert_capacity",
                 "moe_layer_forward_capacity", "moe_grouped_gemm_gate_up_mxfp4",
-                "moe_grouped_gemm_down_mxfp4", "moe_layer_forward_mxfp4")
+                "moe_grouped_gemm_down_mxfp4", "moe_layer_forward_mxfp4",
+                "moe_backward_workspace_size", "moe_layer_backward")
 
 # size of the library's static intermediate array (include/moe.h)
 STATIC_SCRATCH_BYTES = 32 << 20
@@ -91,6 +92,8 @@ def _load():
     i64 = ctypes.c_int64
     L.moe_expert_capacity.argtypes = [i64, i64, i64, ctypes.c_double]
     L.moe_expert_capacity.restype = i64
+    L.moe_backward_workspace_size.argtypes = [sp]
+    L.moe_backward_workspace_size.restype = ctypes.c_size_t
     sigs = {
         "moe_route": [sp, vp, vp, vp, vp, vp, vp],
         "moe_permute": [sp, vp, vp, vp, vp, vp, vp],
@@ -108,6 +111,8 @@ def _load():
         "moe_grouped_gemm_down_mxfp4": [sp, vp, vp, vp, vp, vp, vp],
         "moe_layer_forward_mxfp4": [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                     vp],
+        "moe_layer_backward": [sp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp, vp, vp,
+                               vp, vp, ctypes.c_size_t, vp],
     }
     for name, argtypes in sigs.items():
         fn = getattr(L, name)
@@ -146,6 +151,10 @@ def workspace_size(s: moe_shape) -> int:
 
 def route_balance_workspace_size(s: moe_shape) -> int:
     return int(_lib.moe_route_balance_workspace_size(ctypes.byref(s)))
+
+
+def backward_workspace_size(s: moe_shape) -> int:
+    return int(_lib.moe_backward_workspace_size(ctypes.byref(s)))
 
 
 def expert_capacity(T, k, E, capacity_factor) -> int:
@@ -414,6 +423,30 @@ def moe_layer_forward_mxfp4(s: moe_shape, x, W_router, bias, Wq_gate_up, Ws_gate
           _ptr(Wq_down, s.G * s.d * (s.f // 2), u8, "Wq_down"),
           _ptr(Ws_down, s.G * s.d * (s.f // 32), u8, "Ws_down"),
           _ptr(y, s.T * s.d, fd, "y"),
+          ws_ptr, ws_bytes, _stream(stream))
+
+
+def moe_layer_backward(s: moe_shape, x, W_router, W_gate_up, W_down, dy, fwd_workspace, dx,
+                       dW_router, db, dW_gate_up, dW_down, dw, workspace, stream=None):
+    """Gradients (float32) of the layer given dy, using the forward call's
+    workspace (routing, permutation, act, expert_out); dw may be None."""
+    torch = _torch()
+    fd, f32 = _float_dtype(s), torch.float32
+    fw_ptr, fw_bytes = _workspace(fwd_workspace)
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _call("moe_layer_backward", ctypes.byref(s),
+          _ptr(x, s.T * s.d, fd, "x"),
+          _ptr(W_router, s.E * s.d, fd, "W_router"),
+          _ptr(W_gate_up, s.G * 2 * s.f * s.d, fd, "W_gate_up"),
+          _ptr(W_down, s.G * s.d * s.f, fd, "W_down"),
+          _ptr(dy, s.T * s.d, fd, "dy"),
+          fw_ptr, fw_bytes,
+          _ptr(dx, s.T * s.d, f32, "dx"),
+          _ptr(dW_router, s.E * s.d, f32, "dW_router"),
+          _ptr(db, s.E, f32, "db"),
+          _ptr(dW_gate_up, s.G * 2 * s.f * s.d, f32, "dW_gate_up"),
+          _ptr(dW_down, s.G * s.d * s.f, f32, "dW_down"),
+          _ptr(dw, s.T * s.k, f32, "dw", optional=True),
           ws_ptr, ws_bytes, _stream(stream))
 
 

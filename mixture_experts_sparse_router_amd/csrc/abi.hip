@@ -404,6 +404,46 @@ int moe_layer_forward_mxfp4(const moe_shape* m, const void* x, const void* W_rou
   return hip_status(e);
 }
 
+size_t moe_backward_workspace_size(const moe_shape* m) {
+  if (check_shape(m) != MOE_OK || m->dt != MOE_DT_BF16) return 0;
+  size_t off[7];
+  return bwd_layout(to_shape(m), off);
+}
+
+int moe_layer_backward(const moe_shape* m, const void* x, const void* W_router,
+                       const void* W_gate_up, const void* W_down, const void* dy,
+                       const void* fwd_workspace, size_t fwd_workspace_bytes, float* dx,
+                       float* dW_router, float* db, float* dW_gate_up, float* dW_down,
+                       float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  if (m->dt != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(x, s.T * s.d) || !ok_ptr(W_router, s.E * s.d) ||
+      !ok_ptr(W_gate_up, s.G() * 2 * s.f * s.d) || !ok_ptr(W_down, s.G() * s.d * s.f) ||
+      !ok_ptr(dy, s.T * s.d) || !ok_ptr(dx, s.T * s.d) || !ok_ptr(dW_router, s.E * s.d) ||
+      !ok_ptr(db, s.E) || !ok_ptr(dW_gate_up, s.G() * 2 * s.f * s.d) ||
+      !ok_ptr(dW_down, s.G() * s.d * s.f) || (dw && !aligned16(dw)))
+    return MOE_ERR_INVALID_ARG;
+  size_t foff[MOE_WS_COUNT], ftotal;
+  layout(s, foff, &ftotal);
+  if (fwd_workspace_bytes < ftotal) return MOE_ERR_WORKSPACE;
+  if (ftotal > 0 && (!fwd_workspace || ((uintptr_t)fwd_workspace & 255u)))
+    return MOE_ERR_INVALID_ARG;
+  size_t boff[7];
+  const size_t btotal = bwd_layout(s, boff);
+  if (workspace_bytes < btotal) return MOE_ERR_WORKSPACE;
+  if (btotal > 0 && (!workspace || ((uintptr_t)workspace & 255u))) return MOE_ERR_INVALID_ARG;
+  const char* fw = (const char*)fwd_workspace;
+  return hip_status(launch_backward(
+      s, x, W_router, W_gate_up, W_down, dy, (const int32_t*)(fw + foff[MOE_WS_TOPK_IDX]),
+      (const float*)(fw + foff[MOE_WS_TOPK_W]), (const int32_t*)(fw + foff[MOE_WS_OFFSETS]),
+      (const int32_t*)(fw + foff[MOE_WS_SORTED_SLOT]),
+      (const int32_t*)(fw + foff[MOE_WS_SLOT_POS]), fw + foff[MOE_WS_ACT],
+      fw + foff[MOE_WS_EXPERT_OUT], dx, dW_router, db, dW_gate_up, dW_down, dw, workspace,
+      (hipStream_t)stream));
+}
+
 int moe_layer_forward_static(const moe_shape* m, const void* x, const void* W_router,
                              const float* bias, const void* W_gate_up, const void* W_down,
                              void* y, void* stream) {

@@ -1,0 +1,506 @@
+// bwd.hip -- backward pass of the layer: the gradients that grouped-GEMM
+// training needs (aitoday "MoEs in Transformers" page, section "Training
+// MoEs with Transformers": training standardised on grouped GEMMs).
+//
+// Chain rule through the forward (y_t = sum_j w_tj O_tj + shared,
+// O = Wd_e a, a = silu(g) * u, [g; u] = Wgu_e x_t, w = softmax over the k
+// selected logits), for a loss gradient dy, over the forward's own
+// permutation (expert groups of rows):
+//   1. combine_bwd  dO[r] = w dy_t (shared rows: dy_t), dw_tj = dy_t . O[r],
+//                   dl_tj = w_tj (dw_tj - sum_i w_ti dw_ti)
+//   2. H = Xg Wgu_e^T           grouped GEMM over rows (recomputes [g; u])
+//   3. dA = dO Wd_e             grouped GEMM over rows, weight [d, f] read as [K, N]
+//   4. swiglu_bwd   dH = [dA * u * silu'(g), dA * silu(g)]
+//   5. dXp = dH Wgu_e           grouped GEMM over rows, weight [2f, d] read as [K, N]
+//   6. dWd_e = dO^T A           grouped GEMM over the group's rows as K
+//   7. dWgu_e = dH^T Xg         same, token rows gathered
+//   8. router_wgrad dWr_e = sum_r dl_r x_t(r), db_e = sum_r dl_r (row chunks,
+//                   then a fixed-order sum of the chunks)
+//   9. dx_gather    dx_t = sum_j dXp[slot of (t, j)] + shared rows
+//                   + sum_j dl_tj Wr_{e_tj}
+// Gradients come out in fp32; the intermediates dO and dH are rounded to
+// bf16 (the GEMM operands), H and dA stay fp32.  Every sum has a fixed
+// order (no atomics), so repeated calls are bitwise identical.
+//
+// The grouped GEMMs share one kernel: 128 x 128 tiles, K tiles of 32 staged
+// in LDS (double buffered, the next tile's global loads in registers while
+// the current one is multiplied), 4 waves each 64 x 64 with
+// v_mfma_f32_32x32x16_bf16.  An operand that is K-contiguous in memory is
+// copied to LDS row by row; one that is contiguous along M or N is
+// transposed on its way into LDS (2-byte LDS writes), so the MFMA fragments
+// are always 16-byte reads of 8 consecutive K elements.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBT = 128;        // tile rows and columns
+constexpr int kBK = 32;         // K per stage
+constexpr int kLRow = 40;       // LDS row stride in bf16 (80 bytes: conflict-light 16-byte reads)
+constexpr int kBwdThreads = 256;
+
+// Operand tile in LDS: [128 rows (M or N)][32 K] bf16, row stride kLRow.
+struct BwdSmem {
+  bf16_t a[2][kBT * kLRow];
+  bf16_t b[2][kBT * kLRow];
+  int find[8];
+};
+
+// 16 bytes of a K-contiguous row: elements [k, k+8) of the row at p (or
+// zeros when p is null or k is past K).
+__device__ __forceinline__ u32x4 load_kc(const bf16_t* p, int64_t k, int64_t K) {
+  return (p && k < K) ? ldg16(p + k) : u32x4{0u, 0u, 0u, 0u};
+}
+
+__device__ __forceinline__ void store_kc(bf16_t* tile, int row, int kc, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(tile + row * kLRow + kc) = v;
+}
+
+// 8 consecutive M/N elements of one K row, written transposed: element i
+// goes to LDS row mn + i, column k.
+__device__ __forceinline__ void store_mnc(bf16_t* tile, int mn, int k, const u32x4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tile[(mn + 2 * i) * kLRow + k] = (bf16_t)(w[i] & 0xffffu);
+    tile[(mn + 2 * i + 1) * kLRow + k] = (bf16_t)(w[i] >> 16);
+  }
+}
+
+// Which row group (and m-tile) a workgroup owns: group g has
+// ceil(n_g / 128) m-tiles.  Cooperative over the 256 threads; G <= 1024.
+__device__ bool find_group_tile(const int32_t* offsets, int G, int tile, int* g_out, int* mt_out,
+                                int* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int c[4], mine = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = tid * 4 + i;
+    c[i] = g < G ? (offsets[g + 1] - offsets[g] + kBT - 1) / kBT : 0;
+    mine += c[i];
+  }
+  int inc = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) sh[2 + wave] = inc;
+  if (tid == 0) sh[0] = -1;
+  __syncthreads();
+  int start = inc - mine;
+  for (int w = 0; w < wave; ++w) start += sh[2 + w];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (tile >= start && tile < start + c[i]) {
+      sh[0] = tid * 4 + i;
+      sh[1] = tile - start;
+    }
+    start += c[i];
+  }
+  __syncthreads();
+  *g_out = sh[0];
+  *mt_out = sh[1];
+  const bool ok = sh[0] >= 0;
+  __syncthreads();  // sh is reused by the caller's next lookup, if any
+  return ok;
+}
+
+// ROWS = true:  C[r, n] = sum_k A[src(r), k] B(k, n) over the rows r of each
+//   expert group (M = the group's rows, K fixed); A K-contiguous (row
+//   src(r) = the token of r when GATHER, else r); B of expert g: B_KC ?
+//   B[g][n][k] (K-contiguous) : B[g][k][n] (N-contiguous).  C row r, ldc.
+// ROWS = false: C[g][m, n] = sum_{r in group g} A[r, m] B[src(r), n] (K =
+//   the group's rows, M and N fixed); A and B contiguous along M and N;
+//   C [G][M][N].
+template <bool ROWS, bool B_KC, bool GATHER>
+__global__ __launch_bounds__(kBwdThreads) void bwd_gemm_kernel(
+    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
+    int64_t b_stride, float* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+    const int32_t* __restrict__ offsets, int G, const int32_t* __restrict__ sorted_slot,
+    int64_t Tk, int64_t k, int64_t T, int ntM, int ntN) {
+  __shared__ __attribute__((aligned(16))) BwdSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int g, mt, nt;
+  int64_t row_begin, rows;  // ROWS: the tile's rows; else the group's rows (K)
+  if constexpr (ROWS) {
+    nt = (int)blockIdx.x % ntN;
+    if (!find_group_tile(offsets, G, (int)blockIdx.x / ntN, &g, &mt, sm.find)) return;
+    row_begin = offsets[g] + (int64_t)mt * kBT;
+    const int64_t left = offsets[g + 1] - row_begin;
+    rows = left < kBT ? left : kBT;
+  } else {
+    g = (int)blockIdx.x / (ntM * ntN);
+    mt = ((int)blockIdx.x / ntN) % ntM;
+    nt = (int)blockIdx.x % ntN;
+    row_begin = offsets[g];
+    rows = offsets[g + 1] - row_begin;
+  }
+  const int64_t m0 = ROWS ? 0 : (int64_t)mt * kBT;
+  const int64_t n0 = (int64_t)nt * kBT;
+  const int64_t KK = ROWS ? K : rows;  // contraction length
+  const bf16_t* Bg = B + (ROWS ? (int64_t)g * b_stride : 0);
+
+  // ---- staging plan: thread tid moves chunks tid and tid + 256 of each tile
+  // (512 chunks of 16 bytes).  K-contiguous tile: chunk c = row c/4, K
+  // elements 8*(c%4) ..; M/N-contiguous tile: chunk c = K row c/16, M/N
+  // elements 8*(c%16) ...
+  const bf16_t* arow[2];  // ROWS: A row of the chunk's tile row (null past the tile)
+  const bf16_t* brow[2];  // ROWS && B_KC: B row n of the chunk
+  int akc[2], aro[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + kBwdThreads * i;
+    aro[i] = c / 4;
+    akc[i] = 8 * (c % 4);
+    arow[i] = nullptr;
+    brow[i] = nullptr;
+    if constexpr (ROWS) {
+      const int r = aro[i];
+      if (r < rows) {
+        const int64_t grow = row_begin + r;
+        const int64_t src = GATHER ? row_token(grow, sorted_slot, Tk, k, T) : grow;
+        arow[i] = A + src * lda;
+      }
+      if constexpr (B_KC) {
+        const int64_t n = n0 + aro[i];
+        if (n < N) brow[i] = Bg + n * ldb;
+      }
+    }
+  }
+  u32x4 ra[2], rb[2];
+  // global loads of K tile j into registers
+  auto gload = [&](int j) {
+    const int64_t k0 = (int64_t)j * kBK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + kBwdThreads * i;
+      if constexpr (ROWS) {
+        ra[i] = load_kc(arow[i], k0 + akc[i], KK);
+        if constexpr (B_KC) {
+          rb[i] = load_kc(brow[i], k0 + akc[i], KK);
+        } else {
+          // B[g][k][n]: K row k0 + c/16, columns n0 + 8*(c%16) ..
+          const int64_t kr = k0 + c / 16, n = n0 + 8 * (c % 16);
+          rb[i] = (kr < KK && n < N) ? ldg16(Bg + kr * ldb + n) : u32x4{0u, 0u, 0u, 0u};
+        }
+      } else {
+        // A[r][m] and B[src(r)][n]: K row = group row row_begin + k0 + c/16
+        const int64_t kr = k0 + c / 16;
+        const int64_t m = m0 + 8 * (c % 16), n = n0 + 8 * (c % 16);
+        if (kr < KK) {
+          const int64_t r = row_begin + kr;
+          const int64_t src = GATHER ? row_token(r, sorted_slot, Tk, k, T) : r;
+          ra[i] = m < M ? ldg16(A + r * lda + m) : u32x4{0u, 0u, 0u, 0u};
+          rb[i] = n < N ? ldg16(B + src * ldb + n) : u32x4{0u, 0u, 0u, 0u};
+        } else {
+          ra[i] = rb[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + kBwdThreads * i;
+      if constexpr (ROWS) {
+        store_kc(sm.a[buf], aro[i], akc[i], ra[i]);
+        if constexpr (B_KC) store_kc(sm.b[buf], aro[i], akc[i], rb[i]);
+        else store_mnc(sm.b[buf], 8 * (c % 16), c / 16, rb[i]);
+      } else {
+        store_mnc(sm.a[buf], 8 * (c % 16), c / 16, ra[i]);
+        store_mnc(sm.b[buf], 8 * (c % 16), c / 16, rb[i]);
+      }
+    }
+  };
+
+  // ---- compute: wave (wm, wn) owns rows wm*64 .. +64 and columns wn*64 ..
+  // +64 of the tile, 2 x 2 blocks of 32 x 32
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+
+  const int nk = (int)((KK + kBK - 1) / kBK);
+  if (nk > 0) {
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int j = 0; j < nk; ++j) {
+      const int buf = j & 1;
+      if (j + 1 < nk) gload(j + 1);
+#pragma unroll
+      for (int ks = 0; ks < kBK / 16; ++ks) {
+        u32x4 fa[2], fb[2];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          fa[mi] = *reinterpret_cast<const u32x4*>(
+              sm.a[buf] + (wm * 64 + mi * 32 + lr) * kLRow + 16 * ks + 8 * lh);
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          fb[ni] = *reinterpret_cast<const u32x4*>(
+              sm.b[buf] + (wn * 64 + ni * 32 + lr) * kLRow + 16 * ks + 8 * lh);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma32(fa[mi], fb[ni], acc[mi][ni]);
+      }
+      if (j + 1 < nk) lstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds D[8*(e/4) + 4*lh + (e%4)][lr] of each block
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rl = wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int64_t n = n0 + wn * 64 + ni * 32 + lr;
+        if (n >= N) continue;
+        if constexpr (ROWS) {
+          if (rl < rows) C[(row_begin + rl) * ldc + n] = acc[mi][ni][e];
+        } else {
+          const int64_t m = m0 + rl;
+          if (m < M) C[((int64_t)g * M + m) * ldc + n] = acc[mi][ni][e];
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ elementwise
+
+// 1. Per token (one wave): dO rows, dw and dl.  Lanes stride over d; the
+// dot products are reduced by a fixed butterfly.
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const bf16_t* __restrict__ dy, const bf16_t* __restrict__ O,
+    const int32_t* __restrict__ slot_pos, const float* __restrict__ topk_w,
+    bf16_t* __restrict__ dO, float* __restrict__ dw_out, float* __restrict__ dl_out, int64_t T,
+    int64_t d, int k, int S) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const bf16_t* dyt = dy + t * d;
+  float dwj[64];  // k <= 64
+  for (int j = 0; j < k; ++j) {
+    const int32_t r = slot_pos[t * k + j];
+    const float w = topk_w[t * k + j];
+    float acc = 0.f;
+    if (r >= 0) {
+      const bf16_t* Or = O + (int64_t)r * d;
+      bf16_t* dOr = dO + (int64_t)r * d;
+      for (int64_t i = lane; i < d; i += 64) {
+        const float g = bf16_to_f32(dyt[i]);
+        acc += g * bf16_to_f32(Or[i]);
+        dOr[i] = f32_to_bf16(w * g);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    dwj[j] = acc;
+  }
+  const int64_t Tk = T * k;
+  for (int s = 0; s < S; ++s) {
+    bf16_t* dOr = dO + (Tk + (int64_t)s * T + t) * d;
+    for (int64_t i = lane; i < d; i += 64) dOr[i] = dyt[i];
+  }
+  // softmax over the k selected logits: dl_j = w_j (dw_j - sum_i w_i dw_i)
+  float sw = 0.f;
+  for (int j = 0; j < k; ++j) sw += topk_w[t * k + j] * dwj[j];
+  if (lane == 0) {
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = slot_pos[t * k + j];
+      const float dl = r >= 0 ? topk_w[t * k + j] * (dwj[j] - sw) : 0.f;
+      if (dw_out) dw_out[t * k + j] = dwj[j];
+      dl_out[t * k + j] = dl;
+    }
+  }
+}
+
+// 4. dH[r, n] = dA * u * silu'(g), dH[r, f + n] = dA * silu(g), from H = [g; u].
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ H,
+                                                         const float* __restrict__ dA,
+                                                         bf16_t* __restrict__ dH, int64_t R,
+                                                         int64_t f) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= R * f) return;
+  const int64_t r = i / f, n = i % f;
+  const float g = H[r * 2 * f + n], u = H[r * 2 * f + f + n];
+  const float da = dA[i];
+  const float s = 1.0f / (1.0f + __expf(-g));
+  dH[r * 2 * f + n] = f32_to_bf16(da * u * (s * (1.0f + g * (1.0f - s))));
+  dH[r * 2 * f + f + n] = f32_to_bf16(da * (g * s));
+}
+
+// 8. Router weight and bias gradients: chunk c of expert e's rows adds
+// dl(r) x[t(r)] for its rows in order; then the chunks are added in order.
+constexpr int kRouterChunks = 16;
+
+__global__ __launch_bounds__(256) void router_wgrad_kernel(
+    const bf16_t* __restrict__ x, const float* __restrict__ dl,
+    const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ offsets,
+    float* __restrict__ part, float* __restrict__ part_b, int64_t d, int64_t k, int E) {
+  const int e = blockIdx.x, c = blockIdx.z;
+  const int64_t col = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  const int64_t r0 = offsets[e], n = offsets[e + 1] - r0;
+  const int64_t per = (n + kRouterChunks - 1) / kRouterChunks;
+  const int64_t lo = r0 + (int64_t)c * per;
+  const int64_t hi = (lo + per < r0 + n) ? lo + per : r0 + n;
+  float acc = 0.f, accb = 0.f;
+  for (int64_t r = lo; r < hi; ++r) {
+    const int32_t slot = sorted_slot[r];
+    const float v = dl[slot];
+    if (col < d) acc += v * bf16_to_f32(x[(int64_t)((uint32_t)slot / (uint32_t)k) * d + col]);
+    accb += v;
+  }
+  if (col < d) part[((int64_t)c * E + e) * d + col] = acc;
+  if (blockIdx.y == 0 && threadIdx.x == 0) part_b[c * E + e] = accb;
+}
+
+__global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __restrict__ part,
+                                                               const float* __restrict__ part_b,
+                                                               float* __restrict__ dWr,
+                                                               float* __restrict__ db, int64_t d,
+                                                               int E) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < (int64_t)E * d) {
+    float s = 0.f;
+    for (int c = 0; c < kRouterChunks; ++c) s += part[(int64_t)c * E * d + i];
+    dWr[i] = s;
+  }
+  if (i < E) {
+    float s = 0.f;
+    for (int c = 0; c < kRouterChunks; ++c) s += part_b[c * E + i];
+    db[i] = s;
+  }
+}
+
+// 9. dx_t = sum_j dXp[slot_pos(t, j)] + sum_s dXp[T*k + s*T + t]
+//         + sum_j dl_tj Wr[e_tj], in that order.
+__global__ __launch_bounds__(256) void dx_gather_kernel(
+    const float* __restrict__ dXp, const int32_t* __restrict__ slot_pos,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
+    const bf16_t* __restrict__ Wr, float* __restrict__ dx, int64_t T, int64_t d, int k, int S,
+    int E) {
+  const int64_t t = blockIdx.x;
+  const int64_t Tk = T * k;
+  for (int64_t i = threadIdx.x; i < d; i += 256) {
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = slot_pos[t * k + j];
+      if (r >= 0) acc += dXp[(int64_t)r * d + i];
+    }
+    for (int s = 0; s < S; ++s) acc += dXp[(Tk + (int64_t)s * T + t) * d + i];
+    for (int j = 0; j < k; ++j) {
+      const int32_t e = topk_idx[t * k + j];
+      if (e >= 0 && e < E) acc += dl[t * k + j] * bf16_to_f32(Wr[(int64_t)e * d + i]);
+    }
+    dx[t * d + i] = acc;
+  }
+}
+
+inline unsigned tiles_bound(const Shape& s) {
+  const int64_t R = s.R();
+  const int64_t nonempty = s.G() < R ? s.G() : R;
+  return (unsigned)(R / kBT + nonempty + 1);
+}
+
+}  // namespace
+
+// Workspace of the backward pass (bytes, 256-aligned pieces):
+//   dO [R, d] bf16, H [R, 2f] fp32, dA [R, f] fp32, dH [R, 2f] bf16,
+//   dXp [R, d] fp32, dl [T, k] fp32, router partials [16, E, d] + [16, E] fp32.
+size_t bwd_layout(const Shape& s, size_t* off) {
+  const size_t R = (size_t)s.R(), d = (size_t)s.d, f = (size_t)s.f;
+  const size_t sizes[7] = {R * d * 2,  R * 2 * f * 4, R * f * 4, R * 2 * f * 2,
+                           R * d * 4,  (size_t)s.Tk() * 4,
+                           (size_t)kRouterChunks * (size_t)s.E * (d + 1) * 4};
+  size_t at = 0;
+  for (int i = 0; i < 7; ++i) {
+    off[i] = at;
+    at += (sizes[i] + 255) & ~(size_t)255;
+  }
+  return at;
+}
+
+hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
+                           const void* W_gate_up, const void* W_down, const void* dy,
+                           const int32_t* topk_idx, const float* topk_w,
+                           const int32_t* offsets, const int32_t* sorted_slot,
+                           const int32_t* slot_pos, const void* act, const void* expert_out,
+                           float* dx, float* dWr, float* db, float* dWgu, float* dWd, float* dw,
+                           void* workspace, hipStream_t st) {
+  size_t off[7];
+  bwd_layout(s, off);
+  char* ws = (char*)workspace;
+  bf16_t* dO = (bf16_t*)(ws + off[0]);
+  float* H = (float*)(ws + off[1]);
+  float* dA = (float*)(ws + off[2]);
+  bf16_t* dH = (bf16_t*)(ws + off[3]);
+  float* dXp = (float*)(ws + off[4]);
+  float* dl = (float*)(ws + off[5]);
+  float* part = (float*)(ws + off[6]);
+  float* part_b = part + (size_t)kRouterChunks * s.E * s.d;
+  const int G = (int)s.G();
+  const int64_t R = s.R(), d = s.d, f = s.f;
+  const bf16_t* xb = (const bf16_t*)x;
+  const bf16_t* Wgu = (const bf16_t*)W_gate_up;
+  const bf16_t* Wd = (const bf16_t*)W_down;
+
+  // 1 (no tokens: the weight gradients below still come out, as zeros)
+  if (s.T > 0)
+    hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)((s.T + 3) / 4)), dim3(256), 0, st,
+                       (const bf16_t*)dy, (const bf16_t*)expert_out, slot_pos, topk_w, dO, dw,
+                       dl, s.T, d, (int)s.k, (int)s.S);
+  const unsigned mt = tiles_bound(s);
+  auto nt = [](int64_t n) { return (int)((n + kBT - 1) / kBT); };
+  // 2. H = Xg Wgu_e^T: rows, B K-contiguous ([2f][d]), gathered token rows
+  hipLaunchKernelGGL((bwd_gemm_kernel<true, true, true>), dim3(mt * nt(2 * f)), dim3(256), 0,
+                     st, xb, d, Wgu, d, 2 * f * d, H, 2 * f, (int64_t)0, 2 * f, d, offsets, G,
+                     sorted_slot, s.Tk(), s.k, s.T, 1, nt(2 * f));
+  // 3. dA = dO Wd_e: rows, B N-contiguous (Wd_e [d][f] read as [K = d][N = f])
+  hipLaunchKernelGGL((bwd_gemm_kernel<true, false, false>), dim3(mt * nt(f)), dim3(256), 0, st,
+                     (const bf16_t*)dO, d, Wd, f, d * f, dA, f, (int64_t)0, f, d, offsets, G,
+                     sorted_slot, s.Tk(), s.k, s.T, 1, nt(f));
+  // 4
+  if (R > 0)
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((R * f + 255) / 256)), dim3(256), 0,
+                       st, (const float*)H, (const float*)dA, dH, R, f);
+  // 5. dXp = dH Wgu_e: rows, B N-contiguous (Wgu_e [2f][d] read as [K = 2f][N = d])
+  hipLaunchKernelGGL((bwd_gemm_kernel<true, false, false>), dim3(mt * nt(d)), dim3(256), 0, st,
+                     (const bf16_t*)dH, 2 * f, Wgu, d, 2 * f * d, dXp, d, (int64_t)0, d, 2 * f,
+                     offsets, G, sorted_slot, s.Tk(), s.k, s.T, 1, nt(d));
+  // 6. dWd_e = dO^T A: K = the group's rows; M = d, N = f
+  hipLaunchKernelGGL((bwd_gemm_kernel<false, false, false>),
+                     dim3((unsigned)(G * nt(d) * nt(f))), dim3(256), 0, st, (const bf16_t*)dO, d,
+                     (const bf16_t*)act, f, (int64_t)0, dWd, f, d, f, (int64_t)0, offsets, G,
+                     sorted_slot, s.Tk(), s.k, s.T, nt(d), nt(f));
+  // 7. dWgu_e = dH^T Xg: M = 2f, N = d, token rows gathered
+  hipLaunchKernelGGL((bwd_gemm_kernel<false, false, true>),
+                     dim3((unsigned)(G * nt(2 * f) * nt(d))), dim3(256), 0, st,
+                     (const bf16_t*)dH, 2 * f, xb, d, (int64_t)0, dWgu, d, 2 * f, d, (int64_t)0,
+                     offsets, G, sorted_slot, s.Tk(), s.k, s.T, nt(2 * f), nt(d));
+  // 8
+  hipLaunchKernelGGL(router_wgrad_kernel, dim3((unsigned)s.E, (unsigned)((d + 255) / 256),
+                                               kRouterChunks),
+                     dim3(256), 0, st, xb, (const float*)dl, sorted_slot, offsets, part, part_b,
+                     d, s.k, (int)s.E);
+  hipLaunchKernelGGL(router_wgrad_sum_kernel, dim3((unsigned)((s.E * d + 255) / 256)), dim3(256),
+                     0, st, (const float*)part, (const float*)part_b, dWr, db, d, (int)s.E);
+  // 9
+  if (s.T > 0)
+    hipLaunchKernelGGL(dx_gather_kernel, dim3((unsigned)s.T), dim3(256), 0, st,
+                     (const float*)dXp, slot_pos, topk_idx, (const float*)dl,
+                     (const bf16_t*)W_router, dx, s.T, d, (int)s.k, (int)s.S, (int)s.E);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -138,6 +138,16 @@ hipError_t launch_stream_mx(bool gated, const Shape& s, const void* A,
                             const int32_t* sorted_slot, const int32_t* offsets,
                             const uint8_t* Wq, const uint8_t* Ws, void* out, int64_t K,
                             int64_t N, hipStream_t st);
+// Backward pass (bf16): workspace layout (7 pieces) and the launch sequence;
+// the forward's routing, permutation, act and expert_out are inputs.
+size_t bwd_layout(const Shape& s, size_t* off);
+hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
+                           const void* W_gate_up, const void* W_down, const void* dy,
+                           const int32_t* topk_idx, const float* topk_w,
+                           const int32_t* offsets, const int32_t* sorted_slot,
+                           const int32_t* slot_pos, const void* act, const void* expert_out,
+                           float* dx, float* dWr, float* db, float* dWgu, float* dWd, float* dw,
+                           void* workspace, hipStream_t st);
 // Router load statistics from the logits: importance[E] (mean softmax
 // probability) and the balance loss; partial holds balance_partials(T) * E
 // doubles.

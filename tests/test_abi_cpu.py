@@ -258,3 +258,24 @@ def test_mxfp4_entry_points_check_shapes_and_pointers():
                                      need - 1, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_layer_forward_mxfp4(ctypes.byref(_shape(k=0)), p, p, None, p, p, p, p, p, p,
                                      need, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_backward_checks_before_any_hip_call():
+    L = moe.lib()
+    p = ctypes.c_void_p(4096)
+    s = _shape()
+    fneed, bneed = moe.workspace_size(s), moe.backward_workspace_size(s)
+    assert bneed > 0
+    assert moe.backward_workspace_size(_shape(dt=moe.MOE_DT_F32)) == 0
+
+    def call(shape, fbytes=fneed, bbytes=bneed, dx=p, fw=p, ws=p, dw=None):
+        return L.moe_layer_backward(ctypes.byref(shape), p, p, p, p, p, fw, fbytes, dx, p, p, p,
+                                    p, dw, ws, bbytes, None)
+    assert call(_shape(dt=moe.MOE_DT_F32)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(_shape(k=0)) == moe.MOE_ERR_INVALID_ARG
+    assert call(s, fbytes=fneed - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(s, bbytes=bneed - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(s, dx=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(s, fw=ctypes.c_void_p(4096 + 16)) == moe.MOE_ERR_INVALID_ARG
+    assert call(s, ws=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(s, dw=ctypes.c_void_p(4096 + 4)) == moe.MOE_ERR_INVALID_ARG
