@@ -6,8 +6,8 @@
 // O = Wd_e a, a = silu(g) * u, [g; u] = Wgu_e x_t, w = softmax over the k
 // selected logits), for a loss gradient dy, over the forward's own
 // permutation (expert groups of rows):
-//   1. combine_bwd  dO[r] = w dy_t (shared rows: dy_t), dw_tj = dy_t . O[r],
-//                   dl_tj = w_tj (dw_tj - sum_i w_ti dw_ti)
+//   1. combine_bwd  dO[r] = w dy_t (shared rows: dy_t), dw_tj = dy_t . O[r];
+//      router_dl    dl_tj = w_tj (dw_tj - sum_i w_ti dw_ti)
 //   2. H = Xg Wgu_e^T           grouped GEMM over rows (recomputes [g; u])
 //   3. dA = dO Wd_e             grouped GEMM over rows, weight [d, f] read as [K, N]
 //   4. swiglu_bwd   dH = [dA * u * silu'(g), dA * silu(g)]
@@ -278,51 +278,57 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_gemm_kernel(
 
 // ------------------------------------------------------------ elementwise
 
-// 1. Per token (one wave): dO rows, dw and dl.  Lanes stride over d; the
-// dot products are reduced by a fixed butterfly.
+// 1a. One wave per routed copy (t, j): dO row = w dy_t (bf16) and
+// dw_tj = dy_t . O_row (lanes stride over d, then a fixed butterfly); one
+// wave per shared row: dO row = dy_t.
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const bf16_t* __restrict__ dy, const bf16_t* __restrict__ O,
     const int32_t* __restrict__ slot_pos, const float* __restrict__ topk_w,
-    bf16_t* __restrict__ dO, float* __restrict__ dw_out, float* __restrict__ dl_out, int64_t T,
-    int64_t d, int k, int S) {
+    bf16_t* __restrict__ dO, float* __restrict__ dw_out, int64_t T, int64_t d, int64_t k,
+    int S) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const bf16_t* dyt = dy + t * d;
-  float dwj[64];  // k <= 64
-  for (int j = 0; j < k; ++j) {
-    const int32_t r = slot_pos[t * k + j];
-    const float w = topk_w[t * k + j];
-    float acc = 0.f;
-    if (r >= 0) {
-      const bf16_t* Or = O + (int64_t)r * d;
-      bf16_t* dOr = dO + (int64_t)r * d;
-      for (int64_t i = lane; i < d; i += 64) {
-        const float g = bf16_to_f32(dyt[i]);
-        acc += g * bf16_to_f32(Or[i]);
-        dOr[i] = f32_to_bf16(w * g);
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    dwj[j] = acc;
-  }
+  const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // copy, then shared row
   const int64_t Tk = T * k;
-  for (int s = 0; s < S; ++s) {
-    bf16_t* dOr = dO + (Tk + (int64_t)s * T + t) * d;
+  if (c >= Tk + (int64_t)S * T) return;
+  if (c >= Tk) {
+    const int64_t t = (c - Tk) % T;
+    const bf16_t* dyt = dy + t * d;
+    bf16_t* dOr = dO + c * d;  // shared rows follow the routed ones in the same order
     for (int64_t i = lane; i < d; i += 64) dOr[i] = dyt[i];
+    return;
   }
-  // softmax over the k selected logits: dl_j = w_j (dw_j - sum_i w_i dw_i)
-  float sw = 0.f;
-  for (int j = 0; j < k; ++j) sw += topk_w[t * k + j] * dwj[j];
-  if (lane == 0) {
-    for (int j = 0; j < k; ++j) {
-      const int32_t r = slot_pos[t * k + j];
-      const float dl = r >= 0 ? topk_w[t * k + j] * (dwj[j] - sw) : 0.f;
-      if (dw_out) dw_out[t * k + j] = dwj[j];
-      dl_out[t * k + j] = dl;
+  const int64_t t = c / k;
+  const int32_t r = slot_pos[c];
+  const float w = topk_w[c];
+  const bf16_t* dyt = dy + t * d;
+  float acc = 0.f;
+  if (r >= 0) {
+    const bf16_t* Or = O + (int64_t)r * d;
+    bf16_t* dOr = dO + (int64_t)r * d;
+    for (int64_t i = lane; i < d; i += 64) {
+      const float g = bf16_to_f32(dyt[i]);
+      acc += g * bf16_to_f32(Or[i]);
+      dOr[i] = f32_to_bf16(w * g);
     }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) dw_out[c] = acc;  // dropped copies: 0
+}
+
+// 1b. Softmax over the k selected logits: dl_j = w_j (dw_j - sum_i w_i dw_i),
+// one thread per token (dropped copies: dl = 0).
+__global__ __launch_bounds__(256) void router_dl_kernel(const float* __restrict__ dw,
+                                                        const float* __restrict__ topk_w,
+                                                        const int32_t* __restrict__ slot_pos,
+                                                        float* __restrict__ dl, int64_t T,
+                                                        int64_t k) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  float sw = 0.f;
+  for (int64_t j = 0; j < k; ++j) sw += topk_w[t * k + j] * dw[t * k + j];
+  for (int64_t j = 0; j < k; ++j)
+    dl[t * k + j] = slot_pos[t * k + j] >= 0 ? topk_w[t * k + j] * (dw[t * k + j] - sw) : 0.f;
 }
 
 // 4. dH[r, n] = dA * u * silu'(g), dH[r, f + n] = dA * silu(g), from H = [g; u].
@@ -341,8 +347,9 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
 }
 
 // 8. Router weight and bias gradients: chunk c of expert e's rows adds
-// dl(r) x[t(r)] for its rows in order; then the chunks are added in order.
-constexpr int kRouterChunks = 16;
+// dl(r) x[t(r)] for its rows in order (8 rows' loads issued together); then
+// the chunks are added in order.
+constexpr int kRouterChunks = 32;
 
 __global__ __launch_bounds__(256) void router_wgrad_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ dl,
@@ -350,16 +357,27 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(
     float* __restrict__ part, float* __restrict__ part_b, int64_t d, int64_t k, int E) {
   const int e = blockIdx.x, c = blockIdx.z;
   const int64_t col = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  const int64_t colc = col < d ? col : d - 1;
   const int64_t r0 = offsets[e], n = offsets[e + 1] - r0;
   const int64_t per = (n + kRouterChunks - 1) / kRouterChunks;
   const int64_t lo = r0 + (int64_t)c * per;
   const int64_t hi = (lo + per < r0 + n) ? lo + per : r0 + n;
   float acc = 0.f, accb = 0.f;
-  for (int64_t r = lo; r < hi; ++r) {
-    const int32_t slot = sorted_slot[r];
-    const float v = dl[slot];
-    if (col < d) acc += v * bf16_to_f32(x[(int64_t)((uint32_t)slot / (uint32_t)k) * d + col]);
-    accb += v;
+  for (int64_t rb = lo; rb < hi; rb += 8) {
+    int32_t slot[8];
+    float v[8], xv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) slot[u] = rb + u < hi ? sorted_slot[rb + u] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v[u] = rb + u < hi ? dl[slot[u]] : 0.f;
+      xv[u] = bf16_to_f32(x[(int64_t)((uint32_t)slot[u] / (uint32_t)k) * d + colc]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc += v[u] * xv[u];
+      accb += v[u];
+    }
   }
   if (col < d) part[((int64_t)c * E + e) * d + col] = acc;
   if (blockIdx.y == 0 && threadIdx.x == 0) part_b[c * E + e] = accb;
@@ -391,20 +409,20 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(
     const bf16_t* __restrict__ Wr, float* __restrict__ dx, int64_t T, int64_t d, int k, int S,
     int E) {
   const int64_t t = blockIdx.x;
+  const int64_t i = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  if (i >= d) return;
   const int64_t Tk = T * k;
-  for (int64_t i = threadIdx.x; i < d; i += 256) {
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int32_t r = slot_pos[t * k + j];
-      if (r >= 0) acc += dXp[(int64_t)r * d + i];
-    }
-    for (int s = 0; s < S; ++s) acc += dXp[(Tk + (int64_t)s * T + t) * d + i];
-    for (int j = 0; j < k; ++j) {
-      const int32_t e = topk_idx[t * k + j];
-      if (e >= 0 && e < E) acc += dl[t * k + j] * bf16_to_f32(Wr[(int64_t)e * d + i]);
-    }
-    dx[t * d + i] = acc;
+  float acc = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int32_t r = slot_pos[t * k + j];
+    if (r >= 0) acc += dXp[(int64_t)r * d + i];
   }
+  for (int s = 0; s < S; ++s) acc += dXp[(Tk + (int64_t)s * T + t) * d + i];
+  for (int j = 0; j < k; ++j) {
+    const int32_t e = topk_idx[t * k + j];
+    if (e >= 0 && e < E) acc += dl[t * k + j] * bf16_to_f32(Wr[(int64_t)e * d + i]);
+  }
+  dx[t * d + i] = acc;
 }
 
 inline unsigned tiles_bound(const Shape& s) {
@@ -456,10 +474,16 @@ hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
   const bf16_t* Wd = (const bf16_t*)W_down;
 
   // 1 (no tokens: the weight gradients below still come out, as zeros)
-  if (s.T > 0)
-    hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)((s.T + 3) / 4)), dim3(256), 0, st,
-                       (const bf16_t*)dy, (const bf16_t*)expert_out, slot_pos, topk_w, dO, dw,
-                       dl, s.T, d, (int)s.k, (int)s.S);
+  if (s.T > 0) {
+    const int64_t rows1 = s.Tk() + s.S * s.T;
+    // dw goes to the caller's array, else to the dl slot (overwritten next)
+    float* dwp = dw ? dw : dl;
+    hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)((rows1 + 3) / 4)), dim3(256), 0, st,
+                       (const bf16_t*)dy, (const bf16_t*)expert_out, slot_pos, topk_w, dO, dwp,
+                       s.T, d, s.k, (int)s.S);
+    hipLaunchKernelGGL(router_dl_kernel, dim3((unsigned)((s.T + 255) / 256)), dim3(256), 0, st,
+                       (const float*)dwp, topk_w, slot_pos, dl, s.T, s.k);
+  }
   const unsigned mt = tiles_bound(s);
   auto nt = [](int64_t n) { return (int)((n + kBT - 1) / kBT); };
   // 2. H = Xg Wgu_e^T: rows, B K-contiguous ([2f][d]), gathered token rows
@@ -497,7 +521,8 @@ hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
                      0, st, (const float*)part, (const float*)part_b, dWr, db, d, (int)s.E);
   // 9
   if (s.T > 0)
-    hipLaunchKernelGGL(dx_gather_kernel, dim3((unsigned)s.T), dim3(256), 0, st,
+    hipLaunchKernelGGL(dx_gather_kernel, dim3((unsigned)s.T, (unsigned)((d + 255) / 256)),
+                       dim3(256), 0, st,
                      (const float*)dXp, slot_pos, topk_idx, (const float*)dl,
                      (const bf16_t*)W_router, dx, s.T, d, (int)s.k, (int)s.S, (int)s.E);
   return hipGetLastError();
