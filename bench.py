@@ -95,6 +95,8 @@ def time_calls(torch, fn, n):
     on the current stream (the stream every call enqueues on)."""
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):  # warm: first calls pay for code and cache misses
+        fn()
     e0.record(st)
     for _ in range(n):
         fn()
@@ -336,8 +338,8 @@ def mxfp4_extra(torch, moe, L, steps):
     for _ in range(5):
         step()
     torch.cuda.synchronize()
-    t_layer = time_calls(torch, step, steps)
-    n = max(20, min(steps, 200))
+    t_layer = time_calls(torch, step, max(steps, 100))
+    n = 100
     t_gu = time_calls(torch, lambda: moe.moe_grouped_gemm_gate_up_mxfp4(
         s, d["x"], views["sorted_slot"], views["offsets"], dm["Wq_gate_up"], dm["Ws_gate_up"],
         views["act"]), n)
