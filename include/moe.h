@@ -181,7 +181,8 @@ int moe_permute_capacity(const moe_shape* s, const int32_t* topk_idx,
 /* Capacity from a capacity factor (yunthe page, sections 4.1 and 5.2: the
  * factor, typically 1.0 to 2.0, scales an expert's even share of the
  * copies): ceil(capacity_factor * T * k / E).  Host only, no HIP call.
- * Returns -1 for T < 0, k < 1, E < 1 or a factor outside [0, 1e9]. */
+ * Returns -1 for T < 0, k < 1, E < 1, a factor outside [0, 1e9] or a
+ * capacity of 4e18 or more. */
 int64_t moe_expert_capacity(int64_t T, int64_t k, int64_t E,
                             double capacity_factor);
 

@@ -45,6 +45,8 @@ int check_shape(const moe_shape* m) {
   if (m->E + m->n_shared > kMaxGroups) return MOE_ERR_UNSUPPORTED;
   if (m->k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (m->d > ((int64_t)1 << 30) || m->f > ((int64_t)1 << 30)) return MOE_ERR_UNSUPPORTED;
+  // element counts of the weight tensors, (E+S) * 2f * d, stay below 2^62
+  if (m->d * m->f > ((int64_t)1 << 60) / (m->E + m->n_shared)) return MOE_ERR_UNSUPPORTED;
   if (m->T >= kMaxRows / (m->k + m->n_shared)) return MOE_ERR_UNSUPPORTED;  // R < 2^31
   // bf16 batches past decode size: the tiled GEMM addresses x and one
   // expert's weights with 32-bit byte offsets below 2^31
@@ -215,7 +217,9 @@ int moe_permute(const moe_shape* m, const int32_t* topk_idx, int32_t* counts,
 int64_t moe_expert_capacity(int64_t T, int64_t k, int64_t E, double capacity_factor) {
   if (T < 0 || k < 1 || E < 1 || !(capacity_factor >= 0.0) || capacity_factor > 1e9)
     return -1;
-  return (int64_t)ceil(capacity_factor * (double)(T * k) / (double)E);
+  // T * k in double: exact below 2^53 copies, and no integer overflow above
+  const double c = ceil(capacity_factor * ((double)T * (double)k) / (double)E);
+  return c < 4.0e18 ? (int64_t)c : -1;
 }
 
 int moe_grouped_gemm_gate_up(const moe_shape* m, const void* x, const int32_t* sorted_slot,

@@ -28,8 +28,7 @@ namespace moe {
 namespace {
 
 constexpr int kBalWaves = 4;
-constexpr int kBalTokensPerWave = 4;
-constexpr int kBalTokens = kBalWaves * kBalTokensPerWave;  // tokens per workgroup
+constexpr int kBalTokensPerWave = kBalTokens / kBalWaves;
 constexpr int kBalMaxE = 1024;
 constexpr int kFinalThreads = 1024;
 
@@ -132,8 +131,6 @@ __global__ __launch_bounds__(kFinalThreads) void balance_final_kernel(
 }
 
 }  // namespace
-
-int64_t balance_partials(int64_t T) { return (T + kBalTokens - 1) / kBalTokens; }
 
 hipError_t launch_balance(const Shape& s, const float* logits, double* partial,
                           double* importance, double* loss, hipStream_t st) {

@@ -349,8 +349,6 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
 // 8. Router weight and bias gradients: chunk c of expert e's rows adds
 // dl(r) x[t(r)] for its rows in order (8 rows' loads issued together); then
 // the chunks are added in order.
-constexpr int kRouterChunks = 32;
-
 __global__ __launch_bounds__(256) void router_wgrad_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ dl,
     const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ offsets,
@@ -432,22 +430,6 @@ inline unsigned tiles_bound(const Shape& s) {
 }
 
 }  // namespace
-
-// Workspace of the backward pass (bytes, 256-aligned pieces):
-//   dO [R, d] bf16, H [R, 2f] fp32, dA [R, f] fp32, dH [R, 2f] bf16,
-//   dXp [R, d] fp32, dl [T, k] fp32, router partials [16, E, d] + [16, E] fp32.
-size_t bwd_layout(const Shape& s, size_t* off) {
-  const size_t R = (size_t)s.R(), d = (size_t)s.d, f = (size_t)s.f;
-  const size_t sizes[7] = {R * d * 2,  R * 2 * f * 4, R * f * 4, R * 2 * f * 2,
-                           R * d * 4,  (size_t)s.Tk() * 4,
-                           (size_t)kRouterChunks * (size_t)s.E * (d + 1) * 4};
-  size_t at = 0;
-  for (int i = 0; i < 7; ++i) {
-    off[i] = at;
-    at += (sizes[i] + 255) & ~(size_t)255;
-  }
-  return at;
-}
 
 hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
                            const void* W_gate_up, const void* W_down, const void* dy,

@@ -138,9 +138,24 @@ hipError_t launch_stream_mx(bool gated, const Shape& s, const void* A,
                             const int32_t* sorted_slot, const int32_t* offsets,
                             const uint8_t* Wq, const uint8_t* Ws, void* out, int64_t K,
                             int64_t N, hipStream_t st);
-// Backward pass (bf16): workspace layout (7 pieces) and the launch sequence;
-// the forward's routing, permutation, act and expert_out are inputs.
-size_t bwd_layout(const Shape& s, size_t* off);
+// Backward pass (bf16): workspace layout and the launch sequence; the
+// forward's routing, permutation, act and expert_out are inputs.
+// Workspace (bytes, 256-aligned pieces): dO [R, d] bf16, H [R, 2f] fp32,
+// dA [R, f] fp32, dH [R, 2f] bf16, dXp [R, d] fp32, dl [T, k] fp32, router
+// partials [kRouterChunks, E, d] + [kRouterChunks, E] fp32.
+constexpr int kRouterChunks = 32;
+inline size_t bwd_layout(const Shape& s, size_t* off) {
+  const size_t R = (size_t)s.R(), d = (size_t)s.d, f = (size_t)s.f;
+  const size_t sizes[7] = {R * d * 2,  R * 2 * f * 4, R * f * 4, R * 2 * f * 2,
+                           R * d * 4,  (size_t)s.Tk() * 4,
+                           (size_t)kRouterChunks * (size_t)s.E * (d + 1) * 4};
+  size_t at = 0;
+  for (int i = 0; i < 7; ++i) {
+    off[i] = at;
+    at += (sizes[i] + 255) & ~(size_t)255;
+  }
+  return at;
+}
 hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
                            const void* W_gate_up, const void* W_down, const void* dy,
                            const int32_t* topk_idx, const float* topk_w,
@@ -150,8 +165,9 @@ hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
                            void* workspace, hipStream_t st);
 // Router load statistics from the logits: importance[E] (mean softmax
 // probability) and the balance loss; partial holds balance_partials(T) * E
-// doubles.
-int64_t balance_partials(int64_t T);
+// doubles (one row per workgroup of kBalTokens tokens).
+constexpr int kBalTokens = 16;
+inline int64_t balance_partials(int64_t T) { return (T + kBalTokens - 1) / kBalTokens; }
 hipError_t launch_balance(const Shape& s, const float* logits, double* partial,
                           double* importance, double* loss, hipStream_t st);
 hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* sorted_slot,

@@ -413,6 +413,7 @@ int oracle_combine(int64_t T, int64_t k, int64_t S, int64_t d, int dt,
       double acc = 0.0;
       for (int64_t j = 0; j < k; ++j) {
         int64_t row = slot_pos[t * k + j];
+        if (row < 0) continue; /* a copy dropped by a capacity adds nothing */
         acc += w[t * k + j] * elem(O, dt, row * d + i);
       }
       for (int64_t sg = 0; sg < S; ++sg) {

@@ -114,7 +114,8 @@ int oracle_dequant_mxfp4(int64_t rows, int64_t K, const uint8_t* q,
 
 /* Weighted combine of expert-output rows stored in permuted order
  * (element type dt, [T*k + S*T, d]):
- * y[t] = sum_j w[t,j] * O[slot_pos[t*k+j]] + sum_sigma O[T*k + sigma*T + t]. */
+ * y[t] = sum_j w[t,j] * O[slot_pos[t*k+j]] + sum_sigma O[T*k + sigma*T + t];
+ * copies with slot_pos < 0 (dropped by a capacity) add nothing. */
 int oracle_combine(int64_t T, int64_t k, int64_t S, int64_t d, int dt,
                    const void* O, const int32_t* slot_pos, const double* w,
                    double* y);
