@@ -27,8 +27,9 @@
 // the current one is multiplied), 4 waves each 64 x 64 with
 // v_mfma_f32_32x32x16_bf16.  An operand that is K-contiguous in memory is
 // copied to LDS row by row; one that is contiguous along M or N is
-// transposed on its way into LDS (2-byte LDS writes), so the MFMA fragments
-// are always 16-byte reads of 8 consecutive K elements.
+// transposed on its way into LDS (in registers, 4 K rows x 8 columns per
+// thread, then 8-byte LDS writes), so the MFMA fragments are always 16-byte
+// reads of 8 consecutive K elements.
 #include "moe_common.h"
 
 namespace moe {
@@ -56,14 +57,23 @@ __device__ __forceinline__ void store_kc(bf16_t* tile, int row, int kc, const u3
   *reinterpret_cast<u32x4*>(tile + row * kLRow + kc) = v;
 }
 
-// 8 consecutive M/N elements of one K row, written transposed: element i
-// goes to LDS row mn + i, column k.
-__device__ __forceinline__ void store_mnc(bf16_t* tile, int mn, int k, const u32x4& v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// A block of 4 K rows x 8 M/N columns (v[r]: the 8 elements of K row k + r,
+// two per word, the lower column in the low half), written transposed:
+// LDS row mn + i gets the 4 K elements k .. k+3 of column i (one 8-byte
+// write per row).
+__device__ __forceinline__ void store_mn_block(bf16_t* tile, int mn, int k, const u32x4 (&v)[4]) {
+  const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+  const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+  const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
+  const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    tile[(mn + 2 * i) * kLRow + k] = (bf16_t)(w[i] & 0xffffu);
-    tile[(mn + 2 * i + 1) * kLRow + k] = (bf16_t)(w[i] >> 16);
+  for (int p = 0; p < 4; ++p) {
+    // column 2p: the low halves; column 2p + 1: the high halves
+    const uint2 even = {(w0[p] & 0xffffu) | (w1[p] << 16), (w2[p] & 0xffffu) | (w3[p] << 16)};
+    const uint2 odd = {(w0[p] >> 16) | (w1[p] & 0xffff0000u),
+                       (w2[p] >> 16) | (w3[p] & 0xffff0000u)};
+    *reinterpret_cast<uint2*>(tile + (mn + 2 * p) * kLRow + k) = even;
+    *reinterpret_cast<uint2*>(tile + (mn + 2 * p + 1) * kLRow + k) = odd;
   }
 }
 
@@ -141,10 +151,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_gemm_kernel(
   const int64_t KK = ROWS ? K : rows;  // contraction length
   const bf16_t* Bg = B + (ROWS ? (int64_t)g * b_stride : 0);
 
-  // ---- staging plan: thread tid moves chunks tid and tid + 256 of each tile
-  // (512 chunks of 16 bytes).  K-contiguous tile: chunk c = row c/4, K
-  // elements 8*(c%4) ..; M/N-contiguous tile: chunk c = K row c/16, M/N
-  // elements 8*(c%16) ...
+  // ---- staging plan.  K-contiguous tile (ROWS: A, and B when B_KC):
+  // thread tid moves chunks tid and tid + 256 of the 512 chunks of 16
+  // bytes: tile row c/4, K elements 8*(c%4) ...  M/N-contiguous tile (its
+  // global rows are K rows): 128 blocks of 4 K rows x 8 M/N columns, block
+  // q = (kq = q/16, mq = q%16); one thread loads the block's four 16-byte
+  // row pieces and writes them transposed, as 8 rows of 4 K elements
+  // (8-byte LDS writes).  ROWS: threads 0..127 move B's blocks; otherwise
+  // threads 0..127 move A's and 128..255 B's.
   const bf16_t* arow[2];  // ROWS: A row of the chunk's tile row (null past the tile)
   const bf16_t* brow[2];  // ROWS && B_KC: B row n of the chunk
   int akc[2], aro[2];
@@ -168,49 +182,58 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_gemm_kernel(
       }
     }
   }
-  u32x4 ra[2], rb[2];
+  constexpr bool kHasMN = !(ROWS && B_KC);  // some operand is M/N-contiguous
+  const int q = tid & 127, kq = q >> 4, mq = q & 15;
+  const bool mn_thread = ROWS ? tid < 128 : true;
+  const bool mn_is_b = ROWS || tid >= 128;  // the operand of this thread's block
+  u32x4 ra[2], rb[2], rm[4];
   // global loads of K tile j into registers
   auto gload = [&](int j) {
     const int64_t k0 = (int64_t)j * kBK;
+    if constexpr (ROWS) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kBwdThreads * i;
-      if constexpr (ROWS) {
+      for (int i = 0; i < 2; ++i) {
         ra[i] = load_kc(arow[i], k0 + akc[i], KK);
-        if constexpr (B_KC) {
-          rb[i] = load_kc(brow[i], k0 + akc[i], KK);
-        } else {
-          // B[g][k][n]: K row k0 + c/16, columns n0 + 8*(c%16) ..
-          const int64_t kr = k0 + c / 16, n = n0 + 8 * (c % 16);
-          rb[i] = (kr < KK && n < N) ? ldg16(Bg + kr * ldb + n) : u32x4{0u, 0u, 0u, 0u};
-        }
-      } else {
-        // A[r][m] and B[src(r)][n]: K row = group row row_begin + k0 + c/16
-        const int64_t kr = k0 + c / 16;
-        const int64_t m = m0 + 8 * (c % 16), n = n0 + 8 * (c % 16);
-        if (kr < KK) {
-          const int64_t r = row_begin + kr;
-          const int64_t src = GATHER ? row_token(r, sorted_slot, Tk, k, T) : r;
-          ra[i] = m < M ? ldg16(A + r * lda + m) : u32x4{0u, 0u, 0u, 0u};
-          rb[i] = n < N ? ldg16(B + src * ldb + n) : u32x4{0u, 0u, 0u, 0u};
-        } else {
-          ra[i] = rb[i] = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (B_KC) rb[i] = load_kc(brow[i], k0 + akc[i], KK);
+      }
+    }
+    if constexpr (kHasMN) {
+      if (mn_thread) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t kr = k0 + 4 * kq + r;
+          u32x4 v = u32x4{0u, 0u, 0u, 0u};
+          if constexpr (ROWS) {
+            // B[g][k][n]: K row kr, columns n0 + 8*mq ..
+            const int64_t n = n0 + 8 * mq;
+            if (kr < KK && n < N) v = ldg16(Bg + kr * ldb + n);
+          } else if (kr < KK) {
+            // A[r][m] or B[src(r)][n] with r the group row row_begin + kr
+            const int64_t rr = row_begin + kr;
+            if (!mn_is_b) {
+              const int64_t m = m0 + 8 * mq;
+              if (m < M) v = ldg16(A + rr * lda + m);
+            } else {
+              const int64_t src = GATHER ? row_token(rr, sorted_slot, Tk, k, T) : rr;
+              const int64_t n = n0 + 8 * mq;
+              if (n < N) v = ldg16(B + src * ldb + n);
+            }
+          }
+          rm[r] = v;
         }
       }
     }
   };
   auto lstore = [&](int buf) {
+    if constexpr (ROWS) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kBwdThreads * i;
-      if constexpr (ROWS) {
+      for (int i = 0; i < 2; ++i) {
         store_kc(sm.a[buf], aro[i], akc[i], ra[i]);
         if constexpr (B_KC) store_kc(sm.b[buf], aro[i], akc[i], rb[i]);
-        else store_mnc(sm.b[buf], 8 * (c % 16), c / 16, rb[i]);
-      } else {
-        store_mnc(sm.a[buf], 8 * (c % 16), c / 16, ra[i]);
-        store_mnc(sm.b[buf], 8 * (c % 16), c / 16, rb[i]);
       }
+    }
+    if constexpr (kHasMN) {
+      if (mn_thread) store_mn_block(mn_is_b ? sm.b[buf] : sm.a[buf], 8 * mq, 4 * kq, rm);
     }
   };
 

@@ -96,15 +96,15 @@ __device__ __forceinline__ GroupFromIds group_from_ids(const int32_t* __restrict
 // themselves instead of a permutation (decode batches: at most 64 tokens),
 // and the workgroups of column tile 0 write that permutation (counts,
 // offsets, sorted_slot, slot_pos) for the steps that follow.
-template <bool GATED, int MB, bool FUSED>
-__global__ __launch_bounds__(256) void stream_gemm_kernel(
+template <bool GATED, int MB, bool FUSED, int NW = 4, int U = 1>
+__global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
     bf16_t* __restrict__ out, int64_t K, int64_t N, int64_t T, int64_t Tk, int64_t k,
     int G, int ntiles, const int32_t* __restrict__ topk_idx, int E,
     int32_t* __restrict__ p_counts, int32_t* __restrict__ p_offsets,
     int32_t* __restrict__ p_sorted, int32_t* __restrict__ p_slot_pos) {
-  __shared__ f32x4 red[3][MB][2][64];  // partials of waves 1..3
+  __shared__ f32x4 red[NW - 1][MB][2][64];  // partials of waves 1..NW-1
   __shared__ int s_list[64];           // FUSED: the group's copies, ascending
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = (int)blockIdx.x / ntiles;
@@ -197,35 +197,42 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
       accg[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
       accu[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // one K step at a time: latency is hidden by the other resident waves
-    // (explicit two-step register pipelining measured slower: it lowers
-    // occupancy more than it adds bytes in flight)
-    for (int64_t k0 = (int64_t)wave * 128; k0 < K; k0 += 512) {
-      StreamRegs<GATED, MB> r;
-      if constexpr (GATED) {
-        if (have_first) {
-          r = first;
-          have_first = false;
+    // U K steps per round (one by default: the other resident waves hide
+    // the latency; more steps per round cost occupancy)
+    for (int64_t k0 = (int64_t)wave * 128; k0 < K; k0 += 128 * NW * U) {
+      // U steps (k0, k0 + 128*NW, ...) loaded before any is used
+      StreamRegs<GATED, MB> r[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t ku = k0 + (int64_t)128 * NW * u;
+        if constexpr (GATED) {
+          if (u == 0 && have_first) {
+            r[0] = first;
+            have_first = false;
+          } else {
+            stream_load_w<GATED, MB>(r[u], Bg, Bu, ku, kb, K);
+          }
         } else {
-          stream_load_w<GATED, MB>(r, Bg, Bu, k0, kb, K);
+          stream_load_w<GATED, MB>(r[u], Bg, Bu, ku, kb, K);
         }
-      } else {
-        stream_load_w<GATED, MB>(r, Bg, Bu, k0, kb, K);
+        stream_load_a<GATED, MB>(r[u], Ap, ku, kb, K);
       }
-      stream_load_a<GATED, MB>(r, Ap, k0, kb, K);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 bg = zero_unless(r.ok[c], r.bg[c]);
-        const u32x4 bu = GATED ? zero_unless(r.ok[c], r.bu[c]) : bg;
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const u32x4 a = zero_unless(r.ok[c], r.a[mb][c]);
-          accg[mb] = mfma16(a, bg, accg[mb]);
-          if constexpr (GATED) accu[mb] = mfma16(a, bu, accu[mb]);
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 bg = zero_unless(r[u].ok[c], r[u].bg[c]);
+          const u32x4 bu = GATED ? zero_unless(r[u].ok[c], r[u].bu[c]) : bg;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const u32x4 a = zero_unless(r[u].ok[c], r[u].a[mb][c]);
+            accg[mb] = mfma16(a, bg, accg[mb]);
+            if constexpr (GATED) accu[mb] = mfma16(a, bu, accu[mb]);
+          }
         }
       }
     }
-    // add the four K-split partials in wave order
+    // add the NW K-split partials in wave order
     if (wave > 0) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-      for (int w = 0; w < 3; ++w) {
+      for (int w = 0; w < NW - 1; ++w) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           accg[mb] += red[w][mb][0][lane];
@@ -278,7 +285,15 @@ hipError_t launch_stream_gemm(bool gated, const Shape& s, const void* A,
                      nullptr, nullptr, nullptr, nullptr)
   if (gated) {
     switch (MB) {
-      case 1: MOE_STREAM(true, 1); break;
+      case 1:
+        // two K steps loaded per round (measured 172 -> 166 us on the decode
+        // gate_up; the fused form, which starts from its prefetched first
+        // step, gains nothing from it and keeps one step per round)
+        hipLaunchKernelGGL((stream_gemm_kernel<true, 1, false, 4, 2>), dim3(grid), dim3(256), 0,
+                           st, (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W,
+                           (bf16_t*)out, K, N, s.T, s.Tk(), s.k, G, ntiles, nullptr, (int)s.E,
+                           nullptr, nullptr, nullptr, nullptr);
+        break;
       case 2: MOE_STREAM(true, 2); break;
       case 3: MOE_STREAM(true, 3); break;
       default: MOE_STREAM(true, 4); break;
