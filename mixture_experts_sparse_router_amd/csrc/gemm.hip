@@ -208,6 +208,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void tiled_gemm_kernel(
   constexpr int BI = TBN / (RPC * NW);  // B copies per wave per stage
   static_assert(SBK == 32 || SBK == 64, "K tile");
   static_assert(AI >= 1 && BI >= 1 && NI >= 2, "tile split");
+  static_assert(BM % (RPC * NW) == 0 && TBN % (RPC * NW) == 0 && BM % 64 == 0, "copy plan");
   constexpr int NF = MI + NI;   // operand fragments per sub-step
   constexpr uint32_t ROWB = SBK * 2;         // bytes per LDS row
   constexpr uint32_t STA = BM * ROWB;         // bytes per stage of A
@@ -542,10 +543,15 @@ hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot
   //  - large groups (>= 512 rows on average): 256 x 256 tiles, 8 waves (two
   //    per SIMD, so one computes while the other waits), K tiles of 64
   //    (whole 128-byte lines per copied row) in 2 stages of 64 KB;
-  //  - smaller groups, gate_up: 128 x 256 tiles, 8 waves, K tiles of 64, 3
-  //    stages; down: 128 x 256 tiles, 4 waves, K tiles of 32, two workgroups
-  //    per CU with 3 stages each.
+  //  - routed groups of 112-168 rows on average (balanced routers with many
+  //    experts): 192 x 256 tiles, 8 waves, K tiles of 64, 2 stages, so that
+  //    a group rarely spills a few rows into a second m-tile that would read
+  //    the weight panel again (DeepSeek-V3 shape: gate_up 3.64 -> 3.54 ms);
+  //  - other small groups, gate_up: 128 x 256 tiles, 8 waves, K tiles of
+  //    64, 3 stages; down: 128 x 256 tiles, 4 waves, K tiles of 32, two
+  //    workgroups per CU with 3 stages each.
   const int64_t avg_rows = s.R() / (s.G() > 0 ? s.G() : 1);
+  const int64_t routed_mean = s.Tk() / s.E;
   const int64_t ncols = GATED ? TBN / 2 : TBN;
   const int ntN = (int)((N + ncols - 1) / ncols);
 #define MOE_TILED(bm, nst, occ, nw, sbk)                                                 \
@@ -555,6 +561,8 @@ hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot
                      (bf16_t*)out, K, N, s.T, s.Tk(), s.k, G, ntN)
   if (avg_rows >= 512) {
     MOE_TILED(256, 2, 1, 8, 64);
+  } else if (routed_mean > 112 && routed_mean <= 168) {
+    MOE_TILED(192, 2, 1, 8, 64);
   } else if (GATED) {
     MOE_TILED(128, 3, 1, 8, 64);
   } else {

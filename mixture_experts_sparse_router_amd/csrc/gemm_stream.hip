@@ -300,7 +300,13 @@ hipError_t launch_stream_gemm(bool gated, const Shape& s, const void* A,
     }
   } else {
     switch (MB) {
-      case 1: MOE_STREAM(false, 1); break;
+      case 1:
+        // 8 waves (measured 85 -> 83 us on the decode down GEMM)
+        hipLaunchKernelGGL((stream_gemm_kernel<false, 1, false, 8, 1>), dim3(grid), dim3(512), 0,
+                           st, (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W,
+                           (bf16_t*)out, K, N, s.T, s.Tk(), s.k, G, ntiles, nullptr, (int)s.E,
+                           nullptr, nullptr, nullptr, nullptr);
+        break;
       case 2: MOE_STREAM(false, 2); break;
       case 3: MOE_STREAM(false, 3); break;
       default: MOE_STREAM(false, 4); break;

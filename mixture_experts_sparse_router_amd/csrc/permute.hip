@@ -7,7 +7,8 @@
 // section "Expert Backend", grouped_mm).  Order inside a group: ascending
 // copy id s = t*k + j, which makes the permutation unique.
 //
-// One workgroup of 16 waves.  Wave w owns the contiguous copy range
+// Batches below 8192 copies: one workgroup of 16 waves (larger ones: the
+// multi-workgroup form further down).  Wave w owns the contiguous copy range
 // [w*seg, (w+1)*seg) and walks it 64 copies at a time:
 //   A. rank every copy among the earlier copies of its expert in the same
 //      wave range: lanes with equal expert id are found with one ballot per
@@ -194,6 +195,166 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
   }
 }
 
+// ------------------------------------------------------- multi-workgroup
+// For large batches (n >= kMultiMin copies) the same permutation in four
+// launches, none of whose workgroups waits for another:
+//   1. rank (NB workgroups of kChunk copies): each copy's rank among the
+//      earlier copies of its key in the workgroup (per-wave ranks as in A,
+//      plus the wave's base inside the workgroup), parked in slot_pos; the
+//      workgroup's key histogram becomes row b of H.
+//   2. scan (one workgroup): per key, the exclusive prefix of H's rows in
+//      place; counts and offsets as in B; row NB of H gets the first row of
+//      each expert's copies over capacity.
+//   3. place (NB workgroups): row = the key's first row + prefix + parked
+//      rank, stored in slot_pos (a dropped copy as -2 - row).
+//   4. scatter: sorted_slot[row] = s, slot_pos = -1 for dropped copies.
+// H, (NB + 1) x (E + 1) int32, lives in sorted_slot until step 4: steps 1-3
+// write no other entry of sorted_slot, and step 4 reads no entry of H.
+constexpr int kChunk = 2 * 64 * kWaves;  // copies per workgroup: 2 steps per wave
+constexpr int64_t kMultiMin = 8192;
+
+__global__ __launch_bounds__(kThreads) void permute_rank_kernel(
+    const int32_t* __restrict__ idx, int32_t* __restrict__ slot_pos, int32_t* __restrict__ H,
+    int64_t n, int E, int nbits) {
+  extern __shared__ int32_t whist[];  // [kWaves][E + 1]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int E1 = E + 1;
+  int32_t* hist = whist + wave * E1;
+  const uint64_t lanes_below = (1ull << lane) - 1ull;
+  const int64_t s0 = (int64_t)blockIdx.x * kChunk + wave * 128 + lane;
+  int v[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) v[u] = s0 + 64 * u < n ? idx[s0 + 64 * u] : -1;
+  for (int e = lane; e < E1; e += 64) hist[e] = 0;
+  int key[2], r[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const bool active = s0 + 64 * u < n;
+    // E: the bin of invalid ids; E + 1: idle lane
+    key[u] = !active ? E + 1 : (v[u] >= 0 && v[u] < E) ? v[u] : E;
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key[u] >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    const int leader = 63 - __clzll(peers);
+    int before = 0;
+    if (active && lane == leader) {
+      before = hist[key[u]];
+      hist[key[u]] = before + __popcll(peers);
+    }
+    r[u] = __shfl(before, leader, 64) + __popcll(peers & lanes_below);
+  }
+  __syncthreads();
+  // per key: the waves' exclusive bases inside the workgroup, and its total
+  for (int e = threadIdx.x; e < E1; e += kThreads) {
+    int run = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = whist[w * E1 + e];
+      whist[w * E1 + e] = run;
+      run += c;
+    }
+    H[(int64_t)blockIdx.x * E1 + e] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (s0 + 64 * u < n) slot_pos[s0 + 64 * u] = hist[key[u]] + r[u];
+}
+
+__global__ __launch_bounds__(kThreads) void permute_scan_kernel(
+    int32_t* __restrict__ H, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int64_t T, int64_t k, int E, int S, int NB, int cap) {
+  __shared__ int32_t part[kThreads];
+  __shared__ int32_t tot[kThreads];
+  __shared__ int32_t tmp[2 * kWaves + 1];
+  const int tid = threadIdx.x;
+  const int E1 = E + 1;  // <= kThreads
+  int Ep = 1;
+  while (Ep < E1) Ep <<= 1;
+  const int P = kThreads / Ep;  // workgroup rows of H split in P parts per key
+  const int e = tid % Ep, p = tid / Ep;
+  const int r0 = (int)((int64_t)NB * p / P), r1 = (int)((int64_t)NB * (p + 1) / P);
+  int sum = 0;
+  if (e < E1)
+    for (int r = r0; r < r1; ++r) sum += H[(int64_t)r * E1 + e];
+  part[tid] = sum;
+  __syncthreads();
+  if (e < E1) {
+    int run = 0, all = 0;
+    for (int q = 0; q < P; ++q) {
+      const int c = part[q * Ep + e];
+      if (q < p) run += c;
+      all += c;
+    }
+    if (p == 0) tot[e] = all;
+    for (int r = r0; r < r1; ++r) {
+      const int c = H[(int64_t)r * E1 + e];
+      H[(int64_t)r * E1 + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // as step B of the one-workgroup kernel
+  const int g = tid;
+  const int total = g < E ? tot[g] : 0;
+  const int n_inv = tot[E];
+  const int kept = g < E ? (total < cap ? total : cap) : 0;
+  int n_over = 0, n_kept = 0;
+  const int over_base = n_inv + block_exclusive_scan(g < E ? total - kept : 0, tmp, &n_over);
+  const int kept_off = block_exclusive_scan(kept, tmp, &n_kept);
+  const int n_drop = n_inv + n_over;
+  const int Tk = (int)(T * k);
+  if (g < E) {
+    counts[g] = kept;
+    offsets[g] = n_drop + kept_off;
+    H[(int64_t)NB * E1 + g] = over_base;
+  } else if (g < E + S) {
+    counts[g] = (int)T;
+    offsets[g] = Tk + (g - E) * (int)T;
+  }
+  if (g == 0) offsets[E + S] = Tk + S * (int)T;
+}
+
+__global__ __launch_bounds__(kThreads) void permute_place_kernel(
+    const int32_t* __restrict__ idx, int32_t* __restrict__ slot_pos,
+    const int32_t* __restrict__ H, const int32_t* __restrict__ offsets, int64_t n, int E,
+    int NB, int cap) {
+  __shared__ int32_t base[kThreads];      // [E + 1]: the key's copies in earlier workgroups
+  __shared__ int32_t row_kept[kThreads];  // [E]
+  __shared__ int32_t row_over[kThreads];  // [E]
+  const int tid = threadIdx.x;
+  const int E1 = E + 1;
+  if (tid < E1) base[tid] = H[(int64_t)blockIdx.x * E1 + tid];
+  if (tid < E) {
+    row_kept[tid] = offsets[tid];
+    row_over[tid] = H[(int64_t)NB * E1 + tid];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t s = (int64_t)blockIdx.x * kChunk + u * kThreads + tid;
+    if (s >= n) continue;
+    const int v = idx[s];
+    const bool valid = v >= 0 && v < E;
+    const int rank = base[valid ? v : E] + slot_pos[s];  // among the same key's copies
+    const bool keep = valid && rank < cap;
+    const int pos = !valid ? rank : keep ? row_kept[v] + rank : row_over[v] + rank - cap;
+    slot_pos[s] = keep ? pos : -2 - pos;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
+    int32_t* __restrict__ slot_pos, int32_t* __restrict__ sorted_slot, int64_t n) {
+  const int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (s >= n) return;
+  const int v = slot_pos[s];
+  sorted_slot[v >= 0 ? v : -2 - v] = (int32_t)s;
+  if (v < 0) slot_pos[s] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int64_t capacity,
@@ -203,6 +364,25 @@ hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int64_t capac
   while ((1 << nbits) <= s.E + 1) ++nbits;  // keys 0..E+1 (E: invalid id, E+1: idle lane)
   // no capacity, or one no expert can reach: every copy of a valid id is kept
   const int cap = capacity < 0 || capacity > s.Tk() ? (int)s.Tk() : (int)capacity;
+  const int64_t n = s.Tk();
+  const int64_t NB = (n + kChunk - 1) / kChunk;
+  const int E1 = (int)s.E + 1;
+  // the multi-workgroup form needs H ((NB + 1) x (E + 1)) to fit in
+  // sorted_slot and at most kThreads keys
+  if (n >= kMultiMin && E1 <= kThreads && (NB + 1) * E1 <= n) {
+    int32_t* H = sorted_slot;
+    const size_t lds = (size_t)kWaves * E1 * sizeof(int32_t);
+    hipLaunchKernelGGL(permute_rank_kernel, dim3((unsigned)NB), dim3(kThreads), lds, st,
+                       topk_idx, slot_pos, H, n, (int)s.E, nbits);
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kThreads), 0, st, H, counts, offsets,
+                       s.T, s.k, (int)s.E, (int)s.S, (int)NB, cap);
+    hipLaunchKernelGGL(permute_place_kernel, dim3((unsigned)NB), dim3(kThreads), 0, st,
+                       topk_idx, slot_pos, (const int32_t*)H, (const int32_t*)offsets, n,
+                       (int)s.E, (int)NB, cap);
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, st, slot_pos, sorted_slot, n);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kThreads), 0, st, topk_idx, counts,
                      offsets, sorted_slot, slot_pos, s.T, s.k, (int)s.E, (int)s.S,
                      nbits, cap);

@@ -112,10 +112,15 @@ def test_route(name):
 # ---------------------------------------------------------------- permute
 
 PERMUTE_CASES = [
-    # (T, E, k, S, zipf)
+    # (T, E, k, S, zipf).  T*k >= 8192 copies with E <= 1023 take the
+    # multi-workgroup kernels (2048 copies per workgroup), the rest one
+    # workgroup: ragged last chunks (8196, 10500), the largest key count
+    # (E = 1023), just below the switch (8190) and E = 1024 above it
     (16, 32, 4, 0, None), (37, 8, 2, 0, None), (1, 1, 1, 0, None), (0, 4, 2, 1, None),
     (4096, 128, 8, 0, 1.2), (4096, 256, 8, 1, None), (8192, 8, 2, 0, None),
     (300, 1000, 7, 24, None), (513, 1023, 64, 1, None), (2000, 64, 3, 2, 2.0),
+    (2049, 1023, 4, 1, None), (1500, 60, 7, 2, 2.0), (1170, 7, 7, 0, None),
+    (200, 1024, 64, 0, None),
 ]
 
 
@@ -138,6 +143,55 @@ def test_permute(case):
     assert np.array_equal(host(sp), sp_ref)
 
 
+def _expect_with_invalid(idx, E, S, T, cap):
+    """The documented layout when some ids lie outside [0, E): those copies
+    first (slot order), then the copies over capacity (by expert, slot
+    order), then each expert's kept copies; dropped copies get slot_pos -1."""
+    flat = idx.ravel().astype(np.int64)
+    n = flat.size
+    valid = (flat >= 0) & (flat < E)
+    per = [np.flatnonzero(flat == e) for e in range(E)]
+    rows = [np.flatnonzero(~valid)]
+    rows += [p[cap:] for p in per]
+    n_drop = sum(len(r) for r in rows)
+    rows += [p[:cap] for p in per]
+    ss = np.concatenate(rows).astype(np.int64)
+    counts = np.array([min(len(p), cap) for p in per] + [T] * S, np.int64)
+    offsets = np.concatenate([[n_drop], n_drop + np.cumsum(counts)])
+    sp = np.full(n, -1, np.int64)
+    sp[ss[n_drop:]] = np.arange(n_drop, n)
+    return counts, offsets, ss, sp
+
+
+@pytest.mark.parametrize("case", [(37, 8, 2, 0), (4096, 128, 8, 1), (1500, 60, 7, 2)], ids=str)
+def test_permute_invalid_ids(case):
+    """Ids outside [0, E) select no expert: their copies take the first rows,
+    in slot order, with slot_pos -1 (one-workgroup and multi-workgroup
+    forms, with and without a capacity)."""
+    T, E, k, S = case
+    idx = moe_synth.random_routing((51, T, E), T, E, k, None)
+    rng = np.random.default_rng([51, T])
+    flat = idx.ravel().copy()
+    m = rng.random(flat.size) < 0.05
+    flat[m] = rng.choice(np.array([-1, E, E + 7, -(1 << 30)], np.int32), int(m.sum()))
+    idx = flat.reshape(idx.shape).astype(np.int32)
+    s = moe.shape(T, 8, 8, E, k, S, moe.MOE_DT_BF16)
+    G = E + S
+    for cap in (None, max(1, T * k // E // 2)):
+        print(f"permute invalid ids T={T} E={E} k={k} S={S} capacity={cap}", flush=True)
+        counts, offsets = empty((G,), "i32"), empty((G + 1,), "i32")
+        ss, sp = empty((T * k,), "i32"), empty((T * k,), "i32")
+        if cap is None:
+            moe.moe_permute(s, dev(idx), counts, offsets, ss, sp)
+        else:
+            moe.moe_permute_capacity(s, dev(idx), cap, counts, offsets, ss, sp)
+        _sync()
+        want = _expect_with_invalid(idx, E, S, T, T * k if cap is None else cap)
+        for got, w, what in zip((counts, offsets, ss, sp), want,
+                                ("counts", "offsets", "sorted_slot", "slot_pos")):
+            assert np.array_equal(host(got), w), f"{what} differs (capacity {cap})"
+
+
 # ----------------------------------------------------------- expert GEMMs
 
 def _rows_of(idx, ss, T, k, E, S):
@@ -158,6 +212,11 @@ GEMM_CASES = [
     ("tiled_T65", 65, 128, 64, 2, 2, 0, "bf16", None),
     # >= 512 rows per group on average: the 256-row tiles; K % 32 = 8 in both GEMMs
     ("tiled_bm256_ragged_k", 1100, 264, 136, 2, 1, 0, "bf16", None),
+    # routed groups of 112-168 rows on average: the 192-row tiles (ragged K,
+    # a shared expert, several bands of n-tiles)
+    ("tiled_bm192_ragged_k", 700, 264, 200, 10, 2, 0, "bf16", None),
+    ("tiled_bm192_shared", 520, 520, 136, 4, 1, 1, "bf16", None),
+    ("tiled_bm192_bands", 300, 1280, 1216, 4, 2, 0, "bf16", None),
     # K shorter than one K tile (40 and 24): one partly zero-filled tile
     ("tiled_k_below_tile", 100, 40, 24, 4, 2, 0, "bf16", None),
     # the most expert groups the library takes (E + S = 1024)
