@@ -26,10 +26,11 @@
 // in LDS (double buffered, the next tile's global loads in registers while
 // the current one is multiplied), 4 waves each 64 x 64 with
 // v_mfma_f32_32x32x16_bf16.  An operand that is K-contiguous in memory is
-// copied to LDS row by row; one that is contiguous along M or N is
-// transposed on its way into LDS (in registers, 4 K rows x 8 columns per
-// thread, then 8-byte LDS writes), so the MFMA fragments are always 16-byte
-// reads of 8 consecutive K elements.
+// copied to LDS row by row and read as 16-byte fragments of 8 consecutive K
+// elements.  One that is contiguous along M or N is copied as it lies (K
+// rows of 128 M/N elements) and its fragments are read with gfx950's
+// transposing LDS load (ds_read_b64_tr_b16), which hands each lane 4
+// consecutive K elements of one M/N column; two of them make a fragment.
 #include "moe_common.h"
 
 namespace moe {
@@ -38,43 +39,41 @@ namespace {
 constexpr int kBT = 128;        // tile rows and columns
 constexpr int kBK = 32;         // K per stage
 constexpr int kLRow = 40;       // LDS row stride in bf16 (80 bytes: conflict-light 16-byte reads)
+constexpr int kMNRow = 160;     // M/N-major tile row stride in bf16 (320 bytes: 64-byte shift per row)
 constexpr int kBwdThreads = 256;
+static_assert(kBK * kMNRow == kBT * kLRow, "both tile forms fill the same LDS");
 
-// Operand tile in LDS: [128 rows (M or N)][32 K] bf16, row stride kLRow.
+// Operand tile in LDS, K-major: [128 rows (M or N)][32 K] bf16, row stride
+// kLRow; or M/N-major: [32 K rows][128 M or N] bf16, row stride kMNRow.
 struct BwdSmem {
   bf16_t a[2][kBT * kLRow];
   bf16_t b[2][kBT * kLRow];
   int find[8];
 };
 
-// 16 bytes of a K-contiguous row: elements [k, k+8) of the row at p (or
-// zeros when p is null or k is past K).
-__device__ __forceinline__ u32x4 load_kc(const bf16_t* p, int64_t k, int64_t K) {
-  return (p && k < K) ? ldg16(p + k) : u32x4{0u, 0u, 0u, 0u};
-}
-
 __device__ __forceinline__ void store_kc(bf16_t* tile, int row, int kc, const u32x4& v) {
   *reinterpret_cast<u32x4*>(tile + row * kLRow + kc) = v;
 }
 
-// A block of 4 K rows x 8 M/N columns (v[r]: the 8 elements of K row k + r,
-// two per word, the lower column in the low half), written transposed:
-// LDS row mn + i gets the 4 K elements k .. k+3 of column i (one 8-byte
-// write per row).
-__device__ __forceinline__ void store_mn_block(bf16_t* tile, int mn, int k, const u32x4 (&v)[4]) {
-  const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-  const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-  const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
-  const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    // column 2p: the low halves; column 2p + 1: the high halves
-    const uint2 even = {(w0[p] & 0xffffu) | (w1[p] << 16), (w2[p] & 0xffffu) | (w3[p] << 16)};
-    const uint2 odd = {(w0[p] >> 16) | (w1[p] & 0xffff0000u),
-                       (w2[p] >> 16) | (w3[p] & 0xffff0000u)};
-    *reinterpret_cast<uint2*>(tile + (mn + 2 * p) * kLRow + k) = even;
-    *reinterpret_cast<uint2*>(tile + (mn + 2 * p + 1) * kLRow + k) = odd;
-  }
+// Fragment of the 32x32x16 MFMA from an M/N-major tile: M/N indices
+// mn .. mn+31, K elements 16 ks .. +15; lane l gets column mn + (l % 32),
+// K 8 (l / 32) .. +7 (the layout of a 16-byte K-major fragment read).  In
+// each group of 16 lanes (g = l / 16, i = l % 16) the transposing load hands
+// lane i element i % 4 of the 8 bytes addressed by lane 4q + i / 4 as its
+// element q; so lane i addresses K row r0 + i / 4, columns c0 + 4 (i % 4) ..
+// +3, and receives column c0 + i of K rows r0 .. r0+3 (a second load: r0+4
+// .. r0+7), with c0 = mn + 16 (g % 2) and r0 = 16 ks + 8 (g / 2).
+__device__ __forceinline__ u32x4 frag_mn(const bf16_t* tile, int mn, int ks, int lane) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const int g = lane >> 4, i = lane & 15;
+  const int row = 16 * ks + 8 * (g >> 1) + (i >> 2);
+  const int col = mn + 16 * (g & 1) + 4 * (i & 3);
+  const bf16_t* p = tile + row * kMNRow + col;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * kMNRow));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return u32x4{a.x, a.y, b.x, b.y};
 }
 
 // Which row group (and m-tile) a workgroup owns: group g has
@@ -151,14 +150,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_gemm_kernel(
   const int64_t KK = ROWS ? K : rows;  // contraction length
   const bf16_t* Bg = B + (ROWS ? (int64_t)g * b_stride : 0);
 
-  // ---- staging plan.  K-contiguous tile (ROWS: A, and B when B_KC):
-  // thread tid moves chunks tid and tid + 256 of the 512 chunks of 16
-  // bytes: tile row c/4, K elements 8*(c%4) ...  M/N-contiguous tile (its
-  // global rows are K rows): 128 blocks of 4 K rows x 8 M/N columns, block
-  // q = (kq = q/16, mq = q%16); one thread loads the block's four 16-byte
-  // row pieces and writes them transposed, as 8 rows of 4 K elements
-  // (8-byte LDS writes).  ROWS: threads 0..127 move B's blocks; otherwise
-  // threads 0..127 move A's and 128..255 B's.
+  // ---- staging plan: every thread moves chunks c = tid and tid + 256 of
+  // the 512 16-byte chunks of each operand tile.  K-major tile (ROWS: A,
+  // and B when B_KC): tile row c/4, K elements 8*(c%4) .. of that row.
+  // M/N-major tile (its global rows are K rows): K row c/16, M/N elements
+  // 8*(c%16) .. of that row.
+  constexpr bool A_MN = !ROWS;
+  constexpr bool B_MN = ROWS ? !B_KC : true;
   const bf16_t* arow[2];  // ROWS: A row of the chunk's tile row (null past the tile)
   const bf16_t* brow[2];  // ROWS && B_KC: B row n of the chunk
   int akc[2], aro[2];
@@ -182,58 +180,55 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_gemm_kernel(
       }
     }
   }
-  constexpr bool kHasMN = !(ROWS && B_KC);  // some operand is M/N-contiguous
-  const int q = tid & 127, kq = q >> 4, mq = q & 15;
-  const bool mn_thread = ROWS ? tid < 128 : true;
-  const bool mn_is_b = ROWS || tid >= 128;  // the operand of this thread's block
-  u32x4 ra[2], rb[2], rm[4];
+  // every load reads a valid address (the group's first row, or the operand's
+  // first row, when the chunk lies outside the tile) and is zeroed by a
+  // select, so the loads stay unconditional
+  const bf16_t* a_safe = ROWS ? A : A + row_begin * lda;
+  const bf16_t* b_safe = ROWS ? Bg : B;
+  u32x4 ra[2], rb[2];
   // global loads of K tile j into registers
   auto gload = [&](int j) {
     const int64_t k0 = (int64_t)j * kBK;
-    if constexpr (ROWS) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        ra[i] = load_kc(arow[i], k0 + akc[i], KK);
-        if constexpr (B_KC) rb[i] = load_kc(brow[i], k0 + akc[i], KK);
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + kBwdThreads * i;
+      const int64_t kr = k0 + c / 16;   // M/N-major: the chunk's K row
+      const int64_t o8 = 8 * (c % 16);  // and its first M/N element in the tile
+      if constexpr (!A_MN) {
+        const bool ok = arow[i] != nullptr && k0 + akc[i] < KK;
+        ra[i] = zero_unless(ok, ldg16(ok ? arow[i] + k0 + akc[i] : a_safe));
+      } else {
+        // A[r][m], r the group row row_begin + kr
+        const int64_t m = m0 + o8;
+        const bool ok = kr < KK && m < M;
+        ra[i] = zero_unless(ok, ldg16(ok ? A + (row_begin + kr) * lda + m : a_safe));
       }
-    }
-    if constexpr (kHasMN) {
-      if (mn_thread) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t kr = k0 + 4 * kq + r;
-          u32x4 v = u32x4{0u, 0u, 0u, 0u};
-          if constexpr (ROWS) {
-            // B[g][k][n]: K row kr, columns n0 + 8*mq ..
-            const int64_t n = n0 + 8 * mq;
-            if (kr < KK && n < N) v = ldg16(Bg + kr * ldb + n);
-          } else if (kr < KK) {
-            // A[r][m] or B[src(r)][n] with r the group row row_begin + kr
-            const int64_t rr = row_begin + kr;
-            if (!mn_is_b) {
-              const int64_t m = m0 + 8 * mq;
-              if (m < M) v = ldg16(A + rr * lda + m);
-            } else {
-              const int64_t src = GATHER ? row_token(rr, sorted_slot, Tk, k, T) : rr;
-              const int64_t n = n0 + 8 * mq;
-              if (n < N) v = ldg16(B + src * ldb + n);
-            }
-          }
-          rm[r] = v;
-        }
+      if constexpr (!B_MN) {
+        const bool ok = brow[i] != nullptr && k0 + akc[i] < KK;
+        rb[i] = zero_unless(ok, ldg16(ok ? brow[i] + k0 + akc[i] : b_safe));
+      } else if constexpr (ROWS) {
+        // B[g][k][n]: K row kr
+        const int64_t n = n0 + o8;
+        const bool ok = kr < KK && n < N;
+        rb[i] = zero_unless(ok, ldg16(ok ? Bg + kr * ldb + n : b_safe));
+      } else {
+        // B[src(r)][n], r the group row row_begin + kr
+        const int64_t n = n0 + o8;
+        const bool ok = kr < KK && n < N;
+        const int64_t rr = row_begin + (ok ? kr : 0);
+        const int64_t src = GATHER ? row_token(rr, sorted_slot, Tk, k, T) : rr;
+        rb[i] = zero_unless(ok, ldg16(ok ? B + src * ldb + n : b_safe));
       }
     }
   };
   auto lstore = [&](int buf) {
-    if constexpr (ROWS) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        store_kc(sm.a[buf], aro[i], akc[i], ra[i]);
-        if constexpr (B_KC) store_kc(sm.b[buf], aro[i], akc[i], rb[i]);
-      }
-    }
-    if constexpr (kHasMN) {
-      if (mn_thread) store_mn_block(mn_is_b ? sm.b[buf] : sm.a[buf], 8 * mq, 4 * kq, rm);
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + kBwdThreads * i;
+      if constexpr (!A_MN) store_kc(sm.a[buf], aro[i], akc[i], ra[i]);
+      else *reinterpret_cast<u32x4*>(sm.a[buf] + (c / 16) * kMNRow + 8 * (c % 16)) = ra[i];
+      if constexpr (!B_MN) store_kc(sm.b[buf], aro[i], akc[i], rb[i]);
+      else *reinterpret_cast<u32x4*>(sm.b[buf] + (c / 16) * kMNRow + 8 * (c % 16)) = rb[i];
     }
   };
 
@@ -262,12 +257,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_gemm_kernel(
         u32x4 fa[2], fb[2];
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
-          fa[mi] = *reinterpret_cast<const u32x4*>(
-              sm.a[buf] + (wm * 64 + mi * 32 + lr) * kLRow + 16 * ks + 8 * lh);
+          fa[mi] = A_MN ? frag_mn(sm.a[buf], wm * 64 + mi * 32, ks, lane)
+                        : *reinterpret_cast<const u32x4*>(
+                              sm.a[buf] + (wm * 64 + mi * 32 + lr) * kLRow + 16 * ks + 8 * lh);
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
-          fb[ni] = *reinterpret_cast<const u32x4*>(
-              sm.b[buf] + (wn * 64 + ni * 32 + lr) * kLRow + 16 * ks + 8 * lh);
+          fb[ni] = B_MN ? frag_mn(sm.b[buf], wn * 64 + ni * 32, ks, lane)
+                        : *reinterpret_cast<const u32x4*>(
+                              sm.b[buf] + (wn * 64 + ni * 32 + lr) * kLRow + 16 * ks + 8 * lh);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll

@@ -25,20 +25,20 @@ namespace {
 // loads, for chunk c of a K step, elements [k0 + 32c + 8kb, +8) of weight
 // row n0+j and of token row j: 4 lanes cover 64 contiguous bytes of a row
 // per load.
-template <bool GATED, int MB>
+template <bool GATED, int MB, int CH>
 struct StreamRegs {
-  u32x4 bg[4], bu[4], a[MB][4];
-  bool ok[4];  // chunk c lies inside K (else its registers are zeroed at use)
+  u32x4 bg[CH], bu[CH], a[MB][CH];
+  bool ok[CH];  // chunk c lies inside K (else its registers are zeroed at use)
 };
 
 // Loads of one K step: the weight rows' chunks and the token rows' chunks.
 // Chunks past K read a valid address (offset 0) and are zeroed by a select
 // when they are used, so the loads stay branch-free.
-template <bool GATED, int MB>
-__device__ __forceinline__ void stream_load_w(StreamRegs<GATED, MB>& r, const bf16_t* Bg,
+template <bool GATED, int MB, int CH>
+__device__ __forceinline__ void stream_load_w(StreamRegs<GATED, MB, CH>& r, const bf16_t* Bg,
                                               const bf16_t* Bu, int64_t k0, int kb, int64_t K) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < CH; ++c) {
     const int64_t kk = k0 + 32 * c + 8 * kb;
     const bool ok = kk < K;
     const int64_t ka = ok ? kk : 0;
@@ -47,11 +47,12 @@ __device__ __forceinline__ void stream_load_w(StreamRegs<GATED, MB>& r, const bf
     if constexpr (GATED) r.bu[c] = ldg16(Bu + ka);
   }
 }
-template <bool GATED, int MB>
-__device__ __forceinline__ void stream_load_a(StreamRegs<GATED, MB>& r, const bf16_t* const* Ap,
-                                              int64_t k0, int kb, int64_t K) {
+template <bool GATED, int MB, int CH>
+__device__ __forceinline__ void stream_load_a(StreamRegs<GATED, MB, CH>& r,
+                                              const bf16_t* const* Ap, int64_t k0, int kb,
+                                              int64_t K) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < CH; ++c) {
     const int64_t kk = k0 + 32 * c + 8 * kb;
     const int64_t ka = kk < K ? kk : 0;
 #pragma unroll
@@ -96,7 +97,7 @@ __device__ __forceinline__ GroupFromIds group_from_ids(const int32_t* __restrict
 // themselves instead of a permutation (decode batches: at most 64 tokens),
 // and the workgroups of column tile 0 write that permutation (counts,
 // offsets, sorted_slot, slot_pos) for the steps that follow.
-template <bool GATED, int MB, bool FUSED, int NW = 4, int U = 1>
+template <bool GATED, int MB, bool FUSED, int NW = 4, int U = 1, int CH = 4>
 __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
@@ -121,9 +122,10 @@ __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
   // group's rows, so their loads are issued before the group is looked up
   // (measured faster; an empty group drops them unused: at most one K step
   // per wave is read of an expert without rows)
-  StreamRegs<GATED, MB> first;
+  constexpr int KW = 32 * CH;  // K elements per step
+  StreamRegs<GATED, MB, CH> first;
   bool have_first = GATED;
-  if constexpr (GATED) stream_load_w<GATED, MB>(first, Bg, Bu, (int64_t)wave * 128, kb, K);
+  if constexpr (GATED) stream_load_w<GATED, MB, CH>(first, Bg, Bu, (int64_t)wave * KW, kb, K);
 
   int64_t row_begin, rows;
   if constexpr (FUSED) {
@@ -199,28 +201,28 @@ __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
     }
     // U K steps per round (one by default: the other resident waves hide
     // the latency; more steps per round cost occupancy)
-    for (int64_t k0 = (int64_t)wave * 128; k0 < K; k0 += 128 * NW * U) {
-      // U steps (k0, k0 + 128*NW, ...) loaded before any is used
-      StreamRegs<GATED, MB> r[U];
+    for (int64_t k0 = (int64_t)wave * KW; k0 < K; k0 += (int64_t)KW * NW * U) {
+      // U steps (k0, k0 + KW*NW, ...) loaded before any is used
+      StreamRegs<GATED, MB, CH> r[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t ku = k0 + (int64_t)128 * NW * u;
+        const int64_t ku = k0 + (int64_t)KW * NW * u;
         if constexpr (GATED) {
           if (u == 0 && have_first) {
             r[0] = first;
             have_first = false;
           } else {
-            stream_load_w<GATED, MB>(r[u], Bg, Bu, ku, kb, K);
+            stream_load_w<GATED, MB, CH>(r[u], Bg, Bu, ku, kb, K);
           }
         } else {
-          stream_load_w<GATED, MB>(r[u], Bg, Bu, ku, kb, K);
+          stream_load_w<GATED, MB, CH>(r[u], Bg, Bu, ku, kb, K);
         }
-        stream_load_a<GATED, MB>(r[u], Ap, ku, kb, K);
+        stream_load_a<GATED, MB, CH>(r[u], Ap, ku, kb, K);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < CH; ++c) {
           const u32x4 bg = zero_unless(r[u].ok[c], r[u].bg[c]);
           const u32x4 bu = GATED ? zero_unless(r[u].ok[c], r[u].bu[c]) : bg;
 #pragma unroll
