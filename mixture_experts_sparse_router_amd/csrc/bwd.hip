@@ -8,7 +8,8 @@
 // permutation (expert groups of rows):
 //   1. combine_bwd  dO[r] = w dy_t (shared rows: dy_t), dw_tj = dy_t . O[r];
 //      router_dl    dl_tj = w_tj (dw_tj - sum_i w_ti dw_ti)
-//   2. H = Xg Wgu_e^T           grouped GEMM over rows (recomputes [g; u])
+//   2. H = Xg Wgu_e^T           the forward's tiled gate_up GEMM with a
+//                               pre-activation fp32 output (recomputes [g; u])
 //   3. dA = dO Wd_e             grouped GEMM over rows, weight [d, f] read as [K, N]
 //   4. swiglu_bwd   dH = [dA * u * silu'(g), dA * silu(g)]
 //   5. dXp = dH Wgu_e           grouped GEMM over rows, weight [2f, d] read as [K, N]
@@ -488,10 +489,11 @@ hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
   }
   const unsigned mt = tiles_bound(s);
   auto nt = [](int64_t n) { return (int)((n + kBT - 1) / kBT); };
-  // 2. H = Xg Wgu_e^T: rows, B K-contiguous ([2f][d]), gathered token rows
-  hipLaunchKernelGGL((bwd_gemm_kernel<true, true, true>), dim3(mt * nt(2 * f)), dim3(256), 0,
-                     st, xb, d, Wgu, d, 2 * f * d, H, 2 * f, (int64_t)0, 2 * f, d, offsets, G,
-                     sorted_slot, s.Tk(), s.k, s.T, 1, nt(2 * f));
+  // 2. H = Xg Wgu_e^T: the forward's tiled gate_up GEMM, pre-activation output
+  {
+    const hipError_t e = launch_gate_up_preact(s, x, sorted_slot, offsets, W_gate_up, H, st);
+    if (e != hipSuccess) return e;
+  }
   // 3. dA = dO Wd_e: rows, B N-contiguous (Wd_e [d][f] read as [K = d][N = f])
   hipLaunchKernelGGL((bwd_gemm_kernel<true, false, false>), dim3(mt * nt(f)), dim3(256), 0, st,
                      (const bf16_t*)dO, d, Wd, f, d * f, dA, f, (int64_t)0, f, d, offsets, G,

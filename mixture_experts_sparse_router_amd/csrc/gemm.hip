@@ -192,12 +192,17 @@ __device__ bool find_tile(const int32_t* offsets, int G, int BM, int ntN, int bi
   return s_res[0] >= 0;
 }
 
-template <bool GATED, int BM, int NST, int OCC, int NW, int SBK>
+// PRE (gate_up only): out is float [R, 2N] and receives the pre-activation
+// gate (columns < N) and up (columns N + c) values instead of the SwiGLU
+// (what the backward pass recomputes).
+template <bool GATED, int BM, int NST, int OCC, int NW, int SBK, bool PRE = false>
 __global__ __launch_bounds__(64 * NW, OCC) void tiled_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
-    bf16_t* __restrict__ out, int64_t K, int64_t N, int64_t T, int64_t Tk, int64_t k,
+    void* __restrict__ out_v, int64_t K, int64_t N, int64_t T, int64_t Tk, int64_t k,
     int G, int ntN) {
+  static_assert(GATED || !PRE, "pre-activation output of gate_up only");
+  bf16_t* out = (bf16_t*)out_v;
   constexpr int WN = NW / 2;            // wave grid 2 x WN
   constexpr int MI = BM / 64;           // 32-row blocks per wave (BM/2 rows)
   constexpr int NI = 8 / WN;            // 32-column blocks per wave (256/WN columns)
@@ -420,7 +425,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void tiled_gemm_kernel(
       const int r = wm * (BM / 2) + mi * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
       if (r >= rows) continue;
       bf16_t* orow = out + (row_begin + r) * N;
-      if constexpr (GATED) {
+      if constexpr (PRE) {
+        float* hrow = (float*)out_v + (row_begin + r) * 2 * N;
+#pragma unroll
+        for (int ni = 0; ni < NI / 2; ++ni) {
+          const int64_t c = n0 + (128 / WN) * wn + 32 * ni + lr;
+          if (c < N) {
+            hrow[c] = acc[mi][ni][e];
+            hrow[N + c] = acc[mi][ni + NI / 2][e];
+          }
+        }
+      } else if constexpr (GATED) {
 #pragma unroll
         for (int ni = 0; ni < NI / 2; ++ni) {
           const int64_t c = n0 + (128 / WN) * wn + 32 * ni + lr;
@@ -533,12 +548,13 @@ inline unsigned mtile_bound(const Shape& s, int BM) {
   return (unsigned)(R / BM + nonempty + 1);
 }
 
-template <bool GATED>
+template <bool GATED, bool PRE = false>
 hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot,
                        const int32_t* offsets, const void* W, void* out, int64_t K,
                        int64_t N, hipStream_t st) {
   const int G = (int)s.G();
-  if (s.T <= 64) return launch_stream_gemm(GATED, s, A, sorted_slot, offsets, W, out, K, N, st);
+  if (!PRE && s.T <= 64)
+    return launch_stream_gemm(GATED, s, A, sorted_slot, offsets, W, out, K, N, st);
   // Tile shapes, as measured fastest on the MI355X:
   //  - large groups (>= 512 rows on average): 256 x 256 tiles, 8 waves (two
   //    per SIMD, so one computes while the other waits), K tiles of 64
@@ -555,10 +571,10 @@ hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot
   const int64_t ncols = GATED ? TBN / 2 : TBN;
   const int ntN = (int)((N + ncols - 1) / ncols);
 #define MOE_TILED(bm, nst, occ, nw, sbk)                                                 \
-  hipLaunchKernelGGL((tiled_gemm_kernel<GATED, bm, nst, occ, nw, sbk>),                 \
+  hipLaunchKernelGGL((tiled_gemm_kernel<GATED, bm, nst, occ, nw, sbk, PRE>),            \
                      dim3(((mtile_bound(s, bm) * (unsigned)ntN) + 7u) & ~7u), dim3(64 * nw), \
-                     0, st, (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W,      \
-                     (bf16_t*)out, K, N, s.T, s.Tk(), s.k, G, ntN)
+                     0, st, (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W, out,  \
+                     K, N, s.T, s.Tk(), s.k, G, ntN)
   if (avg_rows >= 512) {
     MOE_TILED(256, 2, 1, 8, 64);
   } else if (routed_mean > 112 && routed_mean <= 168) {
@@ -593,6 +609,13 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* sorted_s
   if (s.dt == MOE_DT_BF16)
     return launch_bf16<true>(s, x, sorted_slot, offsets, W_gate_up, act, s.d, s.f, st);
   return launch_f32<true>(s, x, sorted_slot, offsets, W_gate_up, act, s.d, s.f, st);
+}
+
+hipError_t launch_gate_up_preact(const Shape& s, const void* x, const int32_t* sorted_slot,
+                                 const int32_t* offsets, const void* W_gate_up, float* H,
+                                 hipStream_t st) {
+  if (s.R() == 0) return hipSuccess;
+  return launch_bf16<true, true>(s, x, sorted_slot, offsets, W_gate_up, H, s.d, s.f, st);
 }
 
 hipError_t launch_down(const Shape& s, const void* act, const int32_t* offsets,

@@ -173,6 +173,11 @@ hipError_t launch_balance(const Shape& s, const float* logits, double* partial,
 hipError_t launch_gate_up(const Shape& s, const void* x, const int32_t* sorted_slot,
                           const int32_t* offsets, const void* W_gate_up, void* act,
                           hipStream_t st);
+// bf16: the gate_up GEMM's pre-activation values, H [R, 2f] fp32 (gate in
+// columns < f, up in f + c), for the backward pass.
+hipError_t launch_gate_up_preact(const Shape& s, const void* x, const int32_t* sorted_slot,
+                                 const int32_t* offsets, const void* W_gate_up, float* H,
+                                 hipStream_t st);
 // Decode-sized groups (T <= 64), bf16 only; gated selects the gate_up form.
 hipError_t launch_stream_gemm(bool gated, const Shape& s, const void* A,
                               const int32_t* sorted_slot, const int32_t* offsets, const void* W,
