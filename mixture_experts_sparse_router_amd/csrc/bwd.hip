@@ -49,8 +49,10 @@ static_assert(kBK * kMNRow == kBT * kLRow, "both tile forms fill the same LDS");
 struct BwdSmem {
   bf16_t a[2][kBT * kLRow];
   bf16_t b[2][kBT * kLRow];
-  int find[8];
 };
+// 40 KB: four workgroups per CU.  The group lookup's scratch borrows the
+// start of b[1], which is first written after the lookup's last barrier.
+static_assert(sizeof(BwdSmem) == 40960, "four workgroups fit one CU's LDS");
 
 __device__ __forceinline__ void store_kc(bf16_t* tile, int row, int kc, const u32x4& v) {
   *reinterpret_cast<u32x4*>(tile + row * kLRow + kc) = v;
@@ -124,7 +126,7 @@ __device__ bool find_group_tile(const int32_t* offsets, int G, int tile, int* g_
 //   the group's rows, M and N fixed); A and B contiguous along M and N;
 //   C [G][M][N].
 template <bool ROWS, bool B_KC, bool GATHER>
-__global__ __launch_bounds__(kBwdThreads) void bwd_gemm_kernel(
+__global__ __launch_bounds__(kBwdThreads, 4) void bwd_gemm_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
     int64_t b_stride, float* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K,
     const int32_t* __restrict__ offsets, int G, const int32_t* __restrict__ sorted_slot,
@@ -135,7 +137,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_gemm_kernel(
   int64_t row_begin, rows;  // ROWS: the tile's rows; else the group's rows (K)
   if constexpr (ROWS) {
     nt = (int)blockIdx.x % ntN;
-    if (!find_group_tile(offsets, G, (int)blockIdx.x / ntN, &g, &mt, sm.find)) return;
+    if (!find_group_tile(offsets, G, (int)blockIdx.x / ntN, &g, &mt,
+                         reinterpret_cast<int*>(sm.b[1])))
+      return;
     row_begin = offsets[g] + (int64_t)mt * kBT;
     const int64_t left = offsets[g + 1] - row_begin;
     rows = left < kBT ? left : kBT;
