@@ -190,6 +190,20 @@ __global__ __launch_bounds__(kBwdThreads, 4) void bwd_gemm_kernel(
   // select, so the loads stay unconditional
   const bf16_t* a_safe = ROWS ? A : A + row_begin * lda;
   const bf16_t* b_safe = ROWS ? Bg : B;
+  // !ROWS && GATHER: token rows of the B chunks of the next tile to load,
+  // looked up one tile ahead so that the row loads do not wait for them
+  int32_t tok[2] = {0, 0};
+  auto tokload = [&](int j) {
+    if constexpr (!ROWS && GATHER) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = tid + kBwdThreads * i;
+        const int64_t kr = (int64_t)j * kBK + c / 16;
+        const int64_t rr = row_begin + (kr < KK ? kr : 0);
+        tok[i] = (int32_t)row_token(rr, sorted_slot, Tk, k, T);
+      }
+    }
+  };
   u32x4 ra[2], rb[2];
   // global loads of K tile j into registers
   auto gload = [&](int j) {
@@ -220,8 +234,7 @@ __global__ __launch_bounds__(kBwdThreads, 4) void bwd_gemm_kernel(
         // B[src(r)][n], r the group row row_begin + kr
         const int64_t n = n0 + o8;
         const bool ok = kr < KK && n < N;
-        const int64_t rr = row_begin + (ok ? kr : 0);
-        const int64_t src = GATHER ? row_token(rr, sorted_slot, Tk, k, T) : rr;
+        const int64_t src = GATHER ? (int64_t)tok[i] : row_begin + (ok ? kr : 0);
         rb[i] = zero_unless(ok, ldg16(ok ? B + src * ldb + n : b_safe));
       }
     }
@@ -251,12 +264,17 @@ __global__ __launch_bounds__(kBwdThreads, 4) void bwd_gemm_kernel(
 
   const int nk = (int)((KK + kBK - 1) / kBK);
   if (nk > 0) {
+    tokload(0);
     gload(0);
+    tokload(1);
     lstore(0);
     __syncthreads();
     for (int j = 0; j < nk; ++j) {
       const int buf = j & 1;
-      if (j + 1 < nk) gload(j + 1);
+      if (j + 1 < nk) {
+        gload(j + 1);
+        tokload(j + 2);
+      }
 #pragma unroll
       for (int ks = 0; ks < kBK / 16; ++ks) {
         u32x4 fa[2], fb[2];
