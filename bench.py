@@ -5,7 +5,9 @@ grouped SwiGLU GEMMs -> combine) through libmoe's C ABI on one MI355X.
                     [--no-prefill]
 
 A step is one moe_layer_forward over one batch of seeded synthetic inputs
-already resident in HBM.  Default workload: the gpt-oss-20b-shaped decode
+already resident in HBM.  Before the W warmup steps, untimed steps run for
+--spinup-ms (default 200 ms) so that the GPU clocks have ramped up from idle
+(short runs otherwise time part of the ramp).  Default workload: the gpt-oss-20b-shaped decode
 layer (T=16, d=2880, f=2880, E=32, top-4, bf16).  Prints ONE JSON line:
 tokens/s of the whole layer (wall clock around exactly K steps, with the
 same interval also measured by HIP events on the stream the kernels run
@@ -44,6 +46,9 @@ def parse(argv=None):
     p.add_argument("--config", type=int, default=2,
                    help="workload 1..5 (2 = gpt-oss-20b-shaped decode, the headline)")
     p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--spinup-ms", type=float, default=200.0,
+                   help="untimed layer steps for this long before the warmup steps, so that "
+                        "the GPU clocks have left their idle state (reported as spinup_ms)")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-prefill", action="store_true",
@@ -425,6 +430,12 @@ def main(argv=None):
     torch.cuda.set_device(0)
     L = Layer(torch, moe, cfg, seed, args.rotate)
 
+    # clock spin-up (untimed), then the warmup steps
+    t_spin = time.perf_counter()
+    while (time.perf_counter() - t_spin) * 1e3 < args.spinup_ms:
+        for i in range(10):
+            L.step(i)
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         L.step(i)
     torch.cuda.synchronize()
@@ -452,6 +463,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spinup_ms": args.spinup_ms,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
