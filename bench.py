@@ -34,7 +34,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_sparse_router_amd", "csrc", "gemm_stream.hip")
+# the decode GEMM kernel's sources: stored counters hold while these are unchanged
+GEMM_SRCS = tuple(os.path.join(ROOT, "mixture_experts_sparse_router_amd", "csrc", f)
+                  for f in ("gemm_stream.hip", "decode_rows.h", "moe_common.h"))
 PREFILL_CONFIG = 3             # Mixtral-8x7B-shaped prefill
 
 
@@ -110,6 +112,15 @@ def time_calls(torch, fn, n):
     return e0.elapsed_time(e1) / n * 1e-3  # seconds
 
 
+def gemm_src_hash():
+    """sha256 (first 16 hex digits) of the decode GEMM kernel's sources."""
+    h = hashlib.sha256()
+    for path in GEMM_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def load_traffic(key):
     """HBM traffic of the dominant kernel from committed rocprofv3 --pmc
     counters, valid only while the kernel source is unchanged."""
@@ -120,8 +131,7 @@ def load_traffic(key):
     ent = data.get(key)
     if not ent:
         return None
-    src_hash = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
-    if ent.get("gemm_src_sha256_16") != src_hash:
+    if ent.get("gemm_src_sha256_16") != gemm_src_hash():
         return None
     return ent.get("bytes_per_launch")
 

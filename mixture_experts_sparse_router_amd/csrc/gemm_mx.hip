@@ -31,7 +31,7 @@
 // rows, U is the smallest of 2, 4, 6 whose round covers K (measured: at
 // K = 2880 one round of U = 6 beats two rounds of U = 4 by 20%, and U = 8
 // lowers occupancy); more rows leave fewer registers for steps.
-#include "moe_common.h"
+#include "decode_rows.h"
 
 namespace moe {
 namespace {
@@ -56,13 +56,19 @@ struct MxStep {
   bool ok;           // the block lies inside K (else used as zeros)
 };
 
-template <bool GATED, int MB, int U, int NW>
+// FUSED (gate_up only): the group's rows are found from the expert ids and
+// the workgroups of column tile 0 write the permutation (decode_rows.h), so
+// the layer needs no permutation launch.
+template <bool GATED, int MB, int U, int NW, bool FUSED = false>
 __global__ __launch_bounds__(64 * NW) void stream_mx_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const uint8_t* __restrict__ Wq,
     const uint8_t* __restrict__ Ws, bf16_t* __restrict__ out, int64_t K, int64_t N,
-    int64_t T, int64_t Tk, int64_t k, int G, int ntiles) {
+    int64_t T, int64_t Tk, int64_t k, int G, int ntiles, const int32_t* __restrict__ topk_idx,
+    int E, DecodePerm perm) {
+  static_assert(GATED || !FUSED, "fused row lookup in gate_up only");
   __shared__ f32x4 red[NW - 1][MB][2][64];  // partials of waves 1..NW-1
+  __shared__ int s_list[64];                // FUSED: the group's copies, ascending
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = (int)blockIdx.x / ntiles;
   if (g >= G) return;
@@ -71,8 +77,13 @@ __global__ __launch_bounds__(64 * NW) void stream_mx_kernel(
   const int64_t col = (int64_t)tile * 16 + j;
   const bool col_ok = col < N;
   const int64_t colc = col_ok ? col : N - 1;
-  const int64_t row_begin = offsets[g];
-  const int64_t rows = offsets[g + 1] - row_begin;
+  int64_t row_begin, rows;
+  if constexpr (FUSED) {
+    decode_group_rows(topk_idx, g, G, E, T, Tk, tile, wave, s_list, perm, &row_begin, &rows);
+  } else {
+    row_begin = offsets[g];
+    rows = offsets[g + 1] - row_begin;
+  }
   if (rows <= 0) return;  // empty expert: its weights are never read
 
   const int64_t wrow = (int64_t)g * (GATED ? 2 * N : N) + colc;  // gate (or down) row
@@ -88,7 +99,10 @@ __global__ __launch_bounds__(64 * NW) void stream_mx_kernel(
       int64_t r = m0 + mb * 16 + j;
       if (r >= rows) r = rows - 1;  // padding rows repeat a valid row
       const int64_t grow = row_begin + r;
-      Ap[mb] = A + (GATED ? row_token(grow, sorted_slot, Tk, k, T) : grow) * K;
+      if constexpr (FUSED)
+        Ap[mb] = A + decode_row_token(g, E, r, grow, Tk, T, k, s_list) * K;
+      else
+        Ap[mb] = A + (GATED ? row_token(grow, sorted_slot, Tk, k, T) : grow) * K;
     }
     f32x4 accg[MB], accu[MB];
 #pragma unroll
@@ -173,21 +187,23 @@ __global__ __launch_bounds__(64 * NW) void stream_mx_kernel(
   }
 }
 
-}  // namespace
 
-hipError_t launch_stream_mx(bool gated, const Shape& s, const void* A,
-                            const int32_t* sorted_slot, const int32_t* offsets,
-                            const uint8_t* Wq, const uint8_t* Ws, void* out, int64_t K,
-                            int64_t N, hipStream_t st) {
+// The launch of one decode MXFP4 GEMM.  fused: gate_up with the rows found
+// from topk_idx, writing the permutation into perm.
+template <bool FUSED>
+hipError_t launch_mx(bool gated, const Shape& s, const void* A, const int32_t* sorted_slot,
+                     const int32_t* offsets, const uint8_t* Wq, const uint8_t* Ws, void* out,
+                     int64_t K, int64_t N, const int32_t* topk_idx, const DecodePerm& perm,
+                     hipStream_t st) {
   if (s.R() == 0) return hipSuccess;
   const int G = (int)s.G();
   const int ntiles = (int)((N + 15) / 16);
   const unsigned grid = (unsigned)((int64_t)G * ntiles);
   const int MB = (int)((s.T + 15) / 16);
 #define MOE_MX(gt, mb, u)                                                                  \
-  hipLaunchKernelGGL((stream_mx_kernel<gt, mb, u, 4>), dim3(grid), dim3(256), 0, st,       \
-                     (const bf16_t*)A, sorted_slot, offsets, Wq, Ws, (bf16_t*)out, K, N, s.T, \
-                     s.Tk(), s.k, G, ntiles)
+  hipLaunchKernelGGL((stream_mx_kernel<gt, mb, u, 4, FUSED && gt>), dim3(grid), dim3(256), 0, \
+                     st, (const bf16_t*)A, sorted_slot, offsets, Wq, Ws, (bf16_t*)out, K, N,   \
+                     s.T, s.Tk(), s.k, G, ntiles, topk_idx, (int)s.E, perm)
   const int u1 = K <= 1024 ? 2 : K <= 2048 ? 4 : 6;  // steps per round, one row block
   if (gated) {
     if (MB == 1) {
@@ -216,6 +232,24 @@ hipError_t launch_stream_mx(bool gated, const Shape& s, const void* A,
   }
 #undef MOE_MX
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_stream_mx(bool gated, const Shape& s, const void* A,
+                            const int32_t* sorted_slot, const int32_t* offsets,
+                            const uint8_t* Wq, const uint8_t* Ws, void* out, int64_t K,
+                            int64_t N, hipStream_t st) {
+  return launch_mx<false>(gated, s, A, sorted_slot, offsets, Wq, Ws, out, K, N, nullptr,
+                          DecodePerm{}, st);
+}
+
+hipError_t launch_gate_up_mx_from_ids(const Shape& s, const void* x, const int32_t* topk_idx,
+                                      const uint8_t* Wq, const uint8_t* Ws, void* act,
+                                      int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                                      int32_t* slot_pos, hipStream_t st) {
+  return launch_mx<true>(true, s, x, nullptr, nullptr, Wq, Ws, act, s.d, s.f, topk_idx,
+                         DecodePerm{counts, offsets, sorted_slot, slot_pos}, st);
 }
 
 }  // namespace moe

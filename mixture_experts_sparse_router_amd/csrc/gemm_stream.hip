@@ -12,7 +12,7 @@
 // weight rows from HBM exactly once, straight into MFMA operand registers
 // (4 waves split K); the few token rows ride along.  Kept in a file of its
 // own so that it can be profiled and versioned apart from the prefill GEMM.
-#include "moe_common.h"
+#include "decode_rows.h"
 
 namespace moe {
 namespace {
@@ -60,39 +60,6 @@ __device__ __forceinline__ void stream_load_a(StreamRegs<GATED, MB, CH>& r,
   }
 }
 
-// Rows of one expert group in the fused form: the copies s (ascending) whose
-// expert id is g, found from the ids themselves.  n_slots = T*k <= 4096.
-struct GroupFromIds {
-  int row_begin, rows;
-};
-// One wave's view: ballots over the ids, 64 at a time.  `list` (LDS, >= 64
-// entries) receives the group's copies in ascending order (a group has at
-// most T <= 64 of them: a token picks an expert at most once).  Ids outside
-// [0, E) count for no group; their copies take the first rows (the layout
-// of the permutation step), so group g starts after them and after the
-// copies of the groups below g.
-__device__ __forceinline__ GroupFromIds group_from_ids(const int32_t* __restrict__ idx,
-                                                       int n_slots, int g, int E, int* list) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t below_lanes = (1ull << lane) - 1ull;
-  int before = 0, found = 0;
-  for (int s0 = 0; s0 < n_slots; s0 += 64) {
-    const int s = s0 + lane;
-    const bool in = s < n_slots;
-    const uint32_t v = in ? (uint32_t)idx[s] : 0u;  // unsigned: ids < 0 are huge
-    // copies placed before group g: ids below g, and ids outside [0, E)
-    const uint64_t lt = __ballot(in && (v < (uint32_t)g || v >= (uint32_t)E));
-    const uint64_t eq = __ballot(in && v == (uint32_t)g);
-    if ((eq >> lane) & 1ull) {
-      const int r = found + __popcll(eq & below_lanes);
-      if (r < 64) list[r] = s;
-    }
-    before += __popcll(lt);
-    found += __popcll(eq);
-  }
-  return GroupFromIds{before, found};
-}
-
 // FUSED (gate_up only): the group's rows are found from the expert ids
 // themselves instead of a permutation (decode batches: at most 64 tokens),
 // and the workgroups of column tile 0 write that permutation (counts,
@@ -129,48 +96,8 @@ __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
 
   int64_t row_begin, rows;
   if constexpr (FUSED) {
-    if (g < E) {
-      // every wave finds the group itself (its own writes to s_list are the
-      // ones it reads; the other waves write the same values).  A token
-      // picks an expert at most once, so a group has at most T <= 64 rows.
-      const GroupFromIds gi = group_from_ids(topk_idx, (int)Tk, g, E, s_list);
-      row_begin = gi.row_begin;
-      rows = gi.rows < 64 ? gi.rows : 64;
-    } else {
-      row_begin = Tk + (int64_t)(g - E) * T;  // shared expert g - E: every token
-      rows = T;
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (tile == 0 && wave == 0) {
-      if (lane == 0) {
-        p_counts[g] = (int32_t)rows;
-        p_offsets[g] = (int32_t)row_begin;
-        if (g == G - 1) p_offsets[G] = (int32_t)(Tk + (int64_t)(G - E) * T);
-      }
-      if (g < E) {
-        for (int r = lane; r < rows && r < 64; r += 64) {
-          const int sl = s_list[r];
-          p_sorted[row_begin + r] = sl;
-          p_slot_pos[sl] = (int32_t)(row_begin + r);
-        }
-      }
-    }
-    if (g == 0 && tile == 0 && wave == 1) {
-      // copies whose expert id is outside [0, E) take no expert: they are
-      // listed first, in slot order, and marked with slot_pos = -1
-      const uint64_t below_lanes = (1ull << lane) - 1ull;
-      int at = 0;
-      for (int s0 = 0; s0 < (int)Tk; s0 += 64) {
-        const int sl = s0 + lane;
-        const bool drop = sl < (int)Tk && (uint32_t)topk_idx[sl] >= (uint32_t)E;
-        const uint64_t m = __ballot(drop);
-        if (drop) {
-          p_sorted[at + __popcll(m & below_lanes)] = sl;
-          p_slot_pos[sl] = -1;
-        }
-        at += __popcll(m);
-      }
-    }
+    decode_group_rows(topk_idx, g, G, E, T, Tk, tile, wave, s_list,
+                      DecodePerm{p_counts, p_offsets, p_sorted, p_slot_pos}, &row_begin, &rows);
   } else {
     row_begin = offsets[g];
     rows = offsets[g + 1] - row_begin;
@@ -185,8 +112,7 @@ __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
       if (r >= rows) r = rows - 1;  // padding rows repeat a valid row
       const int64_t grow = row_begin + r;
       if constexpr (FUSED) {
-        Ap[mb] = A + (g < E ? (int64_t)((uint32_t)s_list[r < 64 ? r : 63] / (uint32_t)k)
-                            : (int64_t)((uint32_t)(grow - Tk) % (uint32_t)T)) * K;
+        Ap[mb] = A + decode_row_token(g, E, r, grow, Tk, T, k, s_list) * K;
       } else if constexpr (GATED) {
         Ap[mb] = A + row_token(grow, sorted_slot, Tk, k, T) * K;
       } else {

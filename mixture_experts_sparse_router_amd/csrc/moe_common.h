@@ -138,6 +138,12 @@ hipError_t launch_stream_mx(bool gated, const Shape& s, const void* A,
                             const int32_t* sorted_slot, const int32_t* offsets,
                             const uint8_t* Wq, const uint8_t* Ws, void* out, int64_t K,
                             int64_t N, hipStream_t st);
+// Decode-sized batches (T <= 64): the MXFP4 gate_up with the group rows found
+// from the expert ids, writing the permutation on the way.
+hipError_t launch_gate_up_mx_from_ids(const Shape& s, const void* x, const int32_t* topk_idx,
+                                      const uint8_t* Wq, const uint8_t* Ws, void* act,
+                                      int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                                      int32_t* slot_pos, hipStream_t st);
 // Backward pass (bf16): workspace layout and the launch sequence; the
 // forward's routing, permutation, act and expert_out are inputs.
 // Workspace (bytes, 256-aligned pieces): dO [R, d] bf16, H [R, 2f] fp32,

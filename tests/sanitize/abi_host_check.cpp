@@ -30,6 +30,9 @@ hipError_t launch_gate_up_from_ids(const Shape&, const void*, const int32_t*, co
 hipError_t launch_stream_mx(bool, const Shape&, const void*, const int32_t*, const int32_t*,
                             const uint8_t*, const uint8_t*, void*, int64_t, int64_t,
                             hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_gate_up_mx_from_ids(const Shape&, const void*, const int32_t*, const uint8_t*,
+                                      const uint8_t*, void*, int32_t*, int32_t*, int32_t*,
+                                      int32_t*, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_balance(const Shape&, const float*, double*, double*, double*, hipStream_t) {
   ++g_launches; return hipSuccess;
 }

@@ -52,18 +52,27 @@ def test_algorithmic_counts_by_hand():
 
 def test_traffic_only_while_the_kernel_is_unchanged(tmp_path, monkeypatch):
     b = _bench()
-    src_hash = hashlib.sha256(open(b.GEMM_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in b.GEMM_SRCS:
+        h.update(open(path, "rb").read())
+    src_hash = h.hexdigest()[:16]
+    assert b.gemm_src_hash() == src_hash
     tf = tmp_path / "traffic.json"
     tf.write_text(json.dumps({"w": {"bytes_per_launch": 123,
                                     "gemm_src_sha256_16": src_hash}}))
     monkeypatch.setattr(b, "TRAFFIC_FILE", str(tf))
     assert b.load_traffic("w") == 123
     assert b.load_traffic("no_such_workload") is None
-    # a changed kernel source invalidates the stored counters
-    src = tmp_path / "gemm_stream.hip"
-    src.write_bytes(open(b.GEMM_SRC, "rb").read() + b"\n// changed\n")
-    monkeypatch.setattr(b, "GEMM_SRC", str(src))
-    assert b.load_traffic("w") is None
+    # a change to any of the kernel's sources invalidates the stored counters
+    orig = tuple(b.GEMM_SRCS)
+    for i in range(len(orig)):
+        src = tmp_path / f"src{i}"
+        src.write_bytes(open(orig[i], "rb").read() + b"\n// changed\n")
+        monkeypatch.setattr(b, "GEMM_SRCS",
+                            tuple(str(src) if j == i else p for j, p in enumerate(orig)))
+        assert b.load_traffic("w") is None
+    monkeypatch.setattr(b, "GEMM_SRCS", orig)
+    assert b.load_traffic("w") == 123
     # the committed file parses and names the kernel it was taken on
     data = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
     for ent in data.values():

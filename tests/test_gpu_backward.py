@@ -61,6 +61,10 @@ BWD_CASES = [
     (70, 264, 136, 5, 2, 1, None, 2),
     (300, 128, 256, 12, 3, 0, 1.2, 3),
     (9, 64, 40, 8, 4, 2, 1.2, 4),
+    # the recomputed H through the forward's 192-row tiles (routed groups of
+    # 140 rows on average) and 256-row tiles (groups of 600 rows)
+    (140, 136, 200, 4, 4, 0, None, 5),
+    (600, 128, 136, 2, 2, 1, None, 6),
 ]
 
 

@@ -6,7 +6,8 @@ the layer on them; the HIP path reads the packed codes and scales itself.
   - dequantisation is checked bit for bit: a down GEMM whose activation rows
     are one-hot returns single weights, which bf16 holds exactly;
   - the GEMMs and the layer within the bf16 tolerance (2e-2 per row);
-  - routing bit-exact (it does not depend on the expert weights)."""
+  - routing and the permutation the layer's gate_up kernel writes
+    bit-exact (they do not depend on the expert weights)."""
 import numpy as np
 import pytest
 
@@ -139,5 +140,10 @@ def test_mxfp4_layer_decode(seed):
                                                  bias=inp["bias"])
     assert np.array_equal(host(views["topk_idx"]), idx_ref)
     assert np.max(np.abs(host(views["topk_w"]) - w_ref)) <= 1e-6
+    # the permutation, written by the gate_up kernel itself
+    for got, want, what in zip((views["counts"], views["offsets"], views["sorted_slot"],
+                                views["slot_pos"]), oracle.permute(idx_ref, cfg.E, cfg.S),
+                               ("counts", "offsets", "sorted_slot", "slot_pos")):
+        assert np.array_equal(host(got), want), what
     worst = assert_rows_close(ys[0], y_ref, "bf16", "mxfp4 layer")
     print(f"  worst row rel err {worst:.3e}", flush=True)
