@@ -167,10 +167,30 @@ def cpu_baseline(cfg, inp, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return dict(value=n_done / el, unit="tokens/s", cores=oracle.num_threads(),
-                kind="oracle", cpu_model=cpu_model(),
-                sample=f"{n_done} tokens of the same workload in {calls} oracle calls of "
-                       f"<= {per_call} tokens, {el:.1f} s wall")
+    out = dict(value=n_done / el, unit="tokens/s", cores=oracle.num_threads(),
+               kind="oracle", cpu_model=cpu_model(),
+               sample=f"{n_done} tokens of the same workload in {calls} oracle calls of "
+                      f"<= {per_call} tokens, {el:.1f} s wall")
+    if T <= 128:
+        # small workloads: the same sample on one core as well
+        threads = oracle.num_threads()
+        oracle.set_num_threads(1)
+        try:
+            n1, c1, t1 = 0, 0, time.perf_counter()
+            while True:
+                sel = toks[(c1 * per_call) % T:][:per_call]
+                oracle.layer_forward(inp["x"], inp["W_router"], inp["W_gate_up"], inp["W_down"],
+                                     cfg.k, S=cfg.S, bias=inp["bias"], tokens=sel)
+                n1 += len(sel)
+                c1 += 1
+                e1 = time.perf_counter() - t1
+                if e1 >= seconds / 3:
+                    break
+        finally:
+            oracle.set_num_threads(threads)
+        out["single_core"] = dict(value=n1 / e1, unit="tokens/s", cores=1,
+                                  sample=f"{n1} tokens in {c1} calls, {e1:.1f} s wall")
+    return out
 
 
 class Layer:
@@ -489,6 +509,7 @@ def main(argv=None):
         out["mxfp4"] = mx
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, L.inp, args.cpu_seconds)
+        out["cpu_baseline"]["gpu_over_cpu"] = round(tok_s / out["cpu_baseline"]["value"], 1)
     if not args.no_prefill and args.config != PREFILL_CONFIG:
         del L
         torch.cuda.empty_cache()

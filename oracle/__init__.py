@@ -50,6 +50,7 @@ _SIGNATURES = {
                              _f32p, _vp, _vp, _i64, _i64p, _i32p, _i64, _i32p,
                              _f64p, _f64p],
     "oracle_num_threads": [],
+    "oracle_set_num_threads": [_int],
 }
 
 
@@ -90,6 +91,9 @@ class Oracle:
 
     def num_threads(self) -> int:
         return self.L.oracle_num_threads()
+
+    def set_num_threads(self, n: int) -> None:
+        self.L.oracle_set_num_threads(int(n))
 
     def route(self, x, W_router, k, bias=None):
         """Return (logits[T,E] f64, idx[T,k] i32, w[T,k] f64)."""
@@ -300,6 +304,10 @@ def default() -> Oracle:
 
 def num_threads():
     return default().num_threads()
+
+
+def set_num_threads(n):
+    default().set_num_threads(n)
 
 
 def route(*a, **kw):

@@ -151,6 +151,8 @@ int oracle_layer_backward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
 
 /* Number of OpenMP threads the oracle uses (for reporting). */
 int oracle_num_threads(void);
+/* Threads of the following calls' parallel loops (n > 0), for timing. */
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
