@@ -615,6 +615,7 @@ hipError_t launch_gate_up_preact(const Shape& s, const void* x, const int32_t* s
                                  const int32_t* offsets, const void* W_gate_up, float* H,
                                  hipStream_t st) {
   if (s.R() == 0) return hipSuccess;
+  if (s.T <= 64) return launch_stream_gate_up_preact(s, x, sorted_slot, offsets, W_gate_up, H, st);
   return launch_bf16<true, true>(s, x, sorted_slot, offsets, W_gate_up, H, s.d, s.f, st);
 }
 

@@ -64,14 +64,19 @@ __device__ __forceinline__ void stream_load_a(StreamRegs<GATED, MB, CH>& r,
 // themselves instead of a permutation (decode batches: at most 64 tokens),
 // and the workgroups of column tile 0 write that permutation (counts,
 // offsets, sorted_slot, slot_pos) for the steps that follow.
-template <bool GATED, int MB, bool FUSED, int NW = 4, int U = 1, int CH = 4>
+// PRE (gate_up only): out is float [R, 2N] and receives the pre-activation
+// gate (column c) and up (column N + c) values instead of the SwiGLU (what
+// the backward pass recomputes).
+template <bool GATED, int MB, bool FUSED, int NW = 4, int U = 1, int CH = 4, bool PRE = false>
 __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
-    bf16_t* __restrict__ out, int64_t K, int64_t N, int64_t T, int64_t Tk, int64_t k,
+    void* __restrict__ out_v, int64_t K, int64_t N, int64_t T, int64_t Tk, int64_t k,
     int G, int ntiles, const int32_t* __restrict__ topk_idx, int E,
     int32_t* __restrict__ p_counts, int32_t* __restrict__ p_offsets,
     int32_t* __restrict__ p_sorted, int32_t* __restrict__ p_slot_pos) {
+  static_assert(GATED || !PRE, "pre-activation output of gate_up only");
+  bf16_t* out = (bf16_t*)out_v;
   __shared__ f32x4 red[NW - 1][MB][2][64];  // partials of waves 1..NW-1
   __shared__ int s_list[64];           // FUSED: the group's copies, ascending
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -186,8 +191,14 @@ __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
           for (int q = 0; q < 4; ++q) {
             const int64_t r = m0 + mb * 16 + kb * 4 + q;
             if (r < rows) {
-              const float v = GATED ? swiglu(accg[mb][q], accu[mb][q]) : accg[mb][q];
-              out[(row_begin + r) * N + col] = f32_to_bf16(v);
+              if constexpr (PRE) {
+                float* hrow = (float*)out_v + (row_begin + r) * 2 * N;
+                hrow[col] = accg[mb][q];
+                hrow[N + col] = accu[mb][q];
+              } else {
+                const float v = GATED ? swiglu(accg[mb][q], accu[mb][q]) : accg[mb][q];
+                out[(row_begin + r) * N + col] = f32_to_bf16(v);
+              }
             }
           }
         }
@@ -241,6 +252,28 @@ hipError_t launch_stream_gemm(bool gated, const Shape& s, const void* A,
     }
   }
 #undef MOE_STREAM
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_gate_up_preact(const Shape& s, const void* x, const int32_t* sorted_slot,
+                                        const int32_t* offsets, const void* W_gate_up, float* H,
+                                        hipStream_t st) {
+  const int G = (int)s.G();
+  const int ntiles = (int)((s.f + 15) / 16);
+  const unsigned grid = (unsigned)((int64_t)G * ntiles);
+  const int MB = (int)((s.T + 15) / 16);
+#define MOE_PRE(mb)                                                                        \
+  hipLaunchKernelGGL((stream_gemm_kernel<true, mb, false, 4, 1, 4, true>), dim3(grid),      \
+                     dim3(256), 0, st, (const bf16_t*)x, sorted_slot, offsets,              \
+                     (const bf16_t*)W_gate_up, H, s.d, s.f, s.T, s.Tk(), s.k, G, ntiles,     \
+                     nullptr, (int)s.E, nullptr, nullptr, nullptr, nullptr)
+  switch (MB) {
+    case 1: MOE_PRE(1); break;
+    case 2: MOE_PRE(2); break;
+    case 3: MOE_PRE(3); break;
+    default: MOE_PRE(4); break;
+  }
+#undef MOE_PRE
   return hipGetLastError();
 }
 

@@ -188,6 +188,11 @@ hipError_t launch_gate_up_preact(const Shape& s, const void* x, const int32_t* s
 hipError_t launch_stream_gemm(bool gated, const Shape& s, const void* A,
                               const int32_t* sorted_slot, const int32_t* offsets, const void* W,
                               void* out, int64_t K, int64_t N, hipStream_t st);
+// Decode-sized batches (T <= 64, bf16): the gate_up GEMM's pre-activation
+// values H [R, 2f] fp32 (as launch_gate_up_preact), streaming kernel.
+hipError_t launch_stream_gate_up_preact(const Shape& s, const void* x, const int32_t* sorted_slot,
+                                        const int32_t* offsets, const void* W_gate_up, float* H,
+                                        hipStream_t st);
 // Decode-sized batches (T <= 64, bf16): gate_up with the group rows found
 // from the expert ids, writing the permutation on the way.
 hipError_t launch_gate_up_from_ids(const Shape& s, const void* x, const int32_t* topk_idx,
