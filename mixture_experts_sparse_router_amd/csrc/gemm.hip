@@ -360,6 +360,27 @@ __global__ __launch_bounds__(64 * NW, OCC) void tiled_gemm_kernel(
 
   const int nk = (int)((K + SBK - 1) / SBK);
   auto next = [](int sg) { return sg + 1 == NST ? 0 : sg + 1; };
+  // A wave none of whose rows lies in the group (the last m-tile of a
+  // group, or a small group) only moves its share of the copies and keeps
+  // the barriers: the same copies, waits and barriers as below, without
+  // fragment reads or MFMAs, which leaves its SIMD to the waves that have
+  // rows.
+  if (__builtin_amdgcn_readfirstlane(wm * (BM / 2) >= rows ? 1 : 0)) {
+#pragma unroll
+    for (int t = 0; t < NST; ++t) issue(t, t);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 1) * (AI + BI)) : "memory");
+    __builtin_amdgcn_s_barrier();
+    int s_id = 0;
+    for (int j = 0; j < nk; ++j) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * (AI + BI)) : "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(s_id, j + NST);
+      s_id = next(s_id);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;  // no row of this wave to write
+  }
   u32x4 f0[NF], f1[NF];
   // tiles 0 .. NST-1 into stages 0 .. NST-1; wait for tile 0
 #pragma unroll
