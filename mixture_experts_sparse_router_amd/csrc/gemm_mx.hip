@@ -17,7 +17,8 @@
 // a bf16 number: 2 significant bits times a power of two).
 //
 // Same work split as the bf16 decode kernel (gemm_stream.hip): one
-// workgroup = 16 output columns of one expert for all of its rows, 4 waves
+// workgroup = 16 output columns (NT x 16 for the down GEMM of one row
+// block) of one expert for all of its rows, 4 waves
 // splitting K into 128-wide steps.  Lane (j = l%16, kb = l/16) loads, per K
 // step, the 32-element block [k0 + 32kb, +32) of weight row n0 + j: 16
 // contiguous bytes and its one scale byte (so 4 lanes cover 64 contiguous
@@ -48,18 +49,22 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t w, float scale) {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3))};
 }
 
-template <bool GATED, int MB>
+template <bool GATED, int MB, int NT>
 struct MxStep {
-  u32x4 qg, qu;      // 32 packed FP4 elements of the gate (and up) row
-  uint32_t sg, su;   // their E8M0 scale bytes
-  u32x4 a[MB][4];    // token rows' elements [k0 + 32kb + 8c, +8), c = 0..3
-  bool ok;           // the block lies inside K (else used as zeros)
+  u32x4 qg[NT], qu[NT];     // 32 packed FP4 elements of each tile's gate (and up) row
+  uint32_t sg[NT], su[NT];  // their E8M0 scale bytes
+  u32x4 a[MB][4];           // token rows' elements [k0 + 32kb + 8c, +8), c = 0..3
+  bool ok;                  // the block lies inside K (else used as zeros)
 };
 
 // FUSED (gate_up only): the group's rows are found from the expert ids and
-// the workgroups of column tile 0 write the permutation (decode_rows.h), so
-// the layer needs no permutation launch.
-template <bool GATED, int MB, int U, int NW, bool FUSED = false>
+// the workgroups that hold column tile 0 write the permutation
+// (decode_rows.h), so the layer needs no permutation launch.
+// NT column tiles of 16 per workgroup: each token-row chunk a lane loads
+// feeds NT weight tiles (the token rows are re-read from L2 by every
+// workgroup of the group; with 4-bit weights they would otherwise be two
+// thirds of the bytes a workgroup moves).
+template <bool GATED, int MB, int U, int NW, bool FUSED = false, int NT = 1>
 __global__ __launch_bounds__(64 * NW) void stream_mx_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const uint8_t* __restrict__ Wq,
@@ -67,30 +72,36 @@ __global__ __launch_bounds__(64 * NW) void stream_mx_kernel(
     int64_t T, int64_t Tk, int64_t k, int G, int ntiles, const int32_t* __restrict__ topk_idx,
     int E, DecodePerm perm) {
   static_assert(GATED || !FUSED, "fused row lookup in gate_up only");
-  __shared__ f32x4 red[NW - 1][MB][2][64];  // partials of waves 1..NW-1
-  __shared__ int s_list[64];                // FUSED: the group's copies, ascending
+  __shared__ f32x4 red[NW - 1][MB][NT][2][64];  // partials of waves 1..NW-1
+  __shared__ int s_list[64];                    // FUSED: the group's copies, ascending
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = (int)blockIdx.x / ntiles;
+  const int ngroups = (ntiles + NT - 1) / NT;  // workgroups per expert group
+  const int g = (int)blockIdx.x / ngroups;
   if (g >= G) return;
-  const int tile = (int)blockIdx.x % ntiles;
+  const int tg = (int)blockIdx.x % ngroups;  // this workgroup's tiles: NT*tg ..
   const int j = lane & 15, kb = lane >> 4;
-  const int64_t col = (int64_t)tile * 16 + j;
-  const bool col_ok = col < N;
-  const int64_t colc = col_ok ? col : N - 1;
+  int64_t col[NT];
+  bool col_ok[NT];
+  const uint8_t *qg[NT], *qu[NT], *sgp[NT], *sup[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    col[u] = (int64_t)(tg * NT + u) * 16 + j;
+    col_ok[u] = col[u] < N;
+    const int64_t colc = col_ok[u] ? col[u] : N - 1;
+    const int64_t wrow = (int64_t)g * (GATED ? 2 * N : N) + colc;  // gate (or down) row
+    qg[u] = Wq + wrow * (K / 2);
+    qu[u] = qg[u] + N * (K / 2);  // up row (GATED only)
+    sgp[u] = Ws + wrow * (K / 32);
+    sup[u] = sgp[u] + N * (K / 32);
+  }
   int64_t row_begin, rows;
   if constexpr (FUSED) {
-    decode_group_rows(topk_idx, g, G, E, T, Tk, tile, wave, s_list, perm, &row_begin, &rows);
+    decode_group_rows(topk_idx, g, G, E, T, Tk, tg, wave, s_list, perm, &row_begin, &rows);
   } else {
     row_begin = offsets[g];
     rows = offsets[g + 1] - row_begin;
   }
   if (rows <= 0) return;  // empty expert: its weights are never read
-
-  const int64_t wrow = (int64_t)g * (GATED ? 2 * N : N) + colc;  // gate (or down) row
-  const uint8_t* qg = Wq + wrow * (K / 2);
-  const uint8_t* qu = qg + N * (K / 2);  // up row (GATED only)
-  const uint8_t* sgp = Ws + wrow * (K / 32);
-  const uint8_t* sup = sgp + N * (K / 32);
 
   for (int64_t m0 = 0; m0 < rows; m0 += 16 * MB) {
     const bf16_t* Ap[MB];
@@ -104,48 +115,56 @@ __global__ __launch_bounds__(64 * NW) void stream_mx_kernel(
       else
         Ap[mb] = A + (GATED ? row_token(grow, sorted_slot, Tk, k, T) : grow) * K;
     }
-    f32x4 accg[MB], accu[MB];
+    f32x4 accg[MB][NT], accu[MB][NT];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      accg[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accu[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        accg[mb][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accu[mb][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     // wave w takes the K steps w, w+NW, ...; U of them per round
     for (int64_t k0 = (int64_t)wave * 128; k0 < K; k0 += 128 * NW * U) {
-      MxStep<GATED, MB> st[U];
+      MxStep<GATED, MB, NT> st[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t kk = k0 + 128 * NW * u + 32 * kb;  // the lane's 32-element block
-        st[u].ok = kk < K;
-        const int64_t ka = st[u].ok ? kk : 0;  // past K: block 0, zeroed at use
-        st[u].qg = ldg16(qg + ka / 2);
-        st[u].sg = sgp[ka / 32];
-        if constexpr (GATED) {
-          st[u].qu = ldg16(qu + ka / 2);
-          st[u].su = sup[ka / 32];
+      for (int v = 0; v < U; ++v) {
+        const int64_t kk = k0 + 128 * NW * v + 32 * kb;  // the lane's 32-element block
+        st[v].ok = kk < K;
+        const int64_t ka = st[v].ok ? kk : 0;  // past K: block 0, zeroed at use
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          st[v].qg[u] = ldg16(qg[u] + ka / 2);
+          st[v].sg[u] = sgp[u][ka / 32];
+          if constexpr (GATED) {
+            st[v].qu[u] = ldg16(qu[u] + ka / 2);
+            st[v].su[u] = sup[u][ka / 32];
+          }
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) st[u].a[mb][c] = ldg16(Ap[mb] + ka + 8 * c);
+          for (int c = 0; c < 4; ++c) st[v].a[mb][c] = ldg16(Ap[mb] + ka + 8 * c);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool ok = st[u].ok;
-        const float scg = __uint_as_float(st[u].sg << 23);
-        const float scu = __uint_as_float(st[u].su << 23);
-        const uint32_t wg[4] = {st[u].qg.x, st[u].qg.y, st[u].qg.z, st[u].qg.w};
-        const uint32_t wu[4] = {st[u].qu.x, st[u].qu.y, st[u].qu.z, st[u].qu.w};
+      for (int v = 0; v < U; ++v) {
+        const bool ok = st[v].ok;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 bg = zero_unless(ok, fp4x8_to_bf16(wg[c], scg));
-          u32x4 bu = bg;
-          if constexpr (GATED) bu = zero_unless(ok, fp4x8_to_bf16(wu[c], scu));
+        for (int u = 0; u < NT; ++u) {
+          const float scg = __uint_as_float(st[v].sg[u] << 23);
+          const float scu = __uint_as_float(st[v].su[u] << 23);
+          const uint32_t wg[4] = {st[v].qg[u].x, st[v].qg[u].y, st[v].qg[u].z, st[v].qg[u].w};
+          const uint32_t wu[4] = {st[v].qu[u].x, st[v].qu[u].y, st[v].qu[u].z, st[v].qu[u].w};
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const u32x4 a = zero_unless(ok, st[u].a[mb][c]);
-            accg[mb] = mfma16(a, bg, accg[mb]);
-            if constexpr (GATED) accu[mb] = mfma16(a, bu, accu[mb]);
+          for (int c = 0; c < 4; ++c) {
+            const u32x4 bg = zero_unless(ok, fp4x8_to_bf16(wg[c], scg));
+            u32x4 bu = bg;
+            if constexpr (GATED) bu = zero_unless(ok, fp4x8_to_bf16(wu[c], scu));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              const u32x4 a = zero_unless(ok, st[v].a[mb][c]);
+              accg[mb][u] = mfma16(a, bg, accg[mb][u]);
+              if constexpr (GATED) accu[mb][u] = mfma16(a, bu, accu[mb][u]);
+            }
           }
         }
       }
@@ -153,31 +172,36 @@ __global__ __launch_bounds__(64 * NW) void stream_mx_kernel(
     // add the NW K-split partials in wave order
     if (wave > 0) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        red[wave - 1][mb][0][lane] = accg[mb];
-        if constexpr (GATED) red[wave - 1][mb][1][lane] = accu[mb];
-      }
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          red[wave - 1][mb][u][0][lane] = accg[mb][u];
+          if constexpr (GATED) red[wave - 1][mb][u][1][lane] = accu[mb][u];
+        }
     }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-      for (int w = 0; w < NW - 1; ++w) {
+      for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          accg[mb] += red[w][mb][0][lane];
-          if constexpr (GATED) accu[mb] += red[w][mb][1][lane];
-        }
-      }
-      // lane holds D[4*kb + q][j], q = 0..3
-      if (col_ok) {
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int u = 0; u < NT; ++u) {
+            accg[mb][u] += red[w][mb][u][0][lane];
+            if constexpr (GATED) accu[mb][u] += red[w][mb][u][1][lane];
+          }
+      // lane holds D[4*kb + q][j], q = 0..3, of each tile
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        if (!col_ok[u]) continue;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int64_t r = m0 + mb * 16 + kb * 4 + q;
             if (r < rows) {
-              const float v = GATED ? swiglu(accg[mb][q], accu[mb][q]) : accg[mb][q];
-              out[(row_begin + r) * N + col] = f32_to_bf16(v);
+              const float v = GATED ? swiglu(accg[mb][u][q], accu[mb][u][q]) : accg[mb][u][q];
+              out[(row_begin + r) * N + col[u]] = f32_to_bf16(v);
             }
           }
         }
@@ -186,7 +210,6 @@ __global__ __launch_bounds__(64 * NW) void stream_mx_kernel(
     __syncthreads();  // red is reused by the next row pass
   }
 }
-
 
 // The launch of one decode MXFP4 GEMM.  fused: gate_up with the rows found
 // from topk_idx, writing the permutation into perm.
@@ -198,12 +221,13 @@ hipError_t launch_mx(bool gated, const Shape& s, const void* A, const int32_t* s
   if (s.R() == 0) return hipSuccess;
   const int G = (int)s.G();
   const int ntiles = (int)((N + 15) / 16);
-  const unsigned grid = (unsigned)((int64_t)G * ntiles);
   const int MB = (int)((s.T + 15) / 16);
-#define MOE_MX(gt, mb, u)                                                                  \
-  hipLaunchKernelGGL((stream_mx_kernel<gt, mb, u, 4, FUSED && gt>), dim3(grid), dim3(256), 0, \
+#define MOE_MX_NT(gt, mb, u, nt)                                                            \
+  hipLaunchKernelGGL((stream_mx_kernel<gt, mb, u, 4, FUSED && gt, nt>),                     \
+                     dim3((unsigned)((int64_t)G * ((ntiles + nt - 1) / nt))), dim3(256), 0,  \
                      st, (const bf16_t*)A, sorted_slot, offsets, Wq, Ws, (bf16_t*)out, K, N,   \
                      s.T, s.Tk(), s.k, G, ntiles, topk_idx, (int)s.E, perm)
+#define MOE_MX(gt, mb, u) MOE_MX_NT(gt, mb, u, 1)
   const int u1 = K <= 1024 ? 2 : K <= 2048 ? 4 : 6;  // steps per round, one row block
   if (gated) {
     if (MB == 1) {
@@ -219,9 +243,10 @@ hipError_t launch_mx(bool gated, const Shape& s, const void* A, const int32_t* s
     }
   } else {
     if (MB == 1) {
-      if (u1 == 2) MOE_MX(false, 1, 2);
-      else if (u1 == 4) MOE_MX(false, 1, 4);
-      else MOE_MX(false, 1, 6);
+      // two column tiles per workgroup, two steps per round (measured at
+      // d = f = 2880: 33.4 -> 28.2 us; the gate_up, with twice the weight
+      // bytes per tile, is fastest with one tile and one round covering K)
+      MOE_MX_NT(false, 1, 2, 2);
     } else if (MB == 2) {
       MOE_MX(false, 2, 2);
     } else if (MB == 3) {
@@ -231,6 +256,7 @@ hipError_t launch_mx(bool gated, const Shape& s, const void* A, const int32_t* s
     }
   }
 #undef MOE_MX
+#undef MOE_MX_NT
   return hipGetLastError();
 }
 
