@@ -25,30 +25,35 @@ namespace {
 // loads, for chunk c of a K step, elements [k0 + 32c + 8kb, +8) of weight
 // row n0+j and of token row j: 4 lanes cover 64 contiguous bytes of a row
 // per load.
-template <bool GATED, int MB, int CH>
+template <bool GATED, int MB, int CH, int NT>
 struct StreamRegs {
-  u32x4 bg[CH], bu[CH], a[MB][CH];
+  u32x4 bg[NT][CH], bu[NT][CH], a[MB][CH];
   bool ok[CH];  // chunk c lies inside K (else its registers are zeroed at use)
 };
 
-// Loads of one K step: the weight rows' chunks and the token rows' chunks.
-// Chunks past K read a valid address (offset 0) and are zeroed by a select
-// when they are used, so the loads stay branch-free.
-template <bool GATED, int MB, int CH>
-__device__ __forceinline__ void stream_load_w(StreamRegs<GATED, MB, CH>& r, const bf16_t* Bg,
-                                              const bf16_t* Bu, int64_t k0, int kb, int64_t K) {
+// Loads of one K step: the weight rows' chunks (of each of the NT column
+// tiles) and the token rows' chunks.  Chunks past K read a valid address
+// (offset 0) and are zeroed by a select when they are used, so the loads
+// stay branch-free.
+template <bool GATED, int MB, int CH, int NT>
+__device__ __forceinline__ void stream_load_w(StreamRegs<GATED, MB, CH, NT>& r,
+                                              const bf16_t* const* Bg, const bf16_t* const* Bu,
+                                              int64_t k0, int kb, int64_t K) {
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t kk = k0 + 32 * c + 8 * kb;
     const bool ok = kk < K;
     const int64_t ka = ok ? kk : 0;
     r.ok[c] = ok;
-    r.bg[c] = ldg16(Bg + ka);
-    if constexpr (GATED) r.bu[c] = ldg16(Bu + ka);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      r.bg[u][c] = ldg16(Bg[u] + ka);
+      if constexpr (GATED) r.bu[u][c] = ldg16(Bu[u] + ka);
+    }
   }
 }
-template <bool GATED, int MB, int CH>
-__device__ __forceinline__ void stream_load_a(StreamRegs<GATED, MB, CH>& r,
+template <bool GATED, int MB, int CH, int NT>
+__device__ __forceinline__ void stream_load_a(StreamRegs<GATED, MB, CH, NT>& r,
                                               const bf16_t* const* Ap, int64_t k0, int kb,
                                               int64_t K) {
 #pragma unroll
@@ -62,12 +67,14 @@ __device__ __forceinline__ void stream_load_a(StreamRegs<GATED, MB, CH>& r,
 
 // FUSED (gate_up only): the group's rows are found from the expert ids
 // themselves instead of a permutation (decode batches: at most 64 tokens),
-// and the workgroups of column tile 0 write that permutation (counts,
-// offsets, sorted_slot, slot_pos) for the steps that follow.
+// and the workgroups that hold column tile 0 write that permutation
+// (counts, offsets, sorted_slot, slot_pos) for the steps that follow.
 // PRE (gate_up only): out is float [R, 2N] and receives the pre-activation
 // gate (column c) and up (column N + c) values instead of the SwiGLU (what
 // the backward pass recomputes).
-template <bool GATED, int MB, bool FUSED, int NW = 4, int U = 1, int CH = 4, bool PRE = false>
+// NT column tiles of 16 per workgroup share each token-row load.
+template <bool GATED, int MB, bool FUSED, int NW = 4, int U = 1, int CH = 4, bool PRE = false,
+          int NT = 1>
 __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
@@ -77,31 +84,38 @@ __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
     int32_t* __restrict__ p_sorted, int32_t* __restrict__ p_slot_pos) {
   static_assert(GATED || !PRE, "pre-activation output of gate_up only");
   bf16_t* out = (bf16_t*)out_v;
-  __shared__ f32x4 red[NW - 1][MB][2][64];  // partials of waves 1..NW-1
-  __shared__ int s_list[64];           // FUSED: the group's copies, ascending
+  __shared__ f32x4 red[NW - 1][MB][NT][2][64];  // partials of waves 1..NW-1
+  __shared__ int s_list[64];                    // FUSED: the group's copies, ascending
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = (int)blockIdx.x / ntiles;
+  const int ngroups = (ntiles + NT - 1) / NT;  // workgroups per expert group
+  const int g = (int)blockIdx.x / ngroups;
   if (g >= G) return;
-  const int tile = (int)blockIdx.x % ntiles;
+  const int tg = (int)blockIdx.x % ngroups;  // this workgroup's tiles: NT*tg ..
   const int j = lane & 15, kb = lane >> 4;
-  const int64_t n0 = (int64_t)tile * 16;
-  const int64_t col = n0 + j;
-  const bool col_ok = col < N;
-  const int64_t colc = col_ok ? col : N - 1;
-  const bf16_t* Bg = W + ((int64_t)g * (GATED ? 2 * N : N) + colc) * K;
-  const bf16_t* Bu = Bg + N * K;  // up rows (GATED only)
+  int64_t col[NT];
+  bool col_ok[NT];
+  const bf16_t *Bg[NT], *Bu[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    col[u] = (int64_t)(tg * NT + u) * 16 + j;
+    col_ok[u] = col[u] < N;
+    const int64_t colc = col_ok[u] ? col[u] : N - 1;
+    Bg[u] = W + ((int64_t)g * (GATED ? 2 * N : N) + colc) * K;
+    Bu[u] = Bg[u] + N * K;  // up rows (GATED only)
+  }
   // gate_up: the weights of this wave's first K step do not depend on the
   // group's rows, so their loads are issued before the group is looked up
   // (measured faster; an empty group drops them unused: at most one K step
   // per wave is read of an expert without rows)
   constexpr int KW = 32 * CH;  // K elements per step
-  StreamRegs<GATED, MB, CH> first;
+  StreamRegs<GATED, MB, CH, NT> first;
   bool have_first = GATED;
-  if constexpr (GATED) stream_load_w<GATED, MB, CH>(first, Bg, Bu, (int64_t)wave * KW, kb, K);
+  if constexpr (GATED)
+    stream_load_w<GATED, MB, CH, NT>(first, Bg, Bu, (int64_t)wave * KW, kb, K);
 
   int64_t row_begin, rows;
   if constexpr (FUSED) {
-    decode_group_rows(topk_idx, g, G, E, T, Tk, tile, wave, s_list,
+    decode_group_rows(topk_idx, g, G, E, T, Tk, tg, wave, s_list,
                       DecodePerm{p_counts, p_offsets, p_sorted, p_slot_pos}, &row_begin, &rows);
   } else {
     row_begin = offsets[g];
@@ -124,43 +138,48 @@ __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
         Ap[mb] = A + grow * K;
       }
     }
-    f32x4 accg[MB], accu[MB];
+    f32x4 accg[MB][NT], accu[MB][NT];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      accg[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accu[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        accg[mb][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accu[mb][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     // U K steps per round (one by default: the other resident waves hide
     // the latency; more steps per round cost occupancy)
     for (int64_t k0 = (int64_t)wave * KW; k0 < K; k0 += (int64_t)KW * NW * U) {
       // U steps (k0, k0 + KW*NW, ...) loaded before any is used
-      StreamRegs<GATED, MB, CH> r[U];
+      StreamRegs<GATED, MB, CH, NT> r[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t ku = k0 + (int64_t)KW * NW * u;
+      for (int v = 0; v < U; ++v) {
+        const int64_t ku = k0 + (int64_t)KW * NW * v;
         if constexpr (GATED) {
-          if (u == 0 && have_first) {
+          if (v == 0 && have_first) {
             r[0] = first;
             have_first = false;
           } else {
-            stream_load_w<GATED, MB, CH>(r[u], Bg, Bu, ku, kb, K);
+            stream_load_w<GATED, MB, CH, NT>(r[v], Bg, Bu, ku, kb, K);
           }
         } else {
-          stream_load_w<GATED, MB, CH>(r[u], Bg, Bu, ku, kb, K);
+          stream_load_w<GATED, MB, CH, NT>(r[v], Bg, Bu, ku, kb, K);
         }
-        stream_load_a<GATED, MB, CH>(r[u], Ap, ku, kb, K);
+        stream_load_a<GATED, MB, CH, NT>(r[v], Ap, ku, kb, K);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int v = 0; v < U; ++v) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-          const u32x4 bg = zero_unless(r[u].ok[c], r[u].bg[c]);
-          const u32x4 bu = GATED ? zero_unless(r[u].ok[c], r[u].bu[c]) : bg;
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const u32x4 a = zero_unless(r[u].ok[c], r[u].a[mb][c]);
-            accg[mb] = mfma16(a, bg, accg[mb]);
-            if constexpr (GATED) accu[mb] = mfma16(a, bu, accu[mb]);
+          for (int u = 0; u < NT; ++u) {
+            const u32x4 bg = zero_unless(r[v].ok[c], r[v].bg[u][c]);
+            const u32x4 bu = GATED ? zero_unless(r[v].ok[c], r[v].bu[u][c]) : bg;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              const u32x4 a = zero_unless(r[v].ok[c], r[v].a[mb][c]);
+              accg[mb][u] = mfma16(a, bg, accg[mb][u]);
+              if constexpr (GATED) accu[mb][u] = mfma16(a, bu, accu[mb][u]);
+            }
           }
         }
       }
@@ -168,23 +187,28 @@ __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
     // add the NW K-split partials in wave order
     if (wave > 0) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        red[wave - 1][mb][0][lane] = accg[mb];
-        if constexpr (GATED) red[wave - 1][mb][1][lane] = accu[mb];
-      }
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          red[wave - 1][mb][u][0][lane] = accg[mb][u];
+          if constexpr (GATED) red[wave - 1][mb][u][1][lane] = accu[mb][u];
+        }
     }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-      for (int w = 0; w < NW - 1; ++w) {
+      for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          accg[mb] += red[w][mb][0][lane];
-          if constexpr (GATED) accu[mb] += red[w][mb][1][lane];
-        }
-      }
-      // lane holds D[4*kb + q][j], q = 0..3
-      if (col_ok) {
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int u = 0; u < NT; ++u) {
+            accg[mb][u] += red[w][mb][u][0][lane];
+            if constexpr (GATED) accu[mb][u] += red[w][mb][u][1][lane];
+          }
+      // lane holds D[4*kb + q][j], q = 0..3, of each tile
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        if (!col_ok[u]) continue;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -193,11 +217,11 @@ __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(
             if (r < rows) {
               if constexpr (PRE) {
                 float* hrow = (float*)out_v + (row_begin + r) * 2 * N;
-                hrow[col] = accg[mb][q];
-                hrow[N + col] = accu[mb][q];
+                hrow[col[u]] = accg[mb][u][q];
+                hrow[N + col[u]] = accu[mb][u][q];
               } else {
-                const float v = GATED ? swiglu(accg[mb][q], accu[mb][q]) : accg[mb][q];
-                out[(row_begin + r) * N + col] = f32_to_bf16(v);
+                const float v = GATED ? swiglu(accg[mb][u][q], accu[mb][u][q]) : accg[mb][u][q];
+                out[(row_begin + r) * N + col[u]] = f32_to_bf16(v);
               }
             }
           }
