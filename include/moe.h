@@ -331,8 +331,11 @@ int moe_layer_forward_mxfp4(const moe_shape* s, const void* x,
  *   dw           [T, k] float32 out (dL/d topk_w), or NULL
  *   workspace    moe_backward_workspace_size(s) bytes, 256-byte aligned
  * Intermediates dO and dH are bf16 (GEMM operands), everything else fp32;
- * sums in a fixed order (repeated calls are bitwise identical).  Copies
- * dropped by a capacity (slot_pos < 0) contribute nothing. */
+ * sums in a fixed order (repeated calls are bitwise identical).  A copy
+ * dropped by a capacity (slot_pos < 0) adds no expert gradient and gets
+ * dw = 0; its weight still enters the softmax over the k selected logits
+ * (the kept weights are not renormalised), so its logit's dl is
+ * -w_tj sum_i w_ti dw_ti and reaches dx, dW_router and db. */
 size_t moe_backward_workspace_size(const moe_shape* s);
 
 int moe_layer_backward(const moe_shape* s, const void* x, const void* W_router,

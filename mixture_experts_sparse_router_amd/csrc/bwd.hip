@@ -15,10 +15,14 @@
 //   5. dXp = dH Wgu_e           grouped GEMM over rows, weight [2f, d] read as [K, N]
 //   6. dWd_e = dO^T A           grouped GEMM over the group's rows as K
 //   7. dWgu_e = dH^T Xg         same, token rows gathered
-//   8. router_wgrad dWr_e = sum_r dl_r x_t(r), db_e = sum_r dl_r (row chunks,
-//                   then a fixed-order sum of the chunks)
+//   8. router_wgrad dWr_e = sum_r dl_r x_t(r), db_e = sum_r dl_r over e's group
+//                   and e's copies dropped by a capacity (row chunks, then a
+//                   fixed-order sum of the chunks)
 //   9. dx_gather    dx_t = sum_j dXp[slot of (t, j)] + shared rows
 //                   + sum_j dl_tj Wr_{e_tj}
+// With a capacity, a dropped copy (slot_pos < 0) has no row: no expert
+// gradient and dw = 0, but its logit keeps dl (the kept weights are not
+// renormalised, so every selected logit moves them).
 // Gradients come out in fp32; the intermediates dO and dH are rounded to
 // bf16 (the GEMM operands), H and dA stay fp32.  Every sum has a fixed
 // order (no atomics), so repeated calls are bitwise identical.
@@ -360,18 +364,18 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 }
 
 // 1b. Softmax over the k selected logits: dl_j = w_j (dw_j - sum_i w_i dw_i),
-// one thread per token (dropped copies: dl = 0).
+// one thread per token.  A copy dropped by a capacity has dw_j = 0 but its
+// weight still enters the normalisation of the kept ones (they are not
+// renormalised), so its dl_j = -w_j sum_i w_i dw_i.
 __global__ __launch_bounds__(256) void router_dl_kernel(const float* __restrict__ dw,
                                                         const float* __restrict__ topk_w,
-                                                        const int32_t* __restrict__ slot_pos,
                                                         float* __restrict__ dl, int64_t T,
                                                         int64_t k) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
   float sw = 0.f;
   for (int64_t j = 0; j < k; ++j) sw += topk_w[t * k + j] * dw[t * k + j];
-  for (int64_t j = 0; j < k; ++j)
-    dl[t * k + j] = slot_pos[t * k + j] >= 0 ? topk_w[t * k + j] * (dw[t * k + j] - sw) : 0.f;
+  for (int64_t j = 0; j < k; ++j) dl[t * k + j] = topk_w[t * k + j] * (dw[t * k + j] - sw);
 }
 
 // 4. dH[r, n] = dA * u * silu'(g), dH[r, f + n] = dA * silu(g), from H = [g; u].
@@ -389,26 +393,57 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
   dH[r * 2 * f + f + n] = f32_to_bf16(da * (g * s));
 }
 
+// First dropped row r in [0, D) whose expert key is >= e.  The dropped rows
+// hold first the copies with ids outside [0, E) (key -1), then the copies
+// over capacity by expert id, so the key never decreases over [0, D).
+__device__ __forceinline__ int64_t dropped_lower_bound(const int32_t* __restrict__ topk_idx,
+                                                       const int32_t* __restrict__ sorted_slot,
+                                                       int64_t D, int e, int E) {
+  int64_t lo = 0, hi = D;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    const int32_t id = topk_idx[sorted_slot[mid]];
+    const int key = (id >= 0 && id < E) ? id : -1;
+    if (key < e) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // 8. Router weight and bias gradients: chunk c of expert e's rows adds
 // dl(r) x[t(r)] for its rows in order (8 rows' loads issued together); then
-// the chunks are added in order.
+// the chunks are added in order.  Expert e's rows are its group, then the
+// copies of e that a capacity dropped (rows in [0, offsets[0]); their dl is
+// not zero, see 1b).
 __global__ __launch_bounds__(256) void router_wgrad_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ dl,
-    const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ offsets,
-    float* __restrict__ part, float* __restrict__ part_b, int64_t d, int64_t k, int E) {
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ sorted_slot,
+    const int32_t* __restrict__ offsets, float* __restrict__ part, float* __restrict__ part_b,
+    int64_t d, int64_t k, int E) {
   const int e = blockIdx.x, c = blockIdx.z;
   const int64_t col = (int64_t)blockIdx.y * 256 + threadIdx.x;
   const int64_t colc = col < d ? col : d - 1;
-  const int64_t r0 = offsets[e], n = offsets[e + 1] - r0;
+  const int64_t r0 = offsets[e], nk = offsets[e + 1] - r0;
+  const int64_t D = offsets[0];
+  int64_t dlo = 0, nd = 0;
+  if (D > 0) {
+    dlo = dropped_lower_bound(topk_idx, sorted_slot, D, e, E);
+    nd = dropped_lower_bound(topk_idx, sorted_slot, D, e + 1, E) - dlo;
+  }
+  const int64_t n = nk + nd;
   const int64_t per = (n + kRouterChunks - 1) / kRouterChunks;
-  const int64_t lo = r0 + (int64_t)c * per;
-  const int64_t hi = (lo + per < r0 + n) ? lo + per : r0 + n;
+  const int64_t lo = (int64_t)c * per;
+  const int64_t hi = (lo + per < n) ? lo + per : n;
   float acc = 0.f, accb = 0.f;
   for (int64_t rb = lo; rb < hi; rb += 8) {
     int32_t slot[8];
     float v[8], xv[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) slot[u] = rb + u < hi ? sorted_slot[rb + u] : 0;
+    for (int u = 0; u < 8; ++u) {
+      const int64_t vi = rb + u;
+      const int64_t row = vi < nk ? r0 + vi : dlo + (vi - nk);
+      slot[u] = vi < hi ? sorted_slot[row] : 0;
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       v[u] = rb + u < hi ? dl[slot[u]] : 0.f;
@@ -507,7 +542,7 @@ hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
                        (const bf16_t*)dy, (const bf16_t*)expert_out, slot_pos, topk_w, dO, dwp,
                        s.T, d, s.k, (int)s.S);
     hipLaunchKernelGGL(router_dl_kernel, dim3((unsigned)((s.T + 255) / 256)), dim3(256), 0, st,
-                       (const float*)dwp, topk_w, slot_pos, dl, s.T, s.k);
+                       (const float*)dwp, topk_w, dl, s.T, s.k);
   }
   const unsigned mt = tiles_bound(s);
   auto nt = [](int64_t n) { return (int)((n + kBT - 1) / kBT); };
@@ -541,8 +576,8 @@ hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
   // 8
   hipLaunchKernelGGL(router_wgrad_kernel, dim3((unsigned)s.E, (unsigned)((d + 255) / 256),
                                                kRouterChunks),
-                     dim3(256), 0, st, xb, (const float*)dl, sorted_slot, offsets, part, part_b,
-                     d, s.k, (int)s.E);
+                     dim3(256), 0, st, xb, (const float*)dl, topk_idx, sorted_slot, offsets, part,
+                     part_b, d, s.k, (int)s.E);
   hipLaunchKernelGGL(router_wgrad_sum_kernel, dim3((unsigned)((s.E * d + 255) / 256)), dim3(256),
                      0, st, (const float*)part, (const float*)part_b, dWr, db, d, (int)s.E);
   // 9

@@ -41,8 +41,8 @@ _SIGNATURES = {
     "oracle_balance": [_i64, _i64, _i64, _int, _vp, _vp, _f32p, _f64p, _f64p, _f64p],
     "oracle_dequant_mxfp4": [_i64, _i64, _vp, _vp, _f64p],
     "oracle_layer_backward": [_i64, _i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _f32p, _vp,
-                              _vp, _vp, _i64, _i64p, _f64p, _i64, _i32p, _f64p, _f64p,
-                              _f64p, _f64p, _f64p],
+                              _vp, _vp, _i64, _i64, _i64p, _f64p, _i64, _i32p, _f64p,
+                              _f64p, _f64p, _f64p, _f64p],
     "oracle_gate_up_rows": [_i64, _i64p, _i32p, _i64, _i64, _int, _vp, _vp, _f64p],
     "oracle_down_rows": [_i64, _i32p, _i64, _i64, _int, _vp, _vp, _f64p],
     "oracle_combine": [_i64, _i64, _i64, _i64, _int, _vp, _i32p, _f64p, _f64p],
@@ -132,11 +132,13 @@ class Oracle:
         return counts, offsets, sorted_slot, slot_pos
 
     def layer_backward(self, x, W_router, W_gate_up, W_down, dy, k, S=0, bias=None,
-                       tokens=None, experts=(), router=True):
+                       tokens=None, experts=(), router=True, capacity=None):
         """Gradients of sum(y * dy).  Returns a dict: dx [n_tok, d] for the
         listed tokens (all when tokens is None), dW_gate_up [n, 2f, d] and
         dW_down [n, d, f] for the listed experts, and with router=True dW_router
-        [E, d], db [E], dw [T, k]; all fp64."""
+        [E, d], db [E], dw [T, k]; all fp64.  capacity: the forward with that
+        expert capacity (layer_forward's); dropped copies get no gradient
+        through their expert and dw 0."""
         x, W_router, W_gate_up, W_down, dy = (_c(a) for a in (x, W_router, W_gate_up,
                                                                W_down, dy))
         dt = _dt(x)
@@ -160,7 +162,8 @@ class Oracle:
                        dw=np.empty((T, k), np.float64))
         rc = self.L.oracle_layer_backward(
             T, d, f, E, k, S, dt, _p(x), _p(W_router), _p(b, _f32p), _p(W_gate_up),
-            _p(W_down), _p(dy), n_tok, _p(tl, _i64p), _p(out["dx"], _f64p), n_exp,
+            _p(W_down), _p(dy), -1 if capacity is None else int(capacity), n_tok,
+            _p(tl, _i64p), _p(out["dx"], _f64p), n_exp,
             _p(el, _i32p) if n_exp else None,
             _p(out["dW_gate_up"], _f64p) if n_exp else None,
             _p(out["dW_down"], _f64p) if n_exp else None,

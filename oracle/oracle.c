@@ -434,6 +434,32 @@ int oracle_combine(int64_t T, int64_t k, int64_t S, int64_t d, int dt,
   return 0;
 }
 
+/* With an expert capacity, whether a copy is kept depends on the copies of
+ * every earlier token: route all tokens first, then walk the copies in slot
+ * order, each expert keeping its first `capacity` (the reading of
+ * oracle_permute_capacity).  *keep_out: [T*k], 1 = kept; the caller frees. */
+static int capacity_keep(int64_t T, int64_t d, int64_t E, int64_t k, int dt, const void* x,
+                         const void* W_router, const float* bias, int64_t capacity,
+                         uint8_t** keep_out) {
+  int32_t* idx_all = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
+  double* w_all = (double*)malloc(sizeof(double) * (size_t)(T * k));
+  int64_t* seen = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+  uint8_t* keep = (uint8_t*)malloc((size_t)(T * k));
+  int rc = (idx_all && w_all && seen && keep) ? 0 : -2;
+  if (rc == 0) rc = oracle_route(T, d, E, k, dt, x, W_router, bias, NULL, idx_all, w_all);
+  if (rc == 0)
+    for (int64_t s = 0; s < T * k; ++s) keep[s] = seen[idx_all[s]]++ < capacity;
+  free(idx_all);
+  free(w_all);
+  free(seen);
+  if (rc != 0) {
+    free(keep);
+    keep = NULL;
+  }
+  *keep_out = keep;
+  return rc;
+}
+
 /* ------------------------------------------------------------ whole layer */
 
 int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
@@ -457,28 +483,10 @@ int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
     for (int64_t q = 0; q < n_tok * k; ++q)
       if (forced_idx[q] < 0 || forced_idx[q] >= E) return -1;
 
-  /* with an expert capacity, whether a copy is kept depends on the copies
-   * of every earlier token: route all tokens first, then walk the copies in
-   * slot order, each expert keeping its first `capacity` (the reading of
-   * oracle_permute_capacity) */
   uint8_t* keep = NULL;
   if (capacity >= 0 && T > 0) {
-    int32_t* idx_all = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
-    double* w_all = (double*)malloc(sizeof(double) * (size_t)(T * k));
-    int64_t* seen = (int64_t*)calloc((size_t)E, sizeof(int64_t));
-    keep = (uint8_t*)malloc((size_t)(T * k));
-    int rc = (idx_all && w_all && seen && keep) ? 0 : -2;
-    if (rc == 0)
-      rc = oracle_route(T, d, E, k, dt, x, W_router, bias, NULL, idx_all, w_all);
-    if (rc == 0)
-      for (int64_t s = 0; s < T * k; ++s) keep[s] = seen[idx_all[s]]++ < capacity;
-    free(idx_all);
-    free(w_all);
-    free(seen);
-    if (rc != 0) {
-      free(keep);
-      return rc;
-    }
+    int rc = capacity_keep(T, d, E, k, dt, x, W_router, bias, capacity, &keep);
+    if (rc != 0) return rc;
   }
 
   int fail = 0;
@@ -561,7 +569,7 @@ int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
 int oracle_layer_backward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
                           int64_t S, int dt, const void* x, const void* W_router,
                           const float* bias, const void* W_gate_up,
-                          const void* W_down, const void* dy, int64_t n_tok,
+                          const void* W_down, const void* dy, int64_t capacity, int64_t n_tok,
                           const int64_t* tok_list, double* dx, int64_t n_exp,
                           const int32_t* exp_list, double* dWgu, double* dWd,
                           double* dWr, double* db, double* dw) {
@@ -590,6 +598,7 @@ int oracle_layer_backward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
   double* O = (double*)malloc(sizeof(double) * (size_t)d);
   double* dO = (double*)malloc(sizeof(double) * (size_t)d);
   double* dxt = (double*)malloc(sizeof(double) * (size_t)d);
+  uint8_t* keep = NULL; /* [T*k] kept copies, with a capacity only */
   int rc = 0;
   if (!tok_pos || !exp_pos || !xt || !lg || !order || !idx || !w || !dwt || !g || !u ||
       !a || !da || !dg || !du || !O || !dO || !dxt) {
@@ -621,6 +630,13 @@ int oracle_layer_backward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
   if (dWr) memset(dWr, 0, sizeof(double) * (size_t)(E * d));
   if (db) memset(db, 0, sizeof(double) * (size_t)E);
   int router_grads = dWr || db || dw;
+  /* copies dropped by an expert capacity add nothing to y: no expert
+   * gradient, and dw = 0 (their weights still enter the softmax of the k
+   * selected logits, so dl keeps its form) */
+  if (capacity >= 0 && T > 0) {
+    rc = capacity_keep(T, d, E, k, dt, x, W_router, bias, capacity, &keep);
+    if (rc != 0) goto done;
+  }
 
   for (int64_t t = 0; t < T; ++t) {
     int listed = tok_pos[t] >= 0;
@@ -631,6 +647,10 @@ int oracle_layer_backward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
       int routed = j < k;
       int64_t e = routed ? idx[j] : E + (j - k);
       double wj = routed ? w[j] : 1.0;
+      if (routed && keep && !keep[t * k + j]) {
+        dwt[j] = 0.0;
+        continue;
+      }
       int want_e = exp_pos[e] >= 0;
       int need_O = routed && (listed || router_grads);
       if (!listed && !want_e && !need_O) continue;
@@ -702,6 +722,7 @@ int oracle_layer_backward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
     if (listed) memcpy(dx + tok_pos[t] * d, dxt, sizeof(double) * (size_t)d);
   }
 done:
+  free(keep);
   free(tok_pos);
   free(exp_pos);
   free(xt);

@@ -140,11 +140,13 @@ int oracle_layer_forward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
  * gate_up and down weights (exp_list, indices 0 .. E+S-1), the router
  * weights and bias, and the routing weights (dw [T, k]); all fp64, each
  * optional.  dx [n_tok, d], dWgu [n_exp, 2f, d], dWd [n_exp, d, f],
- * dWr [E, d], db [E]. */
+ * dWr [E, d], db [E].  capacity >= 0: the forward with that expert capacity
+ * (as oracle_layer_forward); dropped copies get no expert gradient and
+ * dw = 0. */
 int oracle_layer_backward(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
                           int64_t S, int dt, const void* x, const void* W_router,
                           const float* bias, const void* W_gate_up,
-                          const void* W_down, const void* dy, int64_t n_tok,
+                          const void* W_down, const void* dy, int64_t capacity, int64_t n_tok,
                           const int64_t* tok_list, double* dx, int64_t n_exp,
                           const int32_t* exp_list, double* dWgu, double* dWd,
                           double* dWr, double* db, double* dw);

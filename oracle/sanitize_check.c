@@ -83,14 +83,14 @@ int main(void) {
   double* dWr = (double*)malloc(sizeof(double) * E * d);
   double db[5], dw[18];
   int32_t exps[6] = {0, 1, 2, 3, 4, 5};
-  fails += oracle_layer_backward(T, d, f, E, k, S, ORACLE_F32, x, Wr, bias, Wgu, Wd, dy, 3, toks,
-                                 dx, G, exps, dWgu, dWd, dWr, db, dw) != 0;
+  fails += oracle_layer_backward(T, d, f, E, k, S, ORACLE_F32, x, Wr, bias, Wgu, Wd, dy, 2, 3,
+                                 toks, dx, G, exps, dWgu, dWd, dWr, db, dw) != 0;
   /* rejected arguments */
   fails += oracle_route(T, d, E, E + 1, ORACLE_F32, x, Wr, NULL, NULL, idx, w) == 0;
   fails += oracle_dequant_mxfp4(1, 31, q, sc, dq) == 0;
   int64_t dup[2] = {1, 1};
-  fails += oracle_layer_backward(T, d, f, E, k, S, ORACLE_F32, x, Wr, bias, Wgu, Wd, dy, 2, dup,
-                                 dx, 0, NULL, NULL, NULL, NULL, NULL, NULL) == 0;
+  fails += oracle_layer_backward(T, d, f, E, k, S, ORACLE_F32, x, Wr, bias, Wgu, Wd, dy, -1, 2,
+                                 dup, dx, 0, NULL, NULL, NULL, NULL, NULL, NULL) == 0;
   free(x); free(Wr); free(Wgu); free(Wd); free(dy); free(logits); free(idx); free(w);
   free(act); free(act32); free(O); free(O32); free(yc); free(y); free(dx); free(dWgu);
   free(dWd); free(dWr);

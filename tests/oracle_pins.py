@@ -752,4 +752,60 @@ def pin_backward_structure(orc):
     assert np.array_equal(part["dW_down"], full["dW_down"][[3, 0]])
 
 
+
+def pin_backward_capacity(orc):
+    """With an expert capacity: a capacity no expert reaches changes nothing
+    (bitwise); dropped copies get dw = 0; and central differences through
+    the capacity forward (the same keep set at every perturbation, since the
+    selection holds) match every gradient."""
+    T, d, f, E, k = 8, 8, 6, 3, 2
+    x, Wr, Wgu, Wd = rand_layer(54, T, d, f, E, k, 0, "f32")
+    Wr = Wr * 3.0
+    dy = moe_synth.normal((54, 6, 0), (T, d), 1.0, "f32")
+    bias = np.linspace(0.2, -0.1, E).astype(np.float32)
+    free = orc.layer_backward(x, Wr, Wgu, Wd, dy, k, bias=bias, experts=np.arange(E))
+    wide_cap = orc.layer_backward(x, Wr, Wgu, Wd, dy, k, bias=bias, experts=np.arange(E),
+                                  capacity=T * k)
+    for name in free:
+        assert np.array_equal(free[name], wide_cap[name]), name
+    C = 3
+    got = orc.layer_backward(x, Wr, Wgu, Wd, dy, k, bias=bias, experts=np.arange(E),
+                             capacity=C)
+    _, idx0, _ = orc.route(x, Wr, k, bias=bias)
+    _, _, _, slot_pos = orc.permute(idx0, E, capacity=C)
+    dropped = slot_pos.reshape(T, k) < 0
+    assert dropped.any() and not dropped.all()
+    assert np.all(got["dw"][dropped] == 0)
+    assert np.all(got["dw"][~dropped] != 0)
+    h = 2.0 ** -12
+
+    def loss(x_, Wr_, Wgu_, Wd_, b_):
+        _, idx, _ = orc.route(x_, Wr_, k, bias=b_)
+        assert np.array_equal(idx, idx0), "perturbation changed the selection"
+        y, _, _ = orc.layer_forward(x_, Wr_, Wgu_, Wd_, k, bias=b_, capacity=C)
+        return float((y * wide(dy)).sum())
+
+    rng = np.random.default_rng([54, 9])
+    args = dict(x=x, Wr=Wr, Wgu=Wgu, Wd=Wd, b=bias)
+    grads = dict(x=got["dx"], Wr=got["dW_router"], Wgu=got["dW_gate_up"], Wd=got["dW_down"],
+                 b=got["db"])
+    for name in ("x", "Wr", "Wgu", "Wd", "b"):
+        for _ in range(5):
+            pos = tuple(int(rng.integers(0, n)) for n in args[name].shape)
+            plus = {kk: v.copy() for kk, v in args.items()}
+            minus = {kk: v.copy() for kk, v in args.items()}
+            plus[name][pos] += np.float32(h)
+            minus[name][pos] -= np.float32(h)
+            fd = (loss(plus["x"], plus["Wr"], plus["Wgu"], plus["Wd"], plus["b"])
+                  - loss(minus["x"], minus["Wr"], minus["Wgu"], minus["Wd"], minus["b"])) / (2 * h)
+            g = grads[name][pos]
+            assert abs(fd - g) <= 1e-5 * (1.0 + abs(g)), (name, pos, fd, g)
+    # a dropped copy's expert sees no gradient from that token: the tokens
+    # whose every copy of expert e was dropped leave dW of e as if absent
+    for e in range(E):
+        kept_tok = [t for t in range(T) for j in range(k) if idx0[t, j] == e and not dropped[t, j]]
+        if not kept_tok:
+            assert np.all(got["dW_gate_up"][e] == 0) and np.all(got["dW_down"][e] == 0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

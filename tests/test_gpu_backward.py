@@ -115,6 +115,81 @@ def test_backward_small(case):
           flush=True)
 
 
+CAP_CASES = [
+    # (T, d, f, E, k, S, zipf, capacity factor, seed): skewed routing so that
+    # the popular experts drop copies; capacity 0 drops every routed copy;
+    # the last case runs the multi-workgroup permutation (T*k >= 8192)
+    (64, 136, 200, 6, 2, 1, 1.2, 1.0, 11),
+    (33, 64, 72, 5, 3, 0, 1.5, 0.6, 12),
+    (20, 64, 40, 4, 2, 1, None, 0.0, 13),
+    (4200, 64, 64, 8, 2, 0, 1.1, 1.25, 14),
+]
+
+
+@pytest.mark.parametrize("case", CAP_CASES, ids=str)
+def test_backward_capacity(case):
+    """moe_layer_backward after moe_layer_forward_capacity against the
+    oracle's gradients of the capacity forward (pinned by central
+    differences): dropped copies add no expert gradient, get dw = 0, and
+    their logits keep dl."""
+    T, d, f, E, k, S, zipf, factor, seed = case
+    print(f"backward capacity T={T} d={d} f={f} E={E} k={k} S={S} factor={factor}", flush=True)
+    cfg = moe_synth.tiny_config(T=T, d=d, f=f, E=E, k=k, S=S, dtype="bf16", zipf_s=zipf)
+    cfg = cfg.scaled(w_std=0.08)
+    inp = moe_synth.make_layer_inputs(cfg, 90 + seed)
+    dyh = moe_synth.normal((90 + seed, 8, 0), (T, d), 1.0, "bf16")
+    dinp = layer_inputs_to_device(inp)
+    C = oracle.expert_capacity(T, k, E, factor)
+    s = moe.shape(T, d, f, E, k, S, moe.MOE_DT_BF16)
+    fws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    moe.moe_layer_forward_capacity(s, dinp["x"], dinp["W_router"], dinp["bias"],
+                                   dinp["W_gate_up"], dinp["W_down"], C, y, fws)
+    G = E + S
+    out = {"dx": torch.empty(T, d, device="cuda"),
+           "dW_router": torch.empty(E, d, device="cuda"),
+           "db": torch.empty(E, device="cuda"),
+           "dW_gate_up": torch.empty(G, 2 * f, d, device="cuda"),
+           "dW_down": torch.empty(G, d, f, device="cuda"),
+           "dw": torch.empty(T, k, device="cuda")}
+    bws = torch.empty(moe.backward_workspace_size(s), dtype=torch.uint8, device="cuda")
+    moe.moe_layer_backward(s, dinp["x"], dinp["W_router"], dinp["W_gate_up"], dinp["W_down"],
+                           dev(dyh), fws, out["dx"], out["dW_router"], out["db"],
+                           out["dW_gate_up"], out["dW_down"], out["dw"], bws)
+    torch.cuda.synchronize()
+    views = moe.workspace_views(s, fws)
+    sp = host(views["slot_pos"]).reshape(T, k)
+    dropped = sp < 0
+    _, idx_ref, _ = oracle.route(inp["x"], inp["W_router"], k, bias=inp["bias"])
+    _, _, _, sp_ref = oracle.permute(idx_ref, E, S, capacity=C)
+    assert np.array_equal(sp, sp_ref.reshape(T, k))
+    assert dropped.any()
+    ref = oracle.layer_backward(inp["x"], inp["W_router"], inp["W_gate_up"], inp["W_down"], dyh,
+                                k, S=S, bias=inp["bias"], experts=np.arange(G), capacity=C)
+    worst = {}
+    for name in ("dx", "dW_router", "dW_gate_up", "dW_down"):
+        worst[name] = assert_grad_rows(host(out[name]), ref[name], name)
+    db, db_ref = host(out["db"]), ref["db"]
+    assert np.all(np.abs(db - db_ref) <= 2e-2 * np.abs(db_ref) + 1e-3 * np.abs(db_ref).max())
+    dw = host(out["dw"])
+    assert np.all(dw[dropped] == 0)
+    # expert_out rows of dropped copies are never written: read kept rows only
+    kept = ~dropped
+    tk, jk = np.nonzero(kept)
+    O = moe_synth.bf16_bits_to_f32(host(views["expert_out"])[sp[kept]]).astype(np.float64)
+    dyw = moe_synth.bf16_bits_to_f32(dyh).astype(np.float64)
+    cond = np.einsum("cd,cd->c", np.abs(O), np.abs(dyw[tk]))
+    assert np.all(np.abs(dw[tk, jk] - ref["dw"][tk, jk]) <= 2e-2 * cond)
+    # experts whose every copy was dropped (or that none selected): zero
+    # expert gradients; their router rows still move (the dropped logits)
+    counts = host(views["counts"])[:E]
+    empty_e = np.nonzero(counts == 0)[0]
+    assert np.all(host(out["dW_gate_up"])[empty_e] == 0)
+    assert np.all(host(out["dW_down"])[empty_e] == 0)
+    print(f"  capacity {C}, {int(dropped.sum())} of {T * k} copies dropped; worst row rel err "
+          + ", ".join(f"{k2} {v:.2e}" for k2, v in worst.items()), flush=True)
+
+
 def test_backward_decode_full():
     """The gpt-oss-20b-shaped decode layer (T=16, d=f=2880, E=32, top-4):
     every gradient."""

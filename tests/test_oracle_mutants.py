@@ -99,6 +99,9 @@ MUTANTS = {
     # backward: down-weight gradient against the wrong activation column
     "bwd_dWd_misindexed": (
         "gd[i * f + n] += dO[i] * a[n];", "gd[i * f + n] += dO[i] * a[(n + 1) % f];"),
+    # backward with a capacity: dropped copies still sent through their expert
+    "bwd_capacity_ignored": (
+        "if (routed && keep && !keep[t * k + j]) {", "if (routed && keep && 0) {"),
     # balance: KL with its arguments swapped
     "balance_kl_reversed": (
         "kl += u * (log(u) - log(importance[e] + 1e-8));",
