@@ -221,6 +221,10 @@ class Layer:
         self.y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16 if self.dt else torch.float32,
                              device="cuda")
         self.views = moe.workspace_views(self.s, self.ws)
+        # the layer's router keeps partial sums in its workspace; timed alone
+        # through moe_route_ws with a workspace of its own
+        nr = moe.route_workspace_size(self.s)
+        self.rws = torch.empty(nr, dtype=torch.uint8, device="cuda") if nr else None
         self.moe = moe
 
     def step(self, i=0):
@@ -234,8 +238,8 @@ class Layer:
         on the buffers of the last layer call."""
         moe, s, d, v = self.moe, self.s, self.d, self.views
         return {
-            "route": time_calls(torch, lambda: moe.moe_route(
-                s, d["x"], d["W_router"], d["bias"], v["topk_idx"], v["topk_w"]), n),
+            "route": time_calls(torch, lambda: moe.moe_route_ws(
+                s, d["x"], d["W_router"], d["bias"], v["topk_idx"], v["topk_w"], self.rws), n),
             "permute": time_calls(torch, lambda: moe.moe_permute(
                 s, v["topk_idx"], v["counts"], v["offsets"], v["sorted_slot"],
                 v["slot_pos"]), n),
@@ -249,8 +253,9 @@ class Layer:
 
     def aux_times(self, torch, n, factor=1.25):
         """The router auxiliaries on this workload: moe_route_balance (routing
-        plus importance and balance loss) against moe_route, and the layer
-        with an expert capacity of `factor` times the even share."""
+        plus importance and balance loss) against moe_route (both the
+        one-kernel router, without a workspace for partial sums), and the
+        layer with an expert capacity of `factor` times the even share."""
         moe, s, d, v, cfg = self.moe, self.s, self.d, self.views, self.cfg
         ws_b = torch.empty(max(1, moe.route_balance_workspace_size(s)), dtype=torch.uint8,
                            device="cuda")

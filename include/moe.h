@@ -114,6 +114,21 @@ int moe_route(const moe_shape* s, const void* x, const void* W_router,
               const float* bias, int32_t* topk_idx, float* topk_w,
               void* stream);
 
+/* moe_route_ws: moe_route with a workspace for the router's partial sums.
+ * Same steps and results (selection and weights); large bf16 batches with
+ * few experts or a large router matrix route faster with it: the screen runs
+ * as a K-split product over tiles of 64 or 128 tokens, whose fp64 partials
+ * the workspace holds, then a selection pass.  moe_layer_forward does the
+ * same inside its own workspace.
+ *   workspace  moe_route_workspace_size(s) bytes, 256-byte aligned (NULL
+ *              when the size is 0); MOE_ERR_WORKSPACE if smaller; it holds
+ *              nothing of use after the call. */
+size_t moe_route_workspace_size(const moe_shape* s);
+
+int moe_route_ws(const moe_shape* s, const void* x, const void* W_router,
+                 const float* bias, int32_t* topk_idx, float* topk_w,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------- router load statistics
  * moe_route_balance: moe_route plus the router's load statistics and the
  * load-balance loss (yunthe "分工的艺术" page, section 3.1, load balance

@@ -38,7 +38,8 @@ ENTRY_POINTS = ("moe_status_string", "moe_version", "moe_last_hip_error", "moe_r
                 "moe_permute_capacity", "moe_expert_capacity",
                 "moe_layer_forward_capacity", "moe_grouped_gemm_gate_up_mxfp4",
                 "moe_grouped_gemm_down_mxfp4", "moe_layer_forward_mxfp4",
-                "moe_backward_workspace_size", "moe_layer_backward")
+                "moe_backward_workspace_size", "moe_layer_backward",
+                "moe_route_workspace_size", "moe_route_ws")
 
 # size of the library's static intermediate array (include/moe.h)
 STATIC_SCRATCH_BYTES = 32 << 20
@@ -89,6 +90,8 @@ def _load():
     L.moe_workspace_offsets.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
     L.moe_route_balance_workspace_size.argtypes = [sp]
     L.moe_route_balance_workspace_size.restype = ctypes.c_size_t
+    L.moe_route_workspace_size.argtypes = [sp]
+    L.moe_route_workspace_size.restype = ctypes.c_size_t
     i64 = ctypes.c_int64
     L.moe_expert_capacity.argtypes = [i64, i64, i64, ctypes.c_double]
     L.moe_expert_capacity.restype = i64
@@ -96,6 +99,7 @@ def _load():
     L.moe_backward_workspace_size.restype = ctypes.c_size_t
     sigs = {
         "moe_route": [sp, vp, vp, vp, vp, vp, vp],
+        "moe_route_ws": [sp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "moe_permute": [sp, vp, vp, vp, vp, vp, vp],
         "moe_grouped_gemm_gate_up": [sp, vp, vp, vp, vp, vp, vp],
         "moe_grouped_gemm_down": [sp, vp, vp, vp, vp, vp],
@@ -147,6 +151,10 @@ def shape(T, d, f, E, k, n_shared=0, dt=MOE_DT_BF16) -> moe_shape:
 
 def workspace_size(s: moe_shape) -> int:
     return int(_lib.moe_workspace_size(ctypes.byref(s)))
+
+
+def route_workspace_size(s: moe_shape) -> int:
+    return int(_lib.moe_route_workspace_size(ctypes.byref(s)))
 
 
 def route_balance_workspace_size(s: moe_shape) -> int:
@@ -221,6 +229,21 @@ def moe_route(s: moe_shape, x, W_router, bias, topk_idx, topk_w, stream=None):
           _ptr(topk_idx, s.T * s.k, torch.int32, "topk_idx"),
           _ptr(topk_w, s.T * s.k, torch.float32, "topk_w"),
           _stream(stream))
+
+
+def moe_route_ws(s: moe_shape, x, W_router, bias, topk_idx, topk_w, workspace, stream=None):
+    """moe_route with a workspace of route_workspace_size(s) bytes (uint8 GPU
+    tensor, or None when that size is 0)."""
+    torch = _torch()
+    fd = _float_dtype(s)
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _call("moe_route_ws", ctypes.byref(s),
+          _ptr(x, s.T * s.d, fd, "x"),
+          _ptr(W_router, s.E * s.d, fd, "W_router"),
+          _ptr(bias, s.E, torch.float32, "bias", optional=True),
+          _ptr(topk_idx, s.T * s.k, torch.int32, "topk_idx"),
+          _ptr(topk_w, s.T * s.k, torch.float32, "topk_w"),
+          ws_ptr, ws_bytes, _stream(stream))
 
 
 def moe_route_balance(s: moe_shape, x, W_router, bias, topk_idx, topk_w, importance, loss,

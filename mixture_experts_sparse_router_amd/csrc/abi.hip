@@ -158,6 +158,29 @@ int moe_route(const moe_shape* m, const void* x, const void* W_router, const flo
       launch_route(s, x, W_router, bias, topk_idx, topk_w, nullptr, (hipStream_t)stream));
 }
 
+size_t moe_route_workspace_size(const moe_shape* m) {
+  if (check_shape(m) != MOE_OK) return 0;
+  return route_workspace_bytes(to_shape(m));
+}
+
+int moe_route_ws(const moe_shape* m, const void* x, const void* W_router, const float* bias,
+                 int32_t* topk_idx, float* topk_w, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  int rc = check_shape(m);
+  if (rc != MOE_OK) return rc;
+  const Shape s = to_shape(m);
+  if (!ok_ptr(x, s.T * s.d) || !ok_ptr(W_router, s.E * s.d) ||
+      !ok_ptr(topk_idx, s.Tk()) || !ok_ptr(topk_w, s.Tk()))
+    return MOE_ERR_INVALID_ARG;
+  if (bias && ((uintptr_t)bias & 3u)) return MOE_ERR_INVALID_ARG;
+  const size_t need = route_workspace_bytes(s);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u))) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_route(s, x, W_router, bias, topk_idx, topk_w, nullptr,
+                                 (hipStream_t)stream, need > 0 ? workspace : nullptr,
+                                 workspace_bytes));
+}
+
 size_t moe_route_balance_workspace_size(const moe_shape* m) {
   if (check_shape(m) != MOE_OK) return 0;
   size_t lo, part;
@@ -303,7 +326,10 @@ int layer_forward(const moe_shape* m, const void* x, const void* W_router, const
   void* out = ws + off[MOE_WS_EXPERT_OUT];
 
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_route(s, x, W_router, bias, idx, w, nullptr, st);
+  // act and expert_out (the workspace's last two regions) are written only
+  // after the router: it may keep partial sums there
+  hipError_t e = launch_route(s, x, W_router, bias, idx, w, nullptr, st, act,
+                              total - off[MOE_WS_ACT]);
   if (s.dt == MOE_DT_BF16 && s.T <= 64 && capacity < 0) {
     // decode batches: the gate_up kernel finds its rows from the ids and
     // writes the permutation itself (one launch fewer)

@@ -125,9 +125,15 @@ inline Shape to_shape(const moe_shape* s) {
 // Launchers (return hipSuccess or the launch error).  Argument checking is
 // done by the ABI layer before any of these is called.
 // logits_out: NULL, or [T, E] fp32 that receives the logits (bias included).
+// scratch: NULL, or device memory (256-byte aligned) that the router may use
+// for partial sums until it returns to the stream (large bf16 batches).
 hipError_t launch_route(const Shape& s, const void* x, const void* W_router,
                         const float* bias, int32_t* topk_idx, float* topk_w,
-                        float* logits_out, hipStream_t st);
+                        float* logits_out, hipStream_t st, void* scratch = nullptr,
+                        size_t scratch_bytes = 0);
+// Scratch bytes with which launch_route takes its fastest path for this
+// shape (0: it needs none).
+size_t route_workspace_bytes(const Shape& s);
 // capacity < 0: none.
 hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int64_t capacity,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slot,

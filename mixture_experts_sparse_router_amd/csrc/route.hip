@@ -706,10 +706,10 @@ __device__ __forceinline__ double exact_batch(const bf16_t* __restrict__ xt,
   return __shfl(v, lane < CB ? lane * (64 / CB) : 0, 64);
 }
 
-// Steps 2-4 for the workgroup's tokens, one wave per token, once the screen
-// logits and norms are in LDS (and the ring is no longer in use).  M: experts
-// per lane, at least ceil(E / 64).
-template <int M>
+// Steps 2-4 for the workgroup's TT tokens, one wave per token, once the
+// screen logits and norms are in LDS (and the ring is no longer in use).  M:
+// experts per lane, at least ceil(E / 64).
+template <int M, int TT = kScreenTT, int MaxCB = 8>
 __device__ void screen_select(const ScreenSmem& S, const bf16_t* __restrict__ x,
                               const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
                               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -719,7 +719,7 @@ __device__ void screen_select(const ScreenSmem& S, const bf16_t* __restrict__ x,
   uint16_t* mycand = S.cand + wave * E;
   SelSlots* sl = S.sls + wave;
   const double rel = kScreenRel * kScreenFac;
-  for (int tl = wave; tl < kScreenTT; tl += kScreenWaves) {
+  for (int tl = wave; tl < TT; tl += kScreenWaves) {
     const int64_t t = t0 + tl;
     if (t >= T) break;
     double* row = S.lg + (int64_t)tl * E;
@@ -778,10 +778,11 @@ __device__ void screen_select(const ScreenSmem& S, const bf16_t* __restrict__ x,
     int my_e = 0;
     for (int c0 = 0; c0 < ncand;) {
       const int left = ncand - c0;
-      const int cb = left >= 8 ? 8 : left >= 4 ? 4 : left >= 2 ? 2 : 1;
+      const int cb = (left >= 8 && MaxCB >= 8) ? 8 : (left >= 4 && MaxCB >= 4) ? 4
+                     : left >= 2 ? 2 : 1;
       double got;  // lane u < cb: candidate c0 + u
-      if (cb == 8) got = exact_batch<8>(xt, Wr, mycand, c0, ncand, d);
-      else if (cb == 4) got = exact_batch<4>(xt, Wr, mycand, c0, ncand, d);
+      if (MaxCB >= 8 && cb == 8) got = exact_batch<8>(xt, Wr, mycand, c0, ncand, d);
+      else if (MaxCB >= 4 && cb == 4) got = exact_batch<4>(xt, Wr, mycand, c0, ncand, d);
       else if (cb == 2) got = exact_batch<2>(xt, Wr, mycand, c0, ncand, d);
       else got = exact_batch<1>(xt, Wr, mycand, c0, ncand, d);
       if (ncand > 64) {
@@ -1088,6 +1089,388 @@ __global__ __launch_bounds__(kScreenThreads, 1) void route_direct_kernel(
   else screen_select<16>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
 }
 
+// ------------------------------------------------------------ route_split
+// bf16, large T, with a scratch buffer for the partial sums: the screen of
+// route_staged as a K-split product over tiles of 16*NTB tokens x 16*NEB
+// experts (route_part), then the selection, one wave per token (route_pick).
+// route_staged copies every expert row into LDS once per 16 tokens; here
+// once per 16*NTB, and the K split gives every CU a tile when T / (16*NTB)
+// tiles alone would not.  The arithmetic is the screen's: fp32 MFMA sums over
+// groups of 4 K steps of 64 (restarted at the start of each split), each
+// group added to an fp64 total; the splits' fp64 totals are added in split
+// order.  The screen bound therefore holds unchanged.
+//   part [SK][T][E] double   screen logits of split s (no bias)
+//   xsq  [SK][T]    double   ||x_t||^2 of split s (Gram diagonal)
+//   wsq  [SK][E]    double   ||w_e||^2 of split s
+template <int NTB, int NEB, int WT, int WE>
+struct PartCfg {
+  static constexpr int kNWE = NEB / WE;  // wave columns (expert groups)
+  static_assert(NTB % WT == 0 && NEB % WE == 0 && (NTB / WT) * kNWE == kScreenWaves,
+                "one wave tile per wave");
+  static constexpr int kXRows = 16 * NTB, kWRows = 16 * NEB;
+  static constexpr int kXStage = kXRows * 128, kWStage = kWRows * 128;
+  static constexpr int kXCopies = kXRows / 8;
+  static constexpr int kCopies = (kXRows + kWRows) / 8;  // 1 KB copies per K step
+  static constexpr int kCpw = (kCopies + kScreenWaves - 1) / kScreenWaves;
+  static constexpr int kStages = (kXStage + kWStage) * 4 <= 112 * 1024 ? 4 : 3;
+  static_assert((kStages - 1) * kCpw < 64, "vmcnt range");
+};
+
+template <int NTB, int NEB, int WT, int WE>
+__global__ __launch_bounds__(kScreenThreads, 1) void route_part_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, double* __restrict__ part,
+    double* __restrict__ xsq, double* __restrict__ wsq, int64_t T, int64_t d, int E, int SK,
+    int ntiles) {
+  using C = PartCfg<NTB, NEB, WT, WE>;
+  // two LDS objects (see route_staged): the fragment reads need not wait
+  // for copies in flight; the vmcnt waits and barriers order them
+  __shared__ __attribute__((aligned(1024))) unsigned char ringX[C::kStages * C::kXStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char ringW[C::kStages * C::kWStage + 1024];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, kb = lane >> 4;
+  // workgroup -> (token tile, split): consecutive workgroups go to the 8
+  // XCDs in turn; split s = xcd % SK, so the tiles of one split, which read
+  // the same columns of W, share an XCD's L2
+  const int xcd = (int)(blockIdx.x % 8u), slot = (int)(blockIdx.x / 8u);
+  const int s = xcd % SK;
+  const int tile = xcd / SK + (8 / SK) * slot;
+  if (tile >= ntiles) return;
+  const int64_t t0 = (int64_t)tile * C::kXRows;
+  const int64_t nsteps = (d + 63) / 64;
+  const int64_t per = (nsteps + SK - 1) / SK;
+  const int64_t s0 = (int64_t)s * per;
+  const int64_t s1 = s0 + per < nsteps ? s0 + per : nsteps;  // may be <= s0: an empty split
+  const uint32_t rowb = (uint32_t)(d * 2);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)(uint32_t)(T * d * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Wr, 0, (int)(uint32_t)(E * d * 2), kRsrcWord3);
+  uint32_t ringx_i = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ringX;
+  uint32_t ringw_i = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ringW;
+  asm("" : "+s"(ringx_i), "+s"(ringw_i));
+  const uint32_t pad_dst = ringw_i + C::kStages * C::kWStage;
+
+  // copy plan (route_staged's): copy i = wave + 8c moves stage rows 8i ..
+  // 8i+7, lane l row 8i + l/8, LDS chunk l%8 holding the row's chunk
+  // (l%8) ^ (row%8).  Rows < 16*NTB are tokens (past T: the last token
+  // again), the rest experts (past E: out of range, zero).
+  uint32_t base[C::kCpw], kch[C::kCpw], dst[C::kCpw];
+#pragma unroll
+  for (int c = 0; c < C::kCpw; ++c) {
+    const int i = wave + 8 * c;
+    const int r = 8 * i + (lane >> 3);
+    kch[c] = (uint32_t)(((lane & 7) ^ (r & 7)) * 16);
+    uint32_t b = kOOB;
+    if (i < C::kXCopies) {
+      const int64_t t = t0 + r < T ? t0 + r : T - 1;
+      b = (uint32_t)t * rowb;
+    } else if (i < C::kCopies && r - C::kXRows < E) {
+      b = (uint32_t)(r - C::kXRows) * rowb;
+    }
+    base[c] = b;
+    dst[c] = i < C::kXCopies ? (uint32_t)(8 * i) * 128 : (uint32_t)(8 * (i - C::kXCopies)) * 128;
+  }
+  auto issue = [&](int stage, int64_t st) {
+    const uint32_t koff = (uint32_t)(st * 128);
+    const bool live = st < s1;
+#pragma unroll
+    for (int c = 0; c < C::kCpw; ++c) {
+      const int i = wave + 8 * c;
+      const uint32_t o =
+          (live && base[c] != kOOB && koff + kch[c] < rowb) ? base[c] + koff + kch[c] : kOOB;
+      if (i < C::kXCopies)
+        copy16(rx, o, ringx_i + (uint32_t)stage * C::kXStage + dst[c]);
+      else if (i < C::kCopies)
+        copy16(rw, o, ringw_i + (uint32_t)stage * C::kWStage + dst[c]);
+      else
+        copy16(rw, kOOB, pad_dst);
+    }
+  };
+  // this wave's tile: token blocks tg*WT + p, expert blocks eg*WE + q
+  const int tg = wave / C::kNWE, eg = wave % C::kNWE;
+  const uint32_t f0 = (uint32_t)(((2 * kb) ^ (j & 7)) * 16);
+  const uint32_t f1 = (uint32_t)(((2 * kb + 1) ^ (j & 7)) * 16);
+  const bool xnorm = eg == 0;                // every tile: ||x||^2 of its tokens
+  const bool wnorm = tile == 0 && tg == 0;   // tile 0: ||w||^2 of every expert
+
+  f32x4 acc[WT][WE], accx[WT], accw[WE];
+  double accD[WT][WE][4], xsqD[WT][4], wsqD[WE][4];
+#pragma unroll
+  for (int p = 0; p < WT; ++p) {
+    accx[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xsqD[p][i] = 0.0;
+#pragma unroll
+    for (int q = 0; q < WE; ++q) {
+      acc[p][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) accD[p][q][i] = 0.0;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < WE; ++q) {
+    accw[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wsqD[q][i] = 0.0;
+  }
+  auto flush = [&]() {
+#pragma unroll
+    for (int p = 0; p < WT; ++p) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xsqD[p][i] += (double)accx[p][i];
+      accx[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < WE; ++q) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accD[p][q][i] += (double)acc[p][q][i];
+        acc[p][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < WE; ++q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wsqD[q][i] += (double)accw[q][i];
+      accw[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+#pragma unroll
+  for (int q = 0; q < C::kStages; ++q) issue(q, s0 + q);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::kStages - 1) * C::kCpw) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  int stage = 0, mine = 0;
+  for (int64_t st = s0; st < s1; ++st) {
+    const unsigned char* sx = ringX + (uint32_t)stage * C::kXStage;
+    const unsigned char* sw = ringW + (uint32_t)stage * C::kWStage;
+    u32x4 a0[WT], a1[WT], b0[WE], b1[WE];
+#pragma unroll
+    for (int p = 0; p < WT; ++p) {
+      const uint32_t ro = (uint32_t)(16 * (tg * WT + p) + j) * 128;
+      a0[p] = *reinterpret_cast<const u32x4*>(sx + ro + f0);
+      a1[p] = *reinterpret_cast<const u32x4*>(sx + ro + f1);
+    }
+#pragma unroll
+    for (int q = 0; q < WE; ++q) {
+      const uint32_t ro = (uint32_t)(16 * (eg * WE + q) + j) * 128;
+      b0[q] = *reinterpret_cast<const u32x4*>(sw + ro + f0);
+      b1[q] = *reinterpret_cast<const u32x4*>(sw + ro + f1);
+    }
+#pragma unroll
+    for (int p = 0; p < WT; ++p) {
+#pragma unroll
+      for (int q = 0; q < WE; ++q) {
+        acc[p][q] = mfma16(a0[p], b0[q], acc[p][q]);
+        acc[p][q] = mfma16(a1[p], b1[q], acc[p][q]);
+      }
+    }
+    if (xnorm) {
+#pragma unroll
+      for (int p = 0; p < WT; ++p) {
+        accx[p] = mfma16(a0[p], a0[p], accx[p]);
+        accx[p] = mfma16(a1[p], a1[p], accx[p]);
+      }
+    }
+    if (wnorm) {
+#pragma unroll
+      for (int q = 0; q < WE; ++q) {
+        accw[q] = mfma16(b0[q], b0[q], accw[q]);
+        accw[q] = mfma16(b1[q], b1[q], accw[q]);
+      }
+    }
+    if (++mine == kGroupSteps) {
+      flush();
+      mine = 0;
+    }
+    // step st+1 has landed everywhere and every read of step st is done:
+    // refill step st's stage
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((C::kStages - 2) * C::kCpw) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(stage, st + C::kStages);
+    stage = stage + 1 == C::kStages ? 0 : stage + 1;
+  }
+  flush();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // lane (j, kb) holds D[4kb + i][j] of every block pair; the Gram
+  // diagonals sit on the lanes with kb = j/4, element j%4
+  const bool diag = holds_diag(j, kb);
+  const int dq = j & 3;
+#pragma unroll
+  for (int p = 0; p < WT; ++p) {
+    const int64_t tr = t0 + 16 * (tg * WT + p);
+#pragma unroll
+    for (int q = 0; q < WE; ++q) {
+      const int e = 16 * (eg * WE + q) + j;
+      if (e < E) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t t = tr + 4 * kb + i;
+          if (t < T) part[((int64_t)s * T + t) * E + e] = accD[p][q][i];
+        }
+      }
+    }
+    if (xnorm && diag && tr + j < T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (dq == i) xsq[(int64_t)s * T + tr + j] = xsqD[p][i];
+    }
+  }
+  if (wnorm && diag) {
+#pragma unroll
+    for (int q = 0; q < WE; ++q) {
+      const int e = 16 * (eg * WE + q) + j;
+      if (e < E) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (dq == i) wsq[(int64_t)s * E + e] = wsqD[q][i];
+      }
+    }
+  }
+}
+
+// LDS of route_pick: the screen layout for kPickTT tokens, no ring and no
+// K-split partials.
+// Four waves and exact logits in batches of at most 2 keep the kernel at 88
+// VGPRs: five workgroups per CU, every token of a 4096-token batch in
+// flight at once (measured fastest of 8 or 4 waves with batches of 8, 4
+// or 2: Mixtral-shaped 57 -> 41 us, fine-grained Zipf 50 -> 44 us for both
+// kernels together, DeepSeek-shaped unchanged).
+constexpr int kPickWaves = 4;
+constexpr int kPickTT = kPickWaves;  // one token per wave
+constexpr int kPickThreads = 64 * kPickWaves;
+constexpr int kPickCB = 2;  // largest batch of exact logits
+__host__ __device__ constexpr ScreenLds pick_lds(int E) {
+  ScreenLds o{};
+  o.lg = 0;
+  o.wn = o.lg + (int64_t)kPickTT * E * 8;
+  o.xn = o.wn + ((int64_t)E * 4 + 15) / 16 * 16;
+  o.xp = o.xn + kScreenTT * 4;
+  o.sl = o.xp;  // no partials
+  o.un = o.sl + (int64_t)kPickWaves * sizeof(SelSlots);
+  o.total = o.un + ((int64_t)kPickWaves * E * 2 + 15) / 16 * 16;
+  return o;
+}
+
+// Steps 2-4 from the partials: one workgroup of 8 waves per 8 tokens adds
+// the splits (split order), the bias and the norms, then selects as
+// route_staged does.
+template <int M>
+__global__ __launch_bounds__(kPickThreads) void route_pick_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
+    const double* __restrict__ part, const double* __restrict__ xsq,
+    const double* __restrict__ wsq, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ logits_out, int64_t T, int64_t d, int E, int k, int SK) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const ScreenLds L = pick_lds(E);
+  const ScreenSmem S(smem, L);
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * kPickTT;
+  for (int e = tid; e < E; e += kPickThreads) {
+    double q = 0.0;
+    for (int sp = 0; sp < SK; ++sp) q += wsq[(int64_t)sp * E + e];
+    S.wn[e] = __double2float_ru(sqrt(q));
+  }
+  if (tid < kPickTT) {
+    const int64_t t = t0 + tid < T ? t0 + tid : T - 1;
+    double q = 0.0;
+    for (int sp = 0; sp < SK; ++sp) q += xsq[(int64_t)sp * T + t];
+    S.xn[tid] = __double2float_ru(sqrt(q));
+  }
+  for (int o = tid; o < kPickTT * E; o += kPickThreads) {
+    const int tl = o / E, e = o % E;
+    const int64_t t = t0 + tl < T ? t0 + tl : T - 1;
+    double v = 0.0;
+    for (int sp = 0; sp < SK; ++sp) v += part[((int64_t)sp * T + t) * E + e];
+    S.lg[o] = rank_value(v, bias, e);
+  }
+  __syncthreads();
+  screen_select<M, kPickTT, kPickCB>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
+}
+
+// Split count and scratch bytes of route_split for an NTB-token-block tile:
+// the fewest splits (1, 2, 4 or 8) that give 256 workgroups, fewer if the
+// scratch is smaller; 0 if not even one split fits.
+constexpr int kPartMaxSK = 8;
+struct SplitPlan {
+  int SK, ntiles;
+  size_t part_off, xsq_off, wsq_off, bytes;
+};
+inline bool plan_split(const Shape& s, int NTB, size_t scratch_bytes, SplitPlan* pl) {
+  const int64_t ntiles = (s.T + 16 * NTB - 1) / (16 * NTB);
+  const int64_t nsteps = (s.d + 63) / 64;
+  int SK = 1;
+  while (SK < kPartMaxSK && ntiles * SK < 256 && nsteps >= 2 * SK) SK *= 2;
+  auto bytes = [&](int sk, size_t* a, size_t* b, size_t* c) {
+    const size_t p = (size_t)sk * (size_t)s.T * (size_t)s.E * 8;
+    const size_t xq = (size_t)sk * (size_t)s.T * 8;
+    const size_t wq = (size_t)sk * (size_t)s.E * 8;
+    *a = 0;
+    *b = (p + 255) & ~(size_t)255;
+    *c = *b + ((xq + 255) & ~(size_t)255);
+    return *c + wq;
+  };
+  for (; SK >= 1; SK /= 2) {
+    size_t a, b, c;
+    const size_t total = bytes(SK, &a, &b, &c);
+    if (total <= scratch_bytes) {
+      *pl = SplitPlan{SK, (int)ntiles, a, b, c, total};
+      return true;
+    }
+  }
+  return false;
+}
+
+template <int NTB, int NEB, int WT, int WE, int M>
+hipError_t launch_split(const Shape& s, const void* x, const void* Wr, const float* bias,
+                        int32_t* idx, float* w, float* lo, const SplitPlan& pl,
+                        unsigned char* scratch, hipStream_t st) {
+  double* part = (double*)(scratch + pl.part_off);
+  double* xq = (double*)(scratch + pl.xsq_off);
+  double* wq = (double*)(scratch + pl.wsq_off);
+  const unsigned grid1 = (unsigned)((((int64_t)pl.ntiles * pl.SK + 7) / 8) * 8);
+  hipLaunchKernelGGL((route_part_kernel<NTB, NEB, WT, WE>), dim3(grid1), dim3(kScreenThreads), 0,
+                     st, (const bf16_t*)x, (const bf16_t*)Wr, part, xq, wq, s.T, s.d, (int)s.E,
+                     pl.SK, pl.ntiles);
+  const unsigned grid2 = (unsigned)((s.T + kPickTT - 1) / kPickTT);
+  hipLaunchKernelGGL(route_pick_kernel<M>, dim3(grid2), dim3(kPickThreads),
+                     (size_t)pick_lds((int)s.E).total, st, (const bf16_t*)x, (const bf16_t*)Wr,
+                     bias, (const double*)part, (const double*)xq, (const double*)wq, idx, w, lo,
+                     s.T, s.d, (int)s.E, (int)s.k, pl.SK);
+  return hipGetLastError();
+}
+
+// route_split if it applies (bf16, 64 < T, E <= 256, the scratch holds the
+// partials of at least one split) and pays: route_staged copies 128 expert
+// rows per K step even for fewer experts, and streams all of W once per 16
+// tokens, while route_split reads x twice and sums partials.  Measured:
+// E = 8 (Mixtral shape) 82 -> 41 us, W of 3.7 MB (DeepSeek shape, E = 256)
+// 127 -> 109 us, but E = 128 with W of 0.5 MB (fine-grained Zipf) 38.5 ->
+// 44 us: route_split is taken for E <= 64 or W of at least 2 MB.  Else
+// hipErrorNotSupported and nothing is launched.
+inline bool split_applies(const Shape& s) {
+  if (s.dt != MOE_DT_BF16 || s.T <= 64 || s.E > 256 || s.E * s.d * 2 >= ((int64_t)1 << 31))
+    return false;
+  return s.E <= 64 || s.E * s.d * 2 >= ((int64_t)2 << 20);
+}
+inline int split_ntb(const Shape& s) { return s.E <= 32 ? 8 : 4; }
+
+hipError_t try_split(const Shape& s, const void* x, const void* Wr, const float* bias,
+                     int32_t* idx, float* w, float* lo, void* scratch, size_t scratch_bytes,
+                     hipStream_t st) {
+  if (!scratch || !split_applies(s)) return hipErrorNotSupported;
+  SplitPlan pl;
+  unsigned char* sc = (unsigned char*)scratch;
+  if (!plan_split(s, split_ntb(s), scratch_bytes, &pl)) return hipErrorNotSupported;
+  if (s.E <= 16) return launch_split<8, 1, 1, 1, 1>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
+  if (s.E <= 32) return launch_split<8, 2, 2, 1, 1>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
+  if (s.E <= 64) return launch_split<4, 4, 2, 1, 1>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
+  if (s.E <= 128) return launch_split<4, 8, 2, 2, 2>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
+  return launch_split<4, 16, 2, 4, 4>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
+}
+
 template <typename In>
 hipError_t launch_small(const Shape& s, const void* x, const void* Wr, const float* bias,
                         int32_t* idx, float* w, float* lo, hipStream_t st) {
@@ -1166,10 +1549,20 @@ hipError_t launch_dt(const Shape& s, const void* x, const void* Wr, const float*
 
 }  // namespace
 
+size_t route_workspace_bytes(const Shape& s) {
+  SplitPlan pl;
+  if (!split_applies(s) || !plan_split(s, split_ntb(s), ~(size_t)0, &pl)) return 0;
+  return pl.bytes;
+}
+
 hipError_t launch_route(const Shape& s, const void* x, const void* W_router,
                         const float* bias, int32_t* topk_idx, float* topk_w,
-                        float* logits_out, hipStream_t st) {
+                        float* logits_out, hipStream_t st, void* scratch,
+                        size_t scratch_bytes) {
   if (s.T == 0) return hipSuccess;
+  const hipError_t e =
+      try_split(s, x, W_router, bias, topk_idx, topk_w, logits_out, scratch, scratch_bytes, st);
+  if (e != hipErrorNotSupported) return e;
   if (s.dt == MOE_DT_BF16)
     return launch_dt<bf16_t>(s, x, W_router, bias, topk_idx, topk_w, logits_out, st);
   return launch_dt<float>(s, x, W_router, bias, topk_idx, topk_w, logits_out, st);

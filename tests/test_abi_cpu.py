@@ -215,6 +215,34 @@ def test_route_balance_workspace_and_checks():
                                None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_route_workspace_and_checks():
+    L = moe.lib()
+    bf16, f32 = moe.MOE_DT_BF16, moe.MOE_DT_F32
+    # large bf16 batches with few experts or a large router matrix: at least
+    # one split's fp64 partials, [T, E]
+    for dims in ((8192, 4096, 14336, 8, 2, 0, bf16), (4096, 7168, 2048, 256, 8, 1, bf16),
+                 (100, 64, 64, 7, 2, 0, bf16)):
+        s = moe.shape(*dims)
+        assert moe.route_workspace_size(s) >= s.T * s.E * 8
+    # decode batches, fp32, and E = 128 with a 0.5 MB router: no workspace
+    for dims in ((16, 2880, 2880, 32, 4, 0, bf16), (4096, 2048, 768, 128, 8, 0, bf16),
+                 (4096, 4096, 64, 8, 2, 0, f32), (0, 64, 64, 4, 1, 0, bf16)):
+        assert moe.route_workspace_size(moe.shape(*dims)) == 0
+    assert moe.route_workspace_size(_shape(k=0)) == 0
+    s = moe.shape(8192, 4096, 14336, 8, 2, 0, bf16)
+    p = ctypes.c_void_p(4096)
+    need = moe.route_workspace_size(s)
+    args = lambda ws, nbytes: (ctypes.byref(s), p, p, None, p, p, ws, nbytes, None)
+    assert L.moe_route_ws(*args(p, need - 1)) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_route_ws(*args(None, need)) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route_ws(*args(ctypes.c_void_p(4096 + 64), need)) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route_ws(ctypes.byref(s), None, p, None, p, p, p, need,
+                          None) == moe.MOE_ERR_INVALID_ARG
+    bad = _shape(E=0)
+    assert L.moe_route_ws(ctypes.byref(bad), p, p, None, p, p, p, 1 << 30,
+                          None) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_capacity_entry_points_check_arguments():
     L = moe.lib()
     s = _shape()

@@ -109,6 +109,85 @@ def test_route(name):
         assert not amb and np.array_equal(host(idx_d), idx_ref)
 
 
+# The layer's router at bf16, T > 64, E <= 256 with E <= 64 or a router
+# matrix of at least 2 MB keeps K-split partial sums in the workspace (two
+# kernels: screen partials, then selection; every tile shape: E <= 16, 32,
+# 64, 128, 256); the same checks through moe_layer_forward, with f chosen so
+# that the workspace holds the partials of at least one split.  The Zipf
+# workload (E = 128, 0.5 MB) routes with the one-kernel screen.
+SPLIT_ROUTE_CASES = ["screen_E8_long_d", "screen_zero_router", "split_zero_router_E100",
+                     "screen_duplicate_rows", "split_E24_ragged", "split_E200_d5200",
+                     "split_E16_T1000", "split_integer_exact", "fine_grained_zipf_full",
+                     "deepseek_v3_full"]
+
+
+def _split_case(name):
+    n = moe_synth.normal
+    if name == "split_E24_ragged":
+        return n((60, 5, 0), (333, 264), 1.0, "bf16"), n((60, 5, 1), (24, 264), 0.05, "bf16"), \
+            np.linspace(0.1, -0.1, 24).astype(np.float32), 3
+    if name == "split_E200_d5200":
+        # ragged last K step (5200 = 81 * 64 + 16)
+        return n((61, 5, 0), (700, 5200), 1.0, "bf16"), n((61, 5, 1), (200, 5200), 0.02, "bf16"), \
+            None, 6
+    if name == "split_zero_router_E100":
+        # every expert stays a candidate (more than 64): ranked in rounds
+        return n((64, 5, 0), (90, 10496), 1.0, "bf16"), np.zeros((100, 10496), np.uint16), None, 5
+    if name == "split_E16_T1000":
+        return n((62, 5, 0), (1000, 512), 1.0, "bf16"), n((62, 5, 1), (16, 512), 0.05, "bf16"), \
+            None, 2
+    if name == "split_integer_exact":
+        # exact logits and exact ties everywhere: ties go to the lower index
+        return (moe_synth.to_bf16_bits(moe_synth.small_ints((63, 5, 0), (200, 136), -2, 2)),
+                moe_synth.to_bf16_bits(moe_synth.small_ints((63, 5, 1), (48, 136), -1, 1)),
+                None, 5)
+    return _route_case(name)
+
+
+@pytest.mark.parametrize("name", SPLIT_ROUTE_CASES)
+def test_route_split(name):
+    x, W, bias, k = _split_case(name)
+    T, d = x.shape
+    E = W.shape[0]
+    assert x.dtype == np.uint16 and T > 64 and E <= 256
+    # act + expert_out hold the partials of one split at least
+    f = 8
+    while T * k * (f + d) * 2 < T * E * 8 + (T + E) * 8 + 1024:
+        f += 8
+    print(f"route (layer workspace) {name}: T={T} d={d} E={E} k={k} f={f}", flush=True)
+    s = moe.shape(T, d, f, E, k, 0, moe.MOE_DT_BF16)
+    Wgu = torch.zeros(E, 2 * f, d, dtype=torch.bfloat16, device="cuda")
+    Wd = torch.zeros(E, d, f, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    moe.moe_layer_forward(s, dev(x), dev(W), dev(bias), Wgu, Wd, y, ws)
+    _sync()
+    views = moe.workspace_views(s, ws)
+    idx, w = host(views["topk_idx"]), host(views["topk_w"])
+    L, idx_ref, w_ref = oracle.route(x, W, k, bias=bias)
+    amb = check_routing(idx, w, L, abs_scores(x, W), idx_ref, w_ref)
+    assert len(amb) <= max(1, T // 1000), f"{len(amb)} near-tie tokens"
+    if "zero_router" in name or "duplicate" in name or "integer" in name:
+        assert not amb and np.array_equal(idx, idx_ref)
+    # the standalone routers agree exactly: moe_route (one fused kernel) and
+    # moe_route_ws (the layer's path, in a workspace of its own)
+    idx_d, w_d = empty((T, k), "i32"), empty((T, k), "f32")
+    moe.moe_route(s, dev(x), dev(W), dev(bias), idx_d, w_d)
+    _sync()
+    assert np.array_equal(host(idx_d), idx)
+    assert np.array_equal(host(w_d), w)
+    need = moe.route_workspace_size(s)
+    rws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    idx_d.fill_(-1)
+    w_d.fill_(0.0)
+    moe.moe_route_ws(s, dev(x), dev(W), dev(bias), idx_d, w_d, rws)
+    _sync()
+    assert np.array_equal(host(idx_d), idx)
+    assert np.array_equal(host(w_d), w)
+    del ws
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- permute
 
 PERMUTE_CASES = [
