@@ -430,31 +430,33 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(
     dlo = dropped_lower_bound(topk_idx, sorted_slot, D, e, E);
     nd = dropped_lower_bound(topk_idx, sorted_slot, D, e + 1, E) - dlo;
   }
+  // chunk c of the n = nk + nd rows (group rows first, then dropped rows)
   const int64_t n = nk + nd;
   const int64_t per = (n + kRouterChunks - 1) / kRouterChunks;
   const int64_t lo = (int64_t)c * per;
   const int64_t hi = (lo + per < n) ? lo + per : n;
   float acc = 0.f, accb = 0.f;
-  for (int64_t rb = lo; rb < hi; rb += 8) {
-    int32_t slot[8];
-    float v[8], xv[8];
+  // rows base + i for i in [i0, i1), in order
+  auto add_rows = [&](int64_t base, int64_t i0, int64_t i1) {
+    for (int64_t rb = i0; rb < i1; rb += 8) {
+      int32_t slot[8];
+      float v[8], xv[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t vi = rb + u;
-      const int64_t row = vi < nk ? r0 + vi : dlo + (vi - nk);
-      slot[u] = vi < hi ? sorted_slot[row] : 0;
-    }
+      for (int u = 0; u < 8; ++u) slot[u] = rb + u < i1 ? sorted_slot[base + rb + u] : 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      v[u] = rb + u < hi ? dl[slot[u]] : 0.f;
-      xv[u] = bf16_to_f32(x[(int64_t)((uint32_t)slot[u] / (uint32_t)k) * d + colc]);
-    }
+      for (int u = 0; u < 8; ++u) {
+        v[u] = rb + u < i1 ? dl[slot[u]] : 0.f;
+        xv[u] = bf16_to_f32(x[(int64_t)((uint32_t)slot[u] / (uint32_t)k) * d + colc]);
+      }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      acc += v[u] * xv[u];
-      accb += v[u];
+      for (int u = 0; u < 8; ++u) {
+        acc += v[u] * xv[u];
+        accb += v[u];
+      }
     }
-  }
+  };
+  add_rows(r0, lo, hi < nk ? hi : nk);
+  if (hi > nk) add_rows(dlo - nk, lo > nk ? lo : nk, hi);
   if (col < d) part[((int64_t)c * E + e) * d + col] = acc;
   if (blockIdx.y == 0 && threadIdx.x == 0) part_b[c * E + e] = accb;
 }
