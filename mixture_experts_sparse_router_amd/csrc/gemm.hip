@@ -585,8 +585,10 @@ hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot
   //    a group rarely spills a few rows into a second m-tile that would read
   //    the weight panel again (DeepSeek-V3 shape: gate_up 3.64 -> 3.54 ms);
   //  - other small groups, gate_up: 128 x 256 tiles, 8 waves, K tiles of
-  //    64, 3 stages; down: 128 x 256 tiles, 4 waves, K tiles of 32, two
-  //    workgroups per CU with 3 stages each.
+  //    64, 3 stages; down: 128 x 256 tiles, 8 waves, K tiles of 32, two
+  //    workgroups per CU with 3 stages each (fine-grained Zipf shape: down
+  //    199 -> 191 us against 4 waves; the gate_up with two workgroups per
+  //    CU, 4 or 8 waves, measured no faster, 64-row tiles 28% slower).
   const int64_t avg_rows = s.R() / (s.G() > 0 ? s.G() : 1);
   const int64_t routed_mean = s.Tk() / s.E;
   const int64_t ncols = GATED ? TBN / 2 : TBN;
@@ -603,7 +605,7 @@ hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot
   } else if (GATED) {
     MOE_TILED(128, 3, 1, 8, 64);
   } else {
-    MOE_TILED(128, 3, 2, 4, 32);
+    MOE_TILED(128, 3, 2, 8, 32);
   }
 #undef MOE_TILED
   return hipGetLastError();
