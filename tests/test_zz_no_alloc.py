@@ -1,7 +1,7 @@
 """moe_layer_forward_static, the entry point that allocates nothing (its
 intermediates live in the library's static device array), against
 moe_layer_forward with a caller workspace, through the C ABI: two calls in a
-row, the second with a smaller input, each bitwise equal to the workspace
+row, each with a smaller input than the last, each bitwise equal to the workspace
 path (same kernels, same order of every sum) and within tolerance of the
 oracle."""
 import numpy as np
@@ -18,7 +18,11 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 CASES = [
-    # the gpt-oss-20b-shaped decode layer, then a smaller one with a shared expert
+    # a prefill-sized batch whose router keeps its K-split partial sums in the
+    # static array (bf16, T > 64, 16 experts), the gpt-oss-20b-shaped decode
+    # layer, then a smaller one with a shared expert: each call smaller
+    (moe_synth.LayerConfig("static_prefill_split_router", T=200, d=256, f=128, E=16, k=2, S=0,
+                           dtype="bf16", w_std=0.05), 40),
     (moe_synth.CONFIGS[2], 2),
     (moe_synth.LayerConfig("static_small_shared", T=5, d=320, f=192, E=12, k=3, S=1,
                            dtype="bf16", w_std=0.05), 41),
