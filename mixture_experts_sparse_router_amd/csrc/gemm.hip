@@ -109,6 +109,9 @@ __device__ bool find_mtile(const int32_t* offsets, int G, int BM, int tile, int*
 // contiguous run of the tile order, in which one expert group's tiles come
 // as rectangles of its m-tiles by kBandN n-tiles.
 constexpr int TBN = 256;  // weight rows per block tile
+#ifndef MOE_PANEL_NST
+#define MOE_PANEL_NST 4
+#endif
 
 // Scheduling of one MFMA sub-step: after MFMA I come items [I*N/NM,
 // (I+1)*N/NM) of the sequence "NA items of kind KA, then NB of kind KB"
@@ -474,6 +477,238 @@ __global__ __launch_bounds__(64 * NW, OCC) void tiled_gemm_kernel(
   }
 }
 
+// ============================================================ panel_gemm
+// bf16, expert groups of at most BM rows with long K (many experts with a
+// balanced router, e.g. 256 experts of ~128 rows), where each expert's
+// weights are read from HBM once and used by few rows.  Only the token rows
+// go through LDS; the weight rows are loaded straight into the MFMA's B
+// operand registers, D K tiles ahead of their use, so the LDS holds a deeper
+// ring of token rows and no weight tile.
+//
+// Block tile: BM rows x 256 weight rows, 8 waves in a 1 x 8 grid.  Wave w
+// owns 32 weight rows as two 16-row column blocks (gate_up: 16 gate rows and
+// the 16 matching up rows, so SwiGLU pairs the two accumulators of a lane;
+// down: 32 consecutive rows) and the tile's rows as MIL row blocks of
+// v_mfma_f32_16x16x32_bf16 (MIL chosen per tile from its row count, so no
+// MFMA, fragment read or copy is spent on 16-row blocks past the group).
+// Every A fragment read from LDS feeds two MFMAs.
+//
+// K tiles of 64: the token rows of tile j are copied global -> LDS into
+// stage j % NST of the ring (XOR-swizzled as in tiled_gemm); the weight
+// chunks of tile j go to register slot j % D.  Per wave and tile: AI
+// copies, then 4 weight loads, all issued at iteration j - D, so one wait
+// for vmcnt <= (D-1)*(AI+4) covers both, and a barrier covers the other
+// waves' copies.  Tile lookup and tile order: as tiled_gemm.
+template <bool GATED, int BM, int NST, int MIL>
+__device__ __forceinline__ void panel_tile(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
+    const bf16_t* __restrict__ W, bf16_t* __restrict__ out, int64_t K, int64_t N, int64_t T,
+    int64_t Tk, int64_t k, int g, int nt, int64_t row_begin, int rows,
+    unsigned char* __restrict__ ringA) {
+  constexpr int NW = 8;
+  constexpr int SBK = 64, CPR = 8, RPC = 8;
+  constexpr uint32_t ROWB = SBK * 2;     // bytes per LDS row
+  constexpr int AI = (MIL + 3) / 4;      // A copies (1 KB) per wave per stage
+  constexpr int MI = MIL;                // live 16-row blocks (16*MIL >= rows)
+  constexpr int D = NST - 1;             // K tiles of weights loaded ahead
+  constexpr int BL = 4;                  // weight loads per wave per K tile
+  constexpr uint32_t STA = BM * ROWB;    // bytes per stage
+  static_assert(RPC * NW * AI <= BM && MIL * 16 <= BM, "copy plan");
+  static_assert(D >= 1 && (D - 1) * (AI + BL) < 64, "vmcnt range");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t Kb = (uint32_t)(K * 2);
+
+  const bf16_t* abase = GATED ? A : A + row_begin * K;
+  const uint32_t a_bytes = GATED ? (uint32_t)(T * K * 2) : (uint32_t)rows * Kb;
+  const int64_t wrows = GATED ? 2 * N : N;
+  const bf16_t* bbase = W + (int64_t)g * wrows * K;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, (int)a_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)bbase, 0, (int)(uint32_t)(wrows * K * 2),
+                                        kRsrcWord3);
+
+  // ---- token-row copies of the 16*MIL rows the MFMAs read: copy c = 8*i + w
+  // (wave w, i < AI) fills rows 8c .. 8c+7 of a stage (1 KB); lane l lands on
+  // row 8c + l/8, physical chunk l%8, which holds logical chunk
+  // (l%8) ^ ((row/2) & 7)
+  const int lrow = lane / CPR;
+  uint32_t aoff[AI];
+  int akc[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int r = RPC * (i * NW + wave) + lrow;
+    akc[i] = ((lane % CPR) ^ ((r >> 1) & (CPR - 1))) * 8;
+    uint32_t o = kOOB;
+    if (r < rows) {
+      const int64_t src_row =
+          GATED ? row_token(row_begin + r, sorted_slot, Tk, k, T) : (int64_t)r;
+      o = (uint32_t)src_row * Kb + (uint32_t)akc[i] * 2;
+    }
+    aoff[i] = o;
+  }
+  uint32_t ring_a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ringA;
+  asm("" : "+s"(ring_a));
+  auto issue_a = [&](int j) {
+    const int64_t k0 = (int64_t)j * SBK;
+    const uint32_t sa = ring_a + (uint32_t)(j % NST) * STA;
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      copy16(ra, k0 + akc[i] < K ? aoff[i] + (uint32_t)k0 * 2 : kOOB,
+             sa + (uint32_t)(RPC * (i * NW + wave)) * ROWB);
+  };
+
+  // ---- weight rows of the wave's two column blocks: lane l loads row l%16
+  // of each, K elements 8*(l/16) .. +8 of every 32-wide sub-step (the MFMA's
+  // B operand layout)
+  const int j16 = lane & 15, kq = lane >> 4;
+  uint32_t boff[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int64_t c = GATED ? (int64_t)nt * 128 + 16 * wave + j16
+                            : (int64_t)nt * 256 + 32 * wave + 16 * b + j16;
+    uint32_t o = kOOB;
+    if (c < N) {
+      const int64_t wr = GATED ? (b == 0 ? c : N + c) : c;
+      o = (uint32_t)wr * Kb + (uint32_t)kq * 16;
+    }
+    boff[b] = o;
+  }
+  u32x4 breg[D][2][2];  // [slot][sub-step][block]
+  auto issue_b = [&](int j, u32x4 (&dst)[2][2]) {
+    const int64_t k0 = (int64_t)j * SBK;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // past K: the offset gets the out-of-range bit (offsets are below 2^31)
+      const uint32_t oob = k0 + 32 * s + 8 * kq < K ? 0u : kOOB;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        uint32_t o = (boff[b] + (uint32_t)(k0 + 32 * s) * 2) | oob;
+        asm("" : "+v"(o));  // one load with a computed offset, not a branch
+        dst[s][b] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)o, 0, 0));
+      }
+    }
+  };
+
+  // ---- A fragment of row block mi, sub-step s: row 16*mi + l%16, logical
+  // chunk 4*s + l/16; the swizzle term ((row/2) & 7) is (l%16)/2 for all mi
+  uint32_t fa[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    fa[s] = (uint32_t)j16 * ROWB + (uint32_t)(((4 * s + kq) ^ (j16 >> 1)) << 4);
+
+  f32x4 acc0[MI], acc1[MI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    acc0[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nk = (int)((K + SBK - 1) / SBK);
+  // tiles 0 .. D-1: copies into stages 0 .. D-1, weights into slots 0 .. D-1,
+  // in tile order (the waits below count on it)
+#pragma unroll
+  for (int t = 0; t < D; ++t) {
+    issue_a(t);
+    issue_b(t, breg[t]);
+    asm volatile("" ::: "memory");
+  }
+  // one K tile: tile j's weights are in register slot bs
+  auto step = [&](int j, u32x4 (&bs)[2][2]) {
+    // this wave's copies and loads of tile j are done, then everyone's
+    // copies; every wave finished reading tile j-1's stage (its fragments
+    // fed the MFMAs of the previous step), which is refilled next
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((D - 1) * (AI + BL)) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue_a(j + D);  // stage (j + D) % NST = (j - 1) % NST; past the end: no data
+    const unsigned char* st = ringA + (uint32_t)(j % NST) * STA;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 af[MI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        af[mi] = *reinterpret_cast<const u32x4*>(st + fa[s] + mi * 16 * ROWB);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        acc0[mi] = mfma16(af[mi], bs[s][0], acc0[mi]);
+        acc1[mi] = mfma16(af[mi], bs[s][1], acc1[mi]);
+      }
+    }
+    issue_b(j + D, bs);  // the same slot, for tile j + D
+  };
+  // whole rounds of D tiles (slot u holds tile j0 + u), then the rest: the
+  // loop has no exit between its steps, so the compiler's own waits for the
+  // weight registers count every load issued since (a partial round inside
+  // the loop would make it wait for nearly all of them)
+  int j0 = 0;
+  for (; j0 + D <= nk; j0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) step(j0 + u, breg[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (j0 + u < nk) step(j0 + u, breg[u]);
+  // drain the loads still in flight before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue: lane holds D[4*(l/16) + q][l%16] of each 16x16 block
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * mi + 4 * kq + q;
+      if (r >= rows) continue;
+      bf16_t* orow = out + (row_begin + r) * N;
+      if constexpr (GATED) {
+        const int64_t c = (int64_t)nt * 128 + 16 * wave + j16;
+        if (c < N) orow[c] = f32_to_bf16(swiglu(acc0[mi][q], acc1[mi][q]));
+      } else {
+        const int64_t c0 = (int64_t)nt * 256 + 32 * wave + j16;
+        if (c0 < N) orow[c0] = f32_to_bf16(acc0[mi][q]);
+        if (c0 + 16 < N) orow[c0 + 16] = f32_to_bf16(acc1[mi][q]);
+      }
+    }
+  }
+}
+
+// The kernel: tile lookup, then the tile with as many 16-row blocks as its
+// rows need (BM/2, 2BM/3, 5BM/6 or BM rows), so that no MFMA or fragment
+// read of a block past the group's rows is issued and the K loop stays
+// free of branches.
+template <bool GATED, int BM, int NST>
+__global__ __launch_bounds__(512, 1) void panel_gemm_kernel(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_slot,
+    const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
+    bf16_t* __restrict__ out, int64_t K, int64_t N, int64_t T, int64_t Tk, int64_t k, int G,
+    int ntN) {
+  constexpr int MI = BM / 16;
+  static_assert(MI % 6 == 0, "row-block split");
+  static_assert(NST * BM * 128 <= 160 * 1024, "ring fits the LDS");
+  __shared__ __attribute__((aligned(1024))) unsigned char ringA[NST * BM * 128];
+  __shared__ int s_tile[3 + 8];
+  int g, mt, nt;
+  if (!find_tile<8>(offsets, G, BM, ntN, (int)blockIdx.x, &g, &mt, &nt, s_tile)) return;
+  const int64_t row_begin = offsets[g] + (int64_t)mt * BM;
+  const int64_t rows_left = offsets[g + 1] - row_begin;
+  const int rows = (int)(rows_left < BM ? rows_left : BM);
+  const int nb = __builtin_amdgcn_readfirstlane((rows + 15) / 16);
+  if (nb <= MI / 2)
+    panel_tile<GATED, BM, NST, MI / 2>(A, sorted_slot, W, out, K, N, T, Tk, k, g, nt, row_begin,
+                                        rows, ringA);
+  else if (nb <= 2 * MI / 3)
+    panel_tile<GATED, BM, NST, 2 * MI / 3>(A, sorted_slot, W, out, K, N, T, Tk, k, g, nt,
+                                            row_begin, rows, ringA);
+  else if (nb <= 5 * MI / 6)
+    panel_tile<GATED, BM, NST, 5 * MI / 6>(A, sorted_slot, W, out, K, N, T, Tk, k, g, nt,
+                                            row_begin, rows, ringA);
+  else
+    panel_tile<GATED, BM, NST, MI>(A, sorted_slot, W, out, K, N, T, Tk, k, g, nt, row_begin,
+                                    rows, ringA);
+}
+
 // ================================================================ f32_gemm
 constexpr int FBM = 64, FBN = 64, FBK = 16;
 
@@ -581,9 +816,12 @@ hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot
   //    per SIMD, so one computes while the other waits), K tiles of 64
   //    (whole 128-byte lines per copied row) in 2 stages of 64 KB;
   //  - routed groups of 112-168 rows on average (balanced routers with many
-  //    experts): 192 x 256 tiles, 8 waves, K tiles of 64, 2 stages, so that
-  //    a group rarely spills a few rows into a second m-tile that would read
-  //    the weight panel again (DeepSeek-V3 shape: gate_up 3.64 -> 3.54 ms);
+  //    experts): 192-row tiles, so that a group rarely spills a few rows
+  //    into a second m-tile that would read the weight panel again
+  //    (DeepSeek-V3 shape: gate_up 3.64 -> 3.54 ms), in panel_gemm (weights
+  //    into registers 3 K tiles ahead, only the token rows through LDS:
+  //    gate_up 3.48 -> 3.42 ms, down 2.01 -> 1.97 ms); the backward's
+  //    pre-activation recompute keeps the 192 x 256 tiled_gemm form;
   //  - other small groups, gate_up: 128 x 256 tiles, 8 waves, K tiles of
   //    64, 3 stages; down: 128 x 256 tiles, 8 waves, K tiles of 32, two
   //    workgroups per CU with 3 stages each (fine-grained Zipf shape: down
@@ -601,7 +839,14 @@ hipError_t launch_bf16(const Shape& s, const void* A, const int32_t* sorted_slot
   if (avg_rows >= 512) {
     MOE_TILED(256, 2, 1, 8, 64);
   } else if (routed_mean > 112 && routed_mean <= 168) {
-    MOE_TILED(192, 2, 1, 8, 64);
+    if constexpr (!PRE) {
+      hipLaunchKernelGGL((panel_gemm_kernel<GATED, 192, MOE_PANEL_NST>),
+                         dim3(((mtile_bound(s, 192) * (unsigned)ntN) + 7u) & ~7u), dim3(512),
+                         0, st, (const bf16_t*)A, sorted_slot, offsets, (const bf16_t*)W,
+                         (bf16_t*)out, K, N, s.T, s.Tk(), s.k, G, ntN);
+    } else {
+      MOE_TILED(192, 2, 1, 8, 64);
+    }
   } else if (GATED) {
     MOE_TILED(128, 3, 1, 8, 64);
   } else {
