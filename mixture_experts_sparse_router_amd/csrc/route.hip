@@ -609,7 +609,7 @@ __device__ void screen_pass_store(const ScreenAcc<NBW>& A, const ScreenSmem& S,
 // pairs are always formed over lane bit 5, then 4, ..., then 0, so every
 // candidate's sum has the same rounding).  Lane u < CB returns the sum of
 // candidate c0 + u.
-template <int CB>
+template <int CB, int PRE = kExactPre>
 __device__ __forceinline__ double exact_batch(const bf16_t* __restrict__ xt,
                                               const bf16_t* __restrict__ Wr,
                                               const uint16_t* cands, int c0, int ncand,
@@ -628,7 +628,7 @@ __device__ __forceinline__ double exact_batch(const bf16_t* __restrict__ xt,
   struct ExRegs {
     u32x4 xv, wv[CB];
   };
-  ExRegs rr[kExactPre];
+  ExRegs rr[PRE];
   // rounds past the row read chunk 0 and add nothing
   auto eld = [&](int64_t r, ExRegs& g) {
     const int64_t ch = 64 * r + lane;
@@ -657,12 +657,12 @@ __device__ __forceinline__ double exact_batch(const bf16_t* __restrict__ xt,
     }
   };
 #pragma unroll
-  for (int q = 0; q < kExactPre; ++q) eld(q, rr[q]);
-  for (int64_t r0 = 0; r0 < nr; r0 += kExactPre) {
+  for (int q = 0; q < PRE; ++q) eld(q, rr[q]);
+  for (int64_t r0 = 0; r0 < nr; r0 += PRE) {
 #pragma unroll
-    for (int q = 0; q < kExactPre; ++q) {
+    for (int q = 0; q < PRE; ++q) {
       eacc(r0 + q, rr[q]);
-      eld(r0 + q + kExactPre, rr[q]);
+      eld(r0 + q + PRE, rr[q]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -709,7 +709,7 @@ __device__ __forceinline__ double exact_batch(const bf16_t* __restrict__ xt,
 // Steps 2-4 for the workgroup's TT tokens, one wave per token, once the
 // screen logits and norms are in LDS (and the ring is no longer in use).  M:
 // experts per lane, at least ceil(E / 64).
-template <int M, int TT = kScreenTT, int MaxCB = 8>
+template <int M, int TT = kScreenTT, int MaxCB = 8, int PRE = kExactPre>
 __device__ void screen_select(const ScreenSmem& S, const bf16_t* __restrict__ x,
                               const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
                               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -781,10 +781,10 @@ __device__ void screen_select(const ScreenSmem& S, const bf16_t* __restrict__ x,
       const int cb = (left >= 8 && MaxCB >= 8) ? 8 : (left >= 4 && MaxCB >= 4) ? 4
                      : left >= 2 ? 2 : 1;
       double got;  // lane u < cb: candidate c0 + u
-      if (MaxCB >= 8 && cb == 8) got = exact_batch<8>(xt, Wr, mycand, c0, ncand, d);
-      else if (MaxCB >= 4 && cb == 4) got = exact_batch<4>(xt, Wr, mycand, c0, ncand, d);
-      else if (cb == 2) got = exact_batch<2>(xt, Wr, mycand, c0, ncand, d);
-      else got = exact_batch<1>(xt, Wr, mycand, c0, ncand, d);
+      if (MaxCB >= 8 && cb == 8) got = exact_batch<8, PRE>(xt, Wr, mycand, c0, ncand, d);
+      else if (MaxCB >= 4 && cb == 4) got = exact_batch<4, PRE>(xt, Wr, mycand, c0, ncand, d);
+      else if (cb == 2) got = exact_batch<2, PRE>(xt, Wr, mycand, c0, ncand, d);
+      else got = exact_batch<1, PRE>(xt, Wr, mycand, c0, ncand, d);
       if (ncand > 64) {
         if (lane < cb) {
           const int e = mycand[c0 + lane];
@@ -1341,7 +1341,8 @@ __global__ __launch_bounds__(kScreenThreads, 1) void route_part_kernel(
 constexpr int kPickWaves = 4;
 constexpr int kPickTT = kPickWaves;  // one token per wave
 constexpr int kPickThreads = 64 * kPickWaves;
-constexpr int kPickCB = 2;  // largest batch of exact logits
+constexpr int kPickMaxE = 256;  // experts of the split screen
+constexpr int kPartMaxSK = 8;   // most K splits of the split screen
 __host__ __device__ constexpr ScreenLds pick_lds(int E) {
   ScreenLds o{};
   o.lg = 0;
@@ -1357,7 +1358,11 @@ __host__ __device__ constexpr ScreenLds pick_lds(int E) {
 // Steps 2-4 from the partials: one workgroup of 8 waves per 8 tokens adds
 // the splits (split order), the bias and the norms, then selects as
 // route_staged does.
-template <int M>
+// CB: largest batch of exact logits, PRE: chunk rounds of their loads in
+// flight (E = 256: one batch of 8 with one round, 95 us at the DeepSeek-V3
+// shape against 111 us for batches of 2 with three rounds; E = 8: batches
+// of 2, three rounds, at five workgroups per CU).
+template <int M, int CB, int PRE>
 __global__ __launch_bounds__(kPickThreads) void route_pick_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const float* __restrict__ bias,
     const double* __restrict__ part, const double* __restrict__ xsq,
@@ -1368,32 +1373,59 @@ __global__ __launch_bounds__(kPickThreads) void route_pick_kernel(
   const ScreenSmem S(smem, L);
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * kPickTT;
-  for (int e = tid; e < E; e += kPickThreads) {
-    double q = 0.0;
-    for (int sp = 0; sp < SK; ++sp) q += wsq[(int64_t)sp * E + e];
-    S.wn[e] = __double2float_ru(sqrt(q));
+  // the splits' sums, each added in split order; every load of a thread is
+  // issued before the first add (one memory latency instead of one per split)
+  static_assert(kPickTT * kPickMaxE <= 4 * kPickThreads, "at most 4 logits per thread");
+  static_assert(kPickMaxE <= kPickThreads, "one norm per thread");
+  {
+    double pw[kPartMaxSK], px[kPartMaxSK];
+    const int64_t t_x = t0 + tid < T ? t0 + tid : T - 1;
+#pragma unroll
+    for (int sp = 0; sp < kPartMaxSK; ++sp) {
+      pw[sp] = sp < SK && tid < E ? wsq[(int64_t)sp * E + tid] : 0.0;
+      px[sp] = sp < SK && tid < kPickTT ? xsq[(int64_t)sp * T + t_x] : 0.0;
+    }
+    double qw = 0.0, qx = 0.0;
+#pragma unroll
+    for (int sp = 0; sp < kPartMaxSK; ++sp) {
+      if (sp < SK) {
+        qw += pw[sp];
+        qx += px[sp];
+      }
+    }
+    if (tid < E) S.wn[tid] = __double2float_ru(sqrt(qw));
+    if (tid < kPickTT) S.xn[tid] = __double2float_ru(sqrt(qx));
   }
-  if (tid < kPickTT) {
-    const int64_t t = t0 + tid < T ? t0 + tid : T - 1;
-    double q = 0.0;
-    for (int sp = 0; sp < SK; ++sp) q += xsq[(int64_t)sp * T + t];
-    S.xn[tid] = __double2float_ru(sqrt(q));
-  }
-  for (int o = tid; o < kPickTT * E; o += kPickThreads) {
-    const int tl = o / E, e = o % E;
-    const int64_t t = t0 + tl < T ? t0 + tl : T - 1;
-    double v = 0.0;
-    for (int sp = 0; sp < SK; ++sp) v += part[((int64_t)sp * T + t) * E + e];
-    S.lg[o] = rank_value(v, bias, e);
+  {
+    double pl[4][kPartMaxSK];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int o = tid + u * kPickThreads;
+      const int tl = o / E, e = o % E;
+      const int64_t t = t0 + tl < T ? t0 + tl : T - 1;
+#pragma unroll
+      for (int sp = 0; sp < kPartMaxSK; ++sp)
+        pl[u][sp] = sp < SK && o < kPickTT * E ? part[((int64_t)sp * T + t) * E + e] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int o = tid + u * kPickThreads;
+      if (o < kPickTT * E) {
+        double v = 0.0;
+#pragma unroll
+        for (int sp = 0; sp < kPartMaxSK; ++sp)
+          if (sp < SK) v += pl[u][sp];
+        S.lg[o] = rank_value(v, bias, o % E);
+      }
+    }
   }
   __syncthreads();
-  screen_select<M, kPickTT, kPickCB>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
+  screen_select<M, kPickTT, CB, PRE>(S, x, Wr, bias, topk_idx, topk_w, logits_out, T, d, E, k, t0);
 }
 
 // Split count and scratch bytes of route_split for an NTB-token-block tile:
 // the fewest splits (1, 2, 4 or 8) that give 256 workgroups, fewer if the
 // scratch is smaller; 0 if not even one split fits.
-constexpr int kPartMaxSK = 8;
 struct SplitPlan {
   int SK, ntiles;
   size_t part_off, xsq_off, wsq_off, bytes;
@@ -1423,7 +1455,7 @@ inline bool plan_split(const Shape& s, int NTB, size_t scratch_bytes, SplitPlan*
   return false;
 }
 
-template <int NTB, int NEB, int WT, int WE, int M>
+template <int NTB, int NEB, int WT, int WE, int M, int CB = 2, int PRE = kExactPre>
 hipError_t launch_split(const Shape& s, const void* x, const void* Wr, const float* bias,
                         int32_t* idx, float* w, float* lo, const SplitPlan& pl,
                         unsigned char* scratch, hipStream_t st) {
@@ -1435,7 +1467,7 @@ hipError_t launch_split(const Shape& s, const void* x, const void* Wr, const flo
                      st, (const bf16_t*)x, (const bf16_t*)Wr, part, xq, wq, s.T, s.d, (int)s.E,
                      pl.SK, pl.ntiles);
   const unsigned grid2 = (unsigned)((s.T + kPickTT - 1) / kPickTT);
-  hipLaunchKernelGGL(route_pick_kernel<M>, dim3(grid2), dim3(kPickThreads),
+  hipLaunchKernelGGL((route_pick_kernel<M, CB, PRE>), dim3(grid2), dim3(kPickThreads),
                      (size_t)pick_lds((int)s.E).total, st, (const bf16_t*)x, (const bf16_t*)Wr,
                      bias, (const double*)part, (const double*)xq, (const double*)wq, idx, w, lo,
                      s.T, s.d, (int)s.E, (int)s.k, pl.SK);
@@ -1467,8 +1499,8 @@ hipError_t try_split(const Shape& s, const void* x, const void* Wr, const float*
   if (s.E <= 16) return launch_split<8, 1, 1, 1, 1>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
   if (s.E <= 32) return launch_split<8, 2, 2, 1, 1>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
   if (s.E <= 64) return launch_split<4, 4, 2, 1, 1>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
-  if (s.E <= 128) return launch_split<4, 8, 2, 2, 2>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
-  return launch_split<4, 16, 2, 4, 4>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
+  if (s.E <= 128) return launch_split<4, 8, 2, 2, 2, 8, 1>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
+  return launch_split<4, 16, 2, 4, 4, 8, 1>(s, x, Wr, bias, idx, w, lo, pl, sc, st);
 }
 
 template <typename In>
