@@ -308,6 +308,10 @@ GEMM_CASES = [
     ("tiled_bands_bm128", 600, 1288, 1160, 6, 2, 0, "bf16", None),
     # the same n-tiling on the 256-row tiles (600 rows per group on average)
     ("tiled_bands_bm256", 1200, 1288, 1160, 2, 1, 0, "bf16", None),
+    # 140 routed rows per group on average, Zipf-skewed (328, 123, 59 and 50 rows
+    # with this seed): the weight-panel kernel with each of its row-block counts
+    # (12 and 10 for the two m-tiles of the largest group, then 8 and 6)
+    ("panel_row_blocks", 560, 264, 136, 4, 1, 0, "bf16", 1.5),
 ]
 
 
