@@ -1333,11 +1333,11 @@ __global__ __launch_bounds__(kScreenThreads, 1) void route_part_kernel(
 
 // LDS of route_pick: the screen layout for kPickTT tokens, no ring and no
 // K-split partials.
-// Four waves and exact logits in batches of at most 2 keep the kernel at 88
-// VGPRs: five workgroups per CU, every token of a 4096-token batch in
-// flight at once (measured fastest of 8 or 4 waves with batches of 8, 4
-// or 2: Mixtral-shaped 57 -> 41 us, fine-grained Zipf 50 -> 44 us for both
-// kernels together, DeepSeek-shaped unchanged).
+// Four waves, one token each (measured faster than 8 waves: Mixtral-shaped
+// 57 -> 41 us for both kernels together).  With batches of at most 2 exact
+// logits the kernel needs 86 VGPRs (five workgroups per CU); with one batch
+// of up to 8 and one chunk round in flight, 116 (four per CU, still every
+// token of a 4096-token batch in flight at once).
 constexpr int kPickWaves = 4;
 constexpr int kPickTT = kPickWaves;  // one token per wave
 constexpr int kPickThreads = 64 * kPickWaves;
