@@ -41,50 +41,61 @@
 namespace moe {
 namespace {
 
-constexpr int kBT = 128;        // tile rows and columns
+constexpr int kBT = 128;        // tile rows and columns of the 4-wave form
 constexpr int kBK = 32;         // K per stage
 constexpr int kLRow = 40;       // LDS row stride in bf16 (80 bytes: conflict-light 16-byte reads)
-constexpr int kMNRow = 160;     // M/N-major tile row stride in bf16 (320 bytes: 64-byte shift per row)
 constexpr int kBwdThreads = 256;
-static_assert(kBK * kMNRow == kBT * kLRow, "both tile forms fill the same LDS");
+// M/N-major tile row stride in bf16 for X columns: X + 32 (a 64-byte shift
+// per row: the 8 rows one transposing load touches fall on distinct banks)
+constexpr int mn_row(int X) { return X + 32; }
+constexpr int tile_elems(int X) {
+  return X * kLRow > kBK * mn_row(X) ? X * kLRow : kBK * mn_row(X);
+}
 
-// Operand tile in LDS, K-major: [128 rows (M or N)][32 K] bf16, row stride
-// kLRow; or M/N-major: [32 K rows][128 M or N] bf16, row stride kMNRow.
+// Operand tiles in LDS, K-major: [X rows (M or N)][32 K] bf16, row stride
+// kLRow; or M/N-major: [32 K rows][X M or N] bf16, row stride mn_row(X).
+template <int BM, int BN>
 struct BwdSmem {
-  bf16_t a[2][kBT * kLRow];
-  bf16_t b[2][kBT * kLRow];
+  bf16_t a[2][tile_elems(BM)];
+  bf16_t b[2][tile_elems(BN)];
 };
-// 40 KB: four workgroups per CU.  The group lookup's scratch borrows the
-// start of b[1], which is first written after the lookup's last barrier.
-static_assert(sizeof(BwdSmem) == 40960, "four workgroups fit one CU's LDS");
+// 128 x 128: 40 KB, four workgroups per CU.  The group lookup's scratch
+// borrows the start of b[1], which is first written after the lookup's last
+// barrier.
+static_assert(sizeof(BwdSmem<128, 128>) == 40960, "four workgroups fit one CU's LDS");
+static_assert(sizeof(BwdSmem<256, 256>) <= 160 * 1024, "one workgroup fits one CU's LDS");
 
 __device__ __forceinline__ void store_kc(bf16_t* tile, int row, int kc, const u32x4& v) {
   *reinterpret_cast<u32x4*>(tile + row * kLRow + kc) = v;
 }
 
-// Fragment of the 32x32x16 MFMA from an M/N-major tile: M/N indices
-// mn .. mn+31, K elements 16 ks .. +15; lane l gets column mn + (l % 32),
-// K 8 (l / 32) .. +7 (the layout of a 16-byte K-major fragment read).  In
-// each group of 16 lanes (g = l / 16, i = l % 16) the transposing load hands
-// lane i element i % 4 of the 8 bytes addressed by lane 4q + i / 4 as its
-// element q; so lane i addresses K row r0 + i / 4, columns c0 + 4 (i % 4) ..
-// +3, and receives column c0 + i of K rows r0 .. r0+3 (a second load: r0+4
-// .. r0+7), with c0 = mn + 16 (g % 2) and r0 = 16 ks + 8 (g / 2).
+// Fragment of the 32x32x16 MFMA from an M/N-major tile of row stride RS:
+// M/N indices mn .. mn+31, K elements 16 ks .. +15; lane l gets column
+// mn + (l % 32), K 8 (l / 32) .. +7 (the layout of a 16-byte K-major
+// fragment read).  In each group of 16 lanes (g = l / 16, i = l % 16) the
+// transposing load hands lane i element i % 4 of the 8 bytes addressed by
+// lane 4q + i / 4 as its element q; so lane i addresses K row r0 + i / 4,
+// columns c0 + 4 (i % 4) .. +3, and receives column c0 + i of K rows r0 ..
+// r0+3 (a second load: r0+4 .. r0+7), with c0 = mn + 16 (g % 2) and
+// r0 = 16 ks + 8 (g / 2).
+template <int RS>
 __device__ __forceinline__ u32x4 frag_mn(const bf16_t* tile, int mn, int ks, int lane) {
   typedef short v4s __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) v4s lds_v4s;
   const int g = lane >> 4, i = lane & 15;
   const int row = 16 * ks + 8 * (g >> 1) + (i >> 2);
   const int col = mn + 16 * (g & 1) + 4 * (i & 3);
-  const bf16_t* p = tile + row * kMNRow + col;
+  const bf16_t* p = tile + row * RS + col;
   const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * kMNRow));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * RS));
   const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
   return u32x4{a.x, a.y, b.x, b.y};
 }
 
 // Which row group (and m-tile) a workgroup owns: group g has
-// ceil(n_g / 128) m-tiles.  Cooperative over the 256 threads; G <= 1024.
+// ceil(n_g / BM) m-tiles.  Cooperative over the workgroup's NW waves
+// (4 groups per thread: 256 * NW >= 1024 >= G); sh: 2 + NW ints.
+template <int BM, int NW>
 __device__ bool find_group_tile(const int32_t* offsets, int G, int tile, int* g_out, int* mt_out,
                                 int* sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -92,7 +103,7 @@ __device__ bool find_group_tile(const int32_t* offsets, int G, int tile, int* g_
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int g = tid * 4 + i;
-    c[i] = g < G ? (offsets[g + 1] - offsets[g] + kBT - 1) / kBT : 0;
+    c[i] = g < G ? (offsets[g + 1] - offsets[g] + BM - 1) / BM : 0;
     mine += c[i];
   }
   int inc = mine;
@@ -129,24 +140,33 @@ __device__ bool find_group_tile(const int32_t* offsets, int G, int tile, int* g_
 // ROWS = false: C[g][m, n] = sum_{r in group g} A[r, m] B[src(r), n] (K =
 //   the group's rows, M and N fixed); A and B contiguous along M and N;
 //   C [G][M][N].
-template <bool ROWS, bool B_KC, bool GATHER>
-__global__ __launch_bounds__(kBwdThreads, 4) void bwd_gemm_kernel(
+// Tile BM x BN (128 or 256 each), one wave per 64 x 64 block of it.
+template <bool ROWS, bool B_KC, bool GATHER, int BM = kBT, int BN = kBT>
+__global__ __launch_bounds__(64 * (BM / 64) * (BN / 64), (BM == 128 && BN == 128) ? 4 : 1)
+void bwd_gemm_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
     int64_t b_stride, float* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K,
     const int32_t* __restrict__ offsets, int G, const int32_t* __restrict__ sorted_slot,
     int64_t Tk, int64_t k, int64_t T, int ntM, int ntN) {
-  __shared__ __attribute__((aligned(16))) BwdSmem sm;
+  constexpr int WN = BN / 64;               // wave columns
+  constexpr int NW = (BM / 64) * WN;        // waves
+  constexpr int NT = 64 * NW;               // threads
+  constexpr int CA = 4 * BM / NT;           // 16-byte chunks of an A tile per thread
+  constexpr int CB = 4 * BN / NT;           // ... of a B tile
+  constexpr int RSA = mn_row(BM), RSB = mn_row(BN);
+  static_assert(CA >= 1 && CB >= 1 && 4 * BM % NT == 0 && 4 * BN % NT == 0, "staging plan");
+  __shared__ __attribute__((aligned(16))) BwdSmem<BM, BN> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int g, mt, nt;
   int64_t row_begin, rows;  // ROWS: the tile's rows; else the group's rows (K)
   if constexpr (ROWS) {
     nt = (int)blockIdx.x % ntN;
-    if (!find_group_tile(offsets, G, (int)blockIdx.x / ntN, &g, &mt,
-                         reinterpret_cast<int*>(sm.b[1])))
+    if (!find_group_tile<BM, NW>(offsets, G, (int)blockIdx.x / ntN, &g, &mt,
+                                 reinterpret_cast<int*>(sm.b[1])))
       return;
-    row_begin = offsets[g] + (int64_t)mt * kBT;
+    row_begin = offsets[g] + (int64_t)mt * BM;
     const int64_t left = offsets[g + 1] - row_begin;
-    rows = left < kBT ? left : kBT;
+    rows = left < BM ? left : BM;
   } else {
     g = (int)blockIdx.x / (ntM * ntN);
     mt = ((int)blockIdx.x / ntN) % ntM;
@@ -154,28 +174,27 @@ __global__ __launch_bounds__(kBwdThreads, 4) void bwd_gemm_kernel(
     row_begin = offsets[g];
     rows = offsets[g + 1] - row_begin;
   }
-  const int64_t m0 = ROWS ? 0 : (int64_t)mt * kBT;
-  const int64_t n0 = (int64_t)nt * kBT;
+  const int64_t m0 = ROWS ? 0 : (int64_t)mt * BM;
+  const int64_t n0 = (int64_t)nt * BN;
   const int64_t KK = ROWS ? K : rows;  // contraction length
   const bf16_t* Bg = B + (ROWS ? (int64_t)g * b_stride : 0);
 
-  // ---- staging plan: every thread moves chunks c = tid and tid + 256 of
-  // the 512 16-byte chunks of each operand tile.  K-major tile (ROWS: A,
-  // and B when B_KC): tile row c/4, K elements 8*(c%4) .. of that row.
-  // M/N-major tile (its global rows are K rows): K row c/16, M/N elements
-  // 8*(c%16) .. of that row.
+  // ---- staging plan: thread tid moves chunks c = tid + NT*i of the 4*X
+  // 16-byte chunks of each operand tile (X = BM for A, BN for B).  K-major
+  // tile (ROWS: A, and B when B_KC): tile row c/4, K elements 8*(c%4) ..
+  // of that row.  M/N-major tile (its global rows are K rows): K row
+  // c/(X/8), M/N elements 8*(c%(X/8)) .. of that row.
   constexpr bool A_MN = !ROWS;
   constexpr bool B_MN = ROWS ? !B_KC : true;
-  const bf16_t* arow[2];  // ROWS: A row of the chunk's tile row (null past the tile)
-  const bf16_t* brow[2];  // ROWS && B_KC: B row n of the chunk
-  int akc[2], aro[2];
+  const bf16_t* arow[CA];  // ROWS: A row of the chunk's tile row (null past the tile)
+  const bf16_t* brow[CB];  // ROWS && B_KC: B row n of the chunk
+  int akc[CA], aro[CA], bkc[CB], bro[CB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + kBwdThreads * i;
+  for (int i = 0; i < CA; ++i) {
+    const int c = tid + NT * i;
     aro[i] = c / 4;
     akc[i] = 8 * (c % 4);
     arow[i] = nullptr;
-    brow[i] = nullptr;
     if constexpr (ROWS) {
       const int r = aro[i];
       if (r < rows) {
@@ -183,10 +202,17 @@ __global__ __launch_bounds__(kBwdThreads, 4) void bwd_gemm_kernel(
         const int64_t src = GATHER ? row_token(grow, sorted_slot, Tk, k, T) : grow;
         arow[i] = A + src * lda;
       }
-      if constexpr (B_KC) {
-        const int64_t n = n0 + aro[i];
-        if (n < N) brow[i] = Bg + n * ldb;
-      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int c = tid + NT * i;
+    bro[i] = c / 4;
+    bkc[i] = 8 * (c % 4);
+    brow[i] = nullptr;
+    if constexpr (ROWS && B_KC) {
+      const int64_t n = n0 + bro[i];
+      if (n < N) brow[i] = Bg + n * ldb;
     }
   }
   // every load reads a valid address (the group's first row, or the operand's
@@ -196,47 +222,52 @@ __global__ __launch_bounds__(kBwdThreads, 4) void bwd_gemm_kernel(
   const bf16_t* b_safe = ROWS ? Bg : B;
   // !ROWS && GATHER: token rows of the B chunks of the next tile to load,
   // looked up one tile ahead so that the row loads do not wait for them
-  int32_t tok[2] = {0, 0};
+  int32_t tok[CB];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) tok[i] = 0;
   auto tokload = [&](int j) {
     if constexpr (!ROWS && GATHER) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + kBwdThreads * i;
-        const int64_t kr = (int64_t)j * kBK + c / 16;
+      for (int i = 0; i < CB; ++i) {
+        const int c = tid + NT * i;
+        const int64_t kr = (int64_t)j * kBK + c / (BN / 8);
         const int64_t rr = row_begin + (kr < KK ? kr : 0);
         tok[i] = (int32_t)row_token(rr, sorted_slot, Tk, k, T);
       }
     }
   };
-  u32x4 ra[2], rb[2];
+  u32x4 ra[CA], rb[CB];
   // global loads of K tile j into registers
   auto gload = [&](int j) {
     const int64_t k0 = (int64_t)j * kBK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kBwdThreads * i;
-      const int64_t kr = k0 + c / 16;   // M/N-major: the chunk's K row
-      const int64_t o8 = 8 * (c % 16);  // and its first M/N element in the tile
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + NT * i;
       if constexpr (!A_MN) {
         const bool ok = arow[i] != nullptr && k0 + akc[i] < KK;
         ra[i] = zero_unless(ok, ldg16(ok ? arow[i] + k0 + akc[i] : a_safe));
       } else {
         // A[r][m], r the group row row_begin + kr
-        const int64_t m = m0 + o8;
+        const int64_t kr = k0 + c / (BM / 8);
+        const int64_t m = m0 + 8 * (c % (BM / 8));
         const bool ok = kr < KK && m < M;
         ra[i] = zero_unless(ok, ldg16(ok ? A + (row_begin + kr) * lda + m : a_safe));
       }
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + NT * i;
+      const int64_t kr = k0 + c / (BN / 8);   // M/N-major: the chunk's K row
+      const int64_t n = n0 + 8 * (c % (BN / 8));
       if constexpr (!B_MN) {
-        const bool ok = brow[i] != nullptr && k0 + akc[i] < KK;
-        rb[i] = zero_unless(ok, ldg16(ok ? brow[i] + k0 + akc[i] : b_safe));
+        const bool ok = brow[i] != nullptr && k0 + bkc[i] < KK;
+        rb[i] = zero_unless(ok, ldg16(ok ? brow[i] + k0 + bkc[i] : b_safe));
       } else if constexpr (ROWS) {
         // B[g][k][n]: K row kr
-        const int64_t n = n0 + o8;
         const bool ok = kr < KK && n < N;
         rb[i] = zero_unless(ok, ldg16(ok ? Bg + kr * ldb + n : b_safe));
       } else {
         // B[src(r)][n], r the group row row_begin + kr
-        const int64_t n = n0 + o8;
         const bool ok = kr < KK && n < N;
         const int64_t src = GATHER ? (int64_t)tok[i] : row_begin + (ok ? kr : 0);
         rb[i] = zero_unless(ok, ldg16(ok ? B + src * ldb + n : b_safe));
@@ -245,18 +276,22 @@ __global__ __launch_bounds__(kBwdThreads, 4) void bwd_gemm_kernel(
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kBwdThreads * i;
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + NT * i;
       if constexpr (!A_MN) store_kc(sm.a[buf], aro[i], akc[i], ra[i]);
-      else *reinterpret_cast<u32x4*>(sm.a[buf] + (c / 16) * kMNRow + 8 * (c % 16)) = ra[i];
-      if constexpr (!B_MN) store_kc(sm.b[buf], aro[i], akc[i], rb[i]);
-      else *reinterpret_cast<u32x4*>(sm.b[buf] + (c / 16) * kMNRow + 8 * (c % 16)) = rb[i];
+      else *reinterpret_cast<u32x4*>(sm.a[buf] + (c / (BM / 8)) * RSA + 8 * (c % (BM / 8))) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + NT * i;
+      if constexpr (!B_MN) store_kc(sm.b[buf], bro[i], bkc[i], rb[i]);
+      else *reinterpret_cast<u32x4*>(sm.b[buf] + (c / (BN / 8)) * RSB + 8 * (c % (BN / 8))) = rb[i];
     }
   };
 
   // ---- compute: wave (wm, wn) owns rows wm*64 .. +64 and columns wn*64 ..
   // +64 of the tile, 2 x 2 blocks of 32 x 32
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, lh = lane >> 5;
   f32x16 acc[2][2];
 #pragma unroll
@@ -284,12 +319,12 @@ __global__ __launch_bounds__(kBwdThreads, 4) void bwd_gemm_kernel(
         u32x4 fa[2], fb[2];
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
-          fa[mi] = A_MN ? frag_mn(sm.a[buf], wm * 64 + mi * 32, ks, lane)
+          fa[mi] = A_MN ? frag_mn<RSA>(sm.a[buf], wm * 64 + mi * 32, ks, lane)
                         : *reinterpret_cast<const u32x4*>(
                               sm.a[buf] + (wm * 64 + mi * 32 + lr) * kLRow + 16 * ks + 8 * lh);
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
-          fb[ni] = B_MN ? frag_mn(sm.b[buf], wn * 64 + ni * 32, ks, lane)
+          fb[ni] = B_MN ? frag_mn<RSB>(sm.b[buf], wn * 64 + ni * 32, ks, lane)
                         : *reinterpret_cast<const u32x4*>(
                               sm.b[buf] + (wn * 64 + ni * 32 + lr) * kLRow + 16 * ks + 8 * lh);
 #pragma unroll
@@ -503,10 +538,48 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(
   dx[t * d + i] = acc;
 }
 
-inline unsigned tiles_bound(const Shape& s) {
+inline unsigned tiles_bound(const Shape& s, int BM) {
   const int64_t R = s.R();
   const int64_t nonempty = s.G() < R ? s.G() : R;
-  return (unsigned)(R / kBT + nonempty + 1);
+  return (unsigned)(R / BM + nonempty + 1);
+}
+
+// The four expert GEMMs of the backward pass: the two over a group's rows
+// with BM x BN tiles, the two weight gradients with WM x WN tiles.
+template <int BM, int BN, int WM, int WN>
+void launch_bwd_gemms(const Shape& s, const bf16_t* dO, const bf16_t* Wd, const bf16_t* Wgu,
+                      bf16_t* dH, const bf16_t* act, const bf16_t* xb, const int32_t* offsets,
+                      const int32_t* sorted_slot, float* dA, float* dXp, float* dWd, float* dWgu,
+                      const float* H, hipStream_t st) {
+  const int G = (int)s.G();
+  const int64_t R = s.R(), d = s.d, f = s.f;
+  constexpr int NT = 64 * (BM / 64) * (BN / 64), NTW = 64 * (WM / 64) * (WN / 64);
+  const unsigned mt = tiles_bound(s, BM);
+  auto ntn = [](int64_t n) { return (int)((n + BN - 1) / BN); };
+  auto wtm = [](int64_t n) { return (int)((n + WM - 1) / WM); };
+  auto wtn = [](int64_t n) { return (int)((n + WN - 1) / WN); };
+  // 3. dA = dO Wd_e: rows, B N-contiguous (Wd_e [d][f] read as [K = d][N = f])
+  hipLaunchKernelGGL((bwd_gemm_kernel<true, false, false, BM, BN>), dim3(mt * ntn(f)), dim3(NT),
+                     0, st, dO, d, Wd, f, d * f, dA, f, (int64_t)0, f, d, offsets, G, sorted_slot,
+                     s.Tk(), s.k, s.T, 1, ntn(f));
+  // 4
+  if (R > 0)
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((R * f + 255) / 256)), dim3(256), 0,
+                       st, H, (const float*)dA, dH, R, f);
+  // 5. dXp = dH Wgu_e: rows, B N-contiguous (Wgu_e [2f][d] read as [K = 2f][N = d])
+  hipLaunchKernelGGL((bwd_gemm_kernel<true, false, false, BM, BN>), dim3(mt * ntn(d)), dim3(NT),
+                     0, st, dH, 2 * f, Wgu, d, 2 * f * d, dXp, d, (int64_t)0, d, 2 * f, offsets,
+                     G, sorted_slot, s.Tk(), s.k, s.T, 1, ntn(d));
+  // 6. dWd_e = dO^T A: K = the group's rows; M = d, N = f
+  hipLaunchKernelGGL((bwd_gemm_kernel<false, false, false, WM, WN>),
+                     dim3((unsigned)(G * wtm(d) * wtn(f))), dim3(NTW), 0, st, dO, d, act, f,
+                     (int64_t)0, dWd, f, d, f, (int64_t)0, offsets, G, sorted_slot, s.Tk(), s.k,
+                     s.T, wtm(d), wtn(f));
+  // 7. dWgu_e = dH^T Xg: M = 2f, N = d, token rows gathered
+  hipLaunchKernelGGL((bwd_gemm_kernel<false, false, true, WM, WN>),
+                     dim3((unsigned)(G * wtm(2 * f) * wtn(d))), dim3(NTW), 0, st, dH, 2 * f, xb,
+                     d, (int64_t)0, dWgu, d, 2 * f, d, (int64_t)0, offsets, G, sorted_slot,
+                     s.Tk(), s.k, s.T, wtm(2 * f), wtn(d));
 }
 
 }  // namespace
@@ -546,35 +619,27 @@ hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
     hipLaunchKernelGGL(router_dl_kernel, dim3((unsigned)((s.T + 255) / 256)), dim3(256), 0, st,
                        (const float*)dwp, topk_w, dl, s.T, s.k);
   }
-  const unsigned mt = tiles_bound(s);
-  auto nt = [](int64_t n) { return (int)((n + kBT - 1) / kBT); };
-  // 2. H = Xg Wgu_e^T: the forward's tiled gate_up GEMM, pre-activation output
+  // 3-7. the expert GEMMs (H = Xg Wgu_e^T first: the forward's tiled gate_up
+  // GEMM with a pre-activation output)
   {
     const hipError_t e = launch_gate_up_preact(s, x, sorted_slot, offsets, W_gate_up, H, st);
     if (e != hipSuccess) return e;
   }
-  // 3. dA = dO Wd_e: rows, B N-contiguous (Wd_e [d][f] read as [K = d][N = f])
-  hipLaunchKernelGGL((bwd_gemm_kernel<true, false, false>), dim3(mt * nt(f)), dim3(256), 0, st,
-                     (const bf16_t*)dO, d, Wd, f, d * f, dA, f, (int64_t)0, f, d, offsets, G,
-                     sorted_slot, s.Tk(), s.k, s.T, 1, nt(f));
-  // 4
-  if (R > 0)
-    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((R * f + 255) / 256)), dim3(256), 0,
-                       st, (const float*)H, (const float*)dA, dH, R, f);
-  // 5. dXp = dH Wgu_e: rows, B N-contiguous (Wgu_e [2f][d] read as [K = 2f][N = d])
-  hipLaunchKernelGGL((bwd_gemm_kernel<true, false, false>), dim3(mt * nt(d)), dim3(256), 0, st,
-                     (const bf16_t*)dH, 2 * f, Wgu, d, 2 * f * d, dXp, d, (int64_t)0, d, 2 * f,
-                     offsets, G, sorted_slot, s.Tk(), s.k, s.T, 1, nt(d));
-  // 6. dWd_e = dO^T A: K = the group's rows; M = d, N = f
-  hipLaunchKernelGGL((bwd_gemm_kernel<false, false, false>),
-                     dim3((unsigned)(G * nt(d) * nt(f))), dim3(256), 0, st, (const bf16_t*)dO, d,
-                     (const bf16_t*)act, f, (int64_t)0, dWd, f, d, f, (int64_t)0, offsets, G,
-                     sorted_slot, s.Tk(), s.k, s.T, nt(d), nt(f));
-  // 7. dWgu_e = dH^T Xg: M = 2f, N = d, token rows gathered
-  hipLaunchKernelGGL((bwd_gemm_kernel<false, false, true>),
-                     dim3((unsigned)(G * nt(2 * f) * nt(d))), dim3(256), 0, st,
-                     (const bf16_t*)dH, 2 * f, xb, d, (int64_t)0, dWgu, d, 2 * f, d, (int64_t)0,
-                     offsets, G, sorted_slot, s.Tk(), s.k, s.T, nt(2 * f), nt(d));
+  // Tiles (Mixtral-, DeepSeek-, Zipf-shaped backward passes, HIP events): 256 x 256
+  // for every GEMM when the groups hold 512+ rows on average (Mixtral 22.5 ->
+  // 21.6 ms); else 128 x 128 for the GEMMs over a group's rows and 256 x 256
+  // for the weight gradients (DeepSeek 26.2 -> 24.7 ms, Zipf 2.49 -> 2.45 ms),
+  // except at decode sizes, where the weight gradients (a few rows of K, fp32
+  // outputs) are fastest with 128 x 128 (1.23 against 1.26 ms).
+  if (G > 0 && R / G >= 512)
+    launch_bwd_gemms<256, 256, 256, 256>(s, dO, Wd, Wgu, dH, (const bf16_t*)act, xb, offsets,
+                                         sorted_slot, dA, dXp, dWd, dWgu, H, st);
+  else if (s.T > 64)
+    launch_bwd_gemms<kBT, kBT, 256, 256>(s, dO, Wd, Wgu, dH, (const bf16_t*)act, xb, offsets,
+                                         sorted_slot, dA, dXp, dWd, dWgu, H, st);
+  else
+    launch_bwd_gemms<kBT, kBT, kBT, kBT>(s, dO, Wd, Wgu, dH, (const bf16_t*)act, xb, offsets,
+                                         sorted_slot, dA, dXp, dWd, dWgu, H, st);
   // 8
   hipLaunchKernelGGL(router_wgrad_kernel, dim3((unsigned)s.E, (unsigned)((d + 255) / 256),
                                                kRouterChunks),

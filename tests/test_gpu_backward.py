@@ -65,6 +65,9 @@ BWD_CASES = [
     # 140 rows on average) and 256-row tiles (groups of 600 rows)
     (140, 136, 200, 4, 4, 0, None, 5),
     (600, 128, 136, 2, 2, 1, None, 6),
+    # groups of at least 512 rows on average: the expert-gradient GEMMs in
+    # 256 x 256 tiles, several of them in every dimension with ragged tails
+    (1100, 520, 264, 2, 1, 0, None, 7),
 ]
 
 
