@@ -520,27 +520,47 @@ __global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __re
 }
 
 // 9. dx_t = sum_j dXp[slot_pos(t, j)] + sum_s dXp[T*k + s*T + t]
-//         + sum_j dl_tj Wr[e_tj], in that order.
+//         + sum_j dl_tj Wr[e_tj], in that order.  Each thread owns 4
+// consecutive elements (d % 8 == 0; dXp, Wr and dx rows 16- or 8-byte
+// aligned), and the rows of up to 8 copies are loaded before they are added.
 __global__ __launch_bounds__(256) void dx_gather_kernel(
     const float* __restrict__ dXp, const int32_t* __restrict__ slot_pos,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
     const bf16_t* __restrict__ Wr, float* __restrict__ dx, int64_t T, int64_t d, int k, int S,
     int E) {
   const int64_t t = blockIdx.x;
-  const int64_t i = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
   if (i >= d) return;
   const int64_t Tk = T * k;
-  float acc = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int32_t r = slot_pos[t * k + j];
-    if (r >= 0) acc += dXp[(int64_t)r * d + i];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    f32x4 v[8];
+    bool ok[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int32_t r = j0 + u < k ? slot_pos[t * k + j0 + u] : -1;
+      ok[u] = r >= 0;
+      v[u] = ok[u] ? *reinterpret_cast<const f32x4*>(dXp + (int64_t)r * d + i)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (ok[u]) acc += v[u];
   }
-  for (int s = 0; s < S; ++s) acc += dXp[(Tk + (int64_t)s * T + t) * d + i];
+  for (int s = 0; s < S; ++s)
+    acc += *reinterpret_cast<const f32x4*>(dXp + (Tk + (int64_t)s * T + t) * d + i);
   for (int j = 0; j < k; ++j) {
     const int32_t e = topk_idx[t * k + j];
-    if (e >= 0 && e < E) acc += dl[t * k + j] * bf16_to_f32(Wr[(int64_t)e * d + i]);
+    if (e >= 0 && e < E) {
+      const float w = dl[t * k + j];
+      const uint2 b = *reinterpret_cast<const uint2*>(Wr + (int64_t)e * d + i);
+      acc[0] += w * bf16lo(b.x);
+      acc[1] += w * bf16hi(b.x);
+      acc[2] += w * bf16lo(b.y);
+      acc[3] += w * bf16hi(b.y);
+    }
   }
-  dx[t * d + i] = acc;
+  *reinterpret_cast<f32x4*>(dx + t * d + i) = acc;
 }
 
 inline unsigned tiles_bound(const Shape& s, int BM) {
@@ -657,7 +677,7 @@ hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
                      0, st, (const float*)part, (const float*)part_b, dWr, db, d, (int)s.E);
   // 9
   if (s.T > 0)
-    hipLaunchKernelGGL(dx_gather_kernel, dim3((unsigned)s.T, (unsigned)((d + 255) / 256)),
+    hipLaunchKernelGGL(dx_gather_kernel, dim3((unsigned)s.T, (unsigned)((d + 1023) / 1024)),
                        dim3(256), 0, st,
                      (const float*)dXp, slot_pos, topk_idx, (const float*)dl,
                      (const bf16_t*)W_router, dx, s.T, d, (int)s.k, (int)s.S, (int)s.E);
