@@ -366,8 +366,9 @@ void bwd_gemm_kernel(
 // ------------------------------------------------------------ elementwise
 
 // 1a. One wave per routed copy (t, j): dO row = w dy_t (bf16) and
-// dw_tj = dy_t . O_row (lanes stride over d, then a fixed butterfly); one
-// wave per shared row: dO row = dy_t.
+// dw_tj = dy_t . O_row (each lane takes 8 consecutive elements at a time,
+// 16-byte loads, striding over d; then a fixed butterfly); one wave per
+// shared row: dO row = dy_t.  d % 8 == 0 and every row is 16-byte aligned.
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const bf16_t* __restrict__ dy, const bf16_t* __restrict__ O,
     const int32_t* __restrict__ slot_pos, const float* __restrict__ topk_w,
@@ -381,7 +382,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const int64_t t = (c - Tk) % T;
     const bf16_t* dyt = dy + t * d;
     bf16_t* dOr = dO + c * d;  // shared rows follow the routed ones in the same order
-    for (int64_t i = lane; i < d; i += 64) dOr[i] = dyt[i];
+    for (int64_t i = 8 * lane; i < d; i += 512)
+      *reinterpret_cast<u32x4*>(dOr + i) = ldg16(dyt + i);
     return;
   }
   const int64_t t = c / k;
@@ -392,10 +394,18 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   if (r >= 0) {
     const bf16_t* Or = O + (int64_t)r * d;
     bf16_t* dOr = dO + (int64_t)r * d;
-    for (int64_t i = lane; i < d; i += 64) {
-      const float g = bf16_to_f32(dyt[i]);
-      acc += g * bf16_to_f32(Or[i]);
-      dOr[i] = f32_to_bf16(w * g);
+    for (int64_t i = 8 * lane; i < d; i += 512) {
+      const u32x4 gv = ldg16(dyt + i), ov = ldg16(Or + i);
+      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, ow[4] = {ov.x, ov.y, ov.z, ov.w};
+      uint32_t res[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float g0 = bf16lo(gw[h]), g1 = bf16hi(gw[h]);
+        acc += g0 * bf16lo(ow[h]);
+        acc += g1 * bf16hi(ow[h]);
+        res[h] = pack_bf16x2(w * g0, w * g1);
+      }
+      *reinterpret_cast<u32x4*>(dOr + i) = u32x4{res[0], res[1], res[2], res[3]};
     }
   }
 #pragma unroll
