@@ -471,8 +471,9 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(
     const int32_t* __restrict__ offsets, float* __restrict__ part, float* __restrict__ part_b,
     int64_t d, int64_t k, int E) {
   const int e = blockIdx.x, c = blockIdx.z;
-  const int64_t col = (int64_t)blockIdx.y * 256 + threadIdx.x;
-  const int64_t colc = col < d ? col : d - 1;
+  // four consecutive columns per thread (d % 8 == 0: 8-byte x loads)
+  const int64_t col = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
+  const int64_t colc = col < d ? col : d - 4;
   const int64_t r0 = offsets[e], nk = offsets[e + 1] - r0;
   const int64_t D = offsets[0];
   int64_t dlo = 0, nd = 0;
@@ -485,29 +486,35 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(
   const int64_t per = (n + kRouterChunks - 1) / kRouterChunks;
   const int64_t lo = (int64_t)c * per;
   const int64_t hi = (lo + per < n) ? lo + per : n;
-  float acc = 0.f, accb = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float accb = 0.f;
   // rows base + i for i in [i0, i1), in order
   auto add_rows = [&](int64_t base, int64_t i0, int64_t i1) {
     for (int64_t rb = i0; rb < i1; rb += 8) {
       int32_t slot[8];
-      float v[8], xv[8];
+      float v[8];
+      uint2 xv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) slot[u] = rb + u < i1 ? sorted_slot[base + rb + u] : 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         v[u] = rb + u < i1 ? dl[slot[u]] : 0.f;
-        xv[u] = bf16_to_f32(x[(int64_t)((uint32_t)slot[u] / (uint32_t)k) * d + colc]);
+        xv[u] = *reinterpret_cast<const uint2*>(
+            x + (int64_t)((uint32_t)slot[u] / (uint32_t)k) * d + colc);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        acc += v[u] * xv[u];
+        acc[0] += v[u] * bf16lo(xv[u].x);
+        acc[1] += v[u] * bf16hi(xv[u].x);
+        acc[2] += v[u] * bf16lo(xv[u].y);
+        acc[3] += v[u] * bf16hi(xv[u].y);
         accb += v[u];
       }
     }
   };
   add_rows(r0, lo, hi < nk ? hi : nk);
   if (hi > nk) add_rows(dlo - nk, lo > nk ? lo : nk, hi);
-  if (col < d) part[((int64_t)c * E + e) * d + col] = acc;
+  if (col < d) *reinterpret_cast<f32x4*>(part + ((int64_t)c * E + e) * d + col) = acc;
   if (blockIdx.y == 0 && threadIdx.x == 0) part_b[c * E + e] = accb;
 }
 
@@ -679,7 +686,7 @@ hipError_t launch_backward(const Shape& s, const void* x, const void* W_router,
     launch_bwd_gemms<kBT, kBT, kBT, kBT>(s, dO, Wd, Wgu, dH, (const bf16_t*)act, xb, offsets,
                                          sorted_slot, dA, dXp, dWd, dWgu, H, st);
   // 8
-  hipLaunchKernelGGL(router_wgrad_kernel, dim3((unsigned)s.E, (unsigned)((d + 255) / 256),
+  hipLaunchKernelGGL(router_wgrad_kernel, dim3((unsigned)s.E, (unsigned)((d + 1023) / 1024),
                                                kRouterChunks),
                      dim3(256), 0, st, xb, (const float*)dl, topk_idx, sorted_slot, offsets, part,
                      part_b, d, s.k, (int)s.E);
